@@ -1,0 +1,161 @@
+"""ctypes front end of the CPU oracle (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` use this module.  It loads ``oracle/liboracle.so`` (built from
+``tlg_oracle.c`` by ``oracle/build_oracle.py``) and works on numpy arrays of raw
+bit patterns, so it never touches the HIP library or its Python binding.
+
+Parity unpinned: NaN/Inf propagation (no workload produces them).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+F16, BF16, F32 = 1, 2, 3
+DTYPE_CODES = {"f16": F16, "bf16": BF16, "f32": F32}
+
+
+class Oracle:
+    """One loaded copy of the oracle library (tests may load a rebuilt copy from another path)."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"oracle library missing: {lib_path} (run oracle/build_oracle.py)")
+        lib = ctypes.CDLL(lib_path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.oracle_gemm_rows.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                         vp, vp, vp, i64, i64, vp, i32]
+        lib.oracle_gemm_rows.restype = i32
+        lib.oracle_gemm_points.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                           vp, vp, vp, i64, vp, vp, vp]
+        lib.oracle_gemm_points.restype = i32
+        lib.oracle_decode.argtypes = [i32, vp, i64, vp]
+        lib.oracle_decode.restype = i32
+        lib.oracle_encode.argtypes = [i32, vp, i64, vp]
+        lib.oracle_encode.restype = i32
+        self.lib = lib
+        self.path = lib_path
+
+    def gemm(self, M, N, K, A_bits, B_bits, *, ab="f16", c="f16", transpose_A=0, transpose_B=0,
+             clear_accum=1, relu=0, C_in_bits=None, rows=None, nthreads=None) -> np.ndarray:
+        """Oracle value o(m, n) in float64 for the rows ``rows=(m0, m1)`` (default: all)."""
+        A, B, C = _u16(A_bits), _u16(B_bits), _cin(C_in_bits, c)
+        m0, m1 = (0, M) if rows is None else rows
+        out = np.empty((m1 - m0, N), dtype=np.float64)
+        nt = nthreads if nthreads is not None else min(os.cpu_count() or 1, 16)
+        rc = self.lib.oracle_gemm_rows(M, N, K, _code(ab), _code(c), int(transpose_A),
+                                       int(transpose_B), int(clear_accum), int(relu),
+                                       _ptr(A), _ptr(B), _ptr(C), m0, m1, out.ctypes.data, int(nt))
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_rows failed with {rc}")
+        return out
+
+    def gemm_points(self, M, N, K, A_bits, B_bits, ms, ns, *, ab="f16", c="f16", transpose_A=0,
+                    transpose_B=0, clear_accum=1, relu=0, C_in_bits=None) -> np.ndarray:
+        """Oracle value at the coordinates (ms[i], ns[i])."""
+        A, B, C = _u16(A_bits), _u16(B_bits), _cin(C_in_bits, c)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_gemm_points(M, N, K, _code(ab), _code(c), int(transpose_A),
+                                         int(transpose_B), int(clear_accum), int(relu),
+                                         _ptr(A), _ptr(B), _ptr(C), ms.shape[0],
+                                         ms.ctypes.data, ns.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_points failed with {rc}")
+        return out
+
+    def decode(self, bits, dtype) -> np.ndarray:
+        b = np.ascontiguousarray(bits).reshape(-1).astype(np.uint32)
+        out = np.empty(b.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_decode(_code(dtype), b.ctypes.data, b.shape[0], out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_decode failed")
+        return out
+
+    def encode(self, x, dtype) -> np.ndarray:
+        """Round-to-nearest-even encoding of doubles; uint16 for f16/bf16, uint32 for f32."""
+        xs = np.ascontiguousarray(x, dtype=np.float64).reshape(-1)
+        out = np.empty(xs.shape[0], dtype=np.uint32)
+        rc = self.lib.oracle_encode(_code(dtype), xs.ctypes.data, xs.shape[0], out.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle_encode failed")
+        return out if _code(dtype) == F32 else out.astype(np.uint16)
+
+    def rne_out(self, x, dtype) -> np.ndarray:
+        """Oracle value rounded to the output dtype and decoded back to float64."""
+        return self.decode(self.encode(x, dtype), dtype)
+
+
+def _code(d):
+    return DTYPE_CODES[d] if isinstance(d, str) else int(d)
+
+
+def _u16(x):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.uint16:
+        raise TypeError(f"operand bits must be uint16, got {a.dtype}")
+    return a.reshape(-1)
+
+
+def _cin(x, c_dtype):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(x).reshape(-1)
+    want = np.uint32 if _code(c_dtype) == F32 else np.uint16
+    if a.dtype != want:
+        raise TypeError(f"C_in bits must be {want.__name__}, got {a.dtype}")
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def gemm(*args, **kw):
+    return default().gemm(*args, **kw)
+
+
+def gemm_points(*args, **kw):
+    return default().gemm_points(*args, **kw)
+
+
+def decode(bits, dtype):
+    return default().decode(bits, dtype)
+
+
+def encode(x, dtype):
+    return default().encode(x, dtype)
+
+
+def rne_out(x, dtype):
+    return default().rne_out(x, dtype)
+
+
+def tolerance(o: np.ndarray, K: int, c_dtype="f16") -> np.ndarray:
+    """Per-element bound |gpu - o| <= 2^-10 |o| + 1e-4 sqrt(K) (inputs in [-1, 1]).
+
+    2^-10 is twice the relative half-ulp (2^-11) of the fp16 output cast, which
+    leaves room for the fp32 accumulation; fp32 output uses the same bound.
+    bf16 output rounds with a relative half-ulp of 2^-9, so its relative term is
+    2^-8 (a reading: the stated bound is for fp16/fp32 outputs)."""
+    rel = 2.0 ** -8 if _code(c_dtype) == BF16 else 2.0 ** -10
+    return rel * np.abs(o) + 1e-4 * np.sqrt(max(K, 1))

@@ -1,0 +1,276 @@
+/*
+ * CPU oracle for the tiled dense GEMM  C = act(A·B)  — TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+ * load this library.  It shares no code, header, table or helper with the HIP
+ * path: it has its own IEEE-754 binary16 / bfloat16 decoders and its own
+ * round-to-nearest-even encoder, written from the format definitions.
+ *
+ * What it computes (plain definition, double precision, ascending k):
+ *
+ *   a(m,k) = dec(transpose_A ? A[k*M + m] : A[m*K + k])
+ *   b(k,n) = dec(transpose_B ? B[n*K + k] : B[k*N + n])
+ *   s(m,n) = (clear_accum ? 0 : dec_c(C_in[m*N + n])) + sum_{k=0}^{K-1} a(m,k) * b(k,n)
+ *   o(m,n) = relu ? (s > 0 ? s : +0.0) : s
+ *
+ * Passages followed:
+ *   - the tile program (grid of block_M x block_N output tiles, K loop of
+ *     block_K steps, gemm into an fp32 fragment, copy back to C):
+ *     "NVIDIA backend codegen" chapter, section 1 (origin of the problem);
+ *     handbook page "TileLang: a tile language one level below Triton",
+ *     section "first kernel: GEMM".  Tiling and pipelining do not change the
+ *     mathematical result, so the oracle is the untiled sum.
+ *   - fp16 inputs, fp32 accumulation, conversion back to the output dtype:
+ *     overview page "TileLang: from tile dataflow to controllable AI kernels",
+ *     section "minimal but complete GEMM skeleton".  The oracle keeps the sum
+ *     in double; the comparison tolerance absorbs the fp32 accumulation.
+ *   - transpose_A / transpose_B only change which dimension is M/N and which is
+ *     K; clear_accum starts from zero instead of C's prior contents; the
+ *     accumulator type is C's fragment type: "core primitives" chapter,
+ *     section 3.3 (T.gemm).
+ *   - T.clear is T.fill(..., 0): "core primitives" chapter, section 3.6.
+ *   - ReLU is max(x, 0) applied to the fp32 tile before it is written out:
+ *     "core primitives" chapter, section 3.8 (the GEMM+ReLU chain) and
+ *     section 4.6.  Non-positive values give +0.0; NaN gives +0.0 (reading of
+ *     an unspecified case; "parity unpinned" for NaN, which no workload makes).
+ *   - out-of-bounds source elements read as the safe value 0 and stores
+ *     outside C are skipped: "core primitives" chapter, section 4.2.  The
+ *     untiled sum never touches padding, which is exactly what zero fill
+ *     must reproduce.
+ *
+ * Output conversion (oracle_encode) is IEEE round-to-nearest-even with
+ * overflow to infinity; the pages name no rounding mode for the cast that
+ * the copy inserts, and this is the plain reading.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_F32 = 3 };
+
+/* ---------------------------------------------------------------------------
+ * Decoders, from the interchange-format definitions.
+ *   binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+ *   bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits.
+ *   binary32: 1 sign, 8 exponent (bias 127), 23 fraction bits.
+ * Exponent field 0 -> subnormal  frac * 2^(1 - bias - p);
+ * all ones -> Inf (frac == 0) or NaN; otherwise (2^p + frac) * 2^(e - bias - p).
+ * ------------------------------------------------------------------------- */
+static double dec_ieee(uint32_t bits, int p, int ebits)
+{
+    const int bias = (1 << (ebits - 1)) - 1;
+    const uint32_t frac = bits & ((1u << p) - 1u);
+    const uint32_t e = (bits >> p) & ((1u << ebits) - 1u);
+    const int neg = (bits >> (p + ebits)) & 1u;
+    double v;
+    if (e == 0)
+        v = ldexp((double)frac, 1 - bias - p);
+    else if (e == (1u << ebits) - 1u)
+        v = frac ? NAN : INFINITY;
+    else
+        v = ldexp((double)((1u << p) + frac), (int)e - bias - p);
+    return neg ? -v : v;
+}
+
+static double dec(int dtype, uint32_t bits)
+{
+    switch (dtype) {
+    case ORACLE_F16: return dec_ieee(bits & 0xffffu, 10, 5);
+    case ORACLE_BF16: return dec_ieee(bits & 0xffffu, 7, 8);
+    default: return dec_ieee(bits, 23, 8);
+    }
+}
+
+/* Round-half-to-even of a non-negative double below 2^53 (all steps exact). */
+static double round_half_even(double q)
+{
+    double fl = floor(q);
+    double d = q - fl;
+    if (d > 0.5) return fl + 1.0;
+    if (d < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+/* Encode a double into a format with p fraction bits and ebits exponent bits,
+ * rounding to nearest, ties to even; overflow gives infinity; NaN gives the
+ * positive quiet NaN. */
+static uint32_t enc_ieee(double x, int p, int ebits)
+{
+    const int bias = (1 << (ebits - 1)) - 1;
+    const int emin = 1 - bias, emax = bias;
+    const uint32_t sign = signbit(x) ? (1u << (p + ebits)) : 0u;
+    const uint32_t expall = ((1u << ebits) - 1u) << p;
+    if (isnan(x)) return expall | (1u << (p - 1));
+    if (isinf(x)) return sign | expall;
+    double a = fabs(x);
+    if (a == 0.0) return sign;
+    int e;
+    (void)frexp(a, &e);
+    e -= 1;                           /* a in [2^e, 2^(e+1)) */
+    if (e < emin) e = emin;           /* subnormal: fixed quantum 2^(emin-p) */
+    double q = ldexp(a, p - e);       /* exact power-of-two scaling, q < 2^(p+1) */
+    double r = round_half_even(q);
+    uint32_t ri = (uint32_t)r;
+    if (ri == (2u << p)) { ri = 1u << p; e += 1; }
+    if (e > emax) return sign | expall;
+    if (ri < (1u << p)) return sign | ri;                 /* subnormal or zero */
+    return sign | ((uint32_t)(e + bias) << p) | (ri - (1u << p));
+}
+
+static uint32_t enc(int dtype, double x)
+{
+    switch (dtype) {
+    case ORACLE_F16: return enc_ieee(x, 10, 5);
+    case ORACLE_BF16: return enc_ieee(x, 7, 8);
+    default: return enc_ieee(x, 23, 8);
+    }
+}
+
+static int valid_dtype(int d) { return d == ORACLE_F16 || d == ORACLE_BF16 || d == ORACLE_F32; }
+
+/* Fetch of the stored prior value of C(m,n) (16- or 32-bit patterns). */
+static uint32_t c_bits(const void *C_in, int c_dtype, int64_t idx)
+{
+    if (c_dtype == ORACLE_F32) return ((const uint32_t *)C_in)[idx];
+    return ((const uint16_t *)C_in)[idx];
+}
+
+/* ---------------------------------------------------------------------------
+ * Full GEMM over the output rows [m0, m1).
+ * The operands are first decoded to double (a as an M-major row per m, b stored
+ * per column n so that both inner reads are contiguous).  Storage order of the
+ * decoded values does not change any arithmetic: every s(m,n) is the sum of the
+ * same products in ascending k.
+ * ------------------------------------------------------------------------- */
+struct job {
+    int64_t M, N, K, m0, m1;
+    int ab, cd, tA, tB, clear, relu;
+    const uint16_t *A;
+    const double *bcol;   /* N x K decoded b, bcol[n*K + k] = b(k, n) */
+    const void *C_in;
+    double *out;          /* (m1-m0) x N */
+    int64_t r_begin, r_end;
+};
+
+static void *run_rows(void *arg)
+{
+    struct job *j = (struct job *)arg;
+    double *arow = (double *)malloc(sizeof(double) * (size_t)(j->K > 0 ? j->K : 1));
+    if (!arow) return (void *)1;
+    for (int64_t m = j->r_begin; m < j->r_end; ++m) {
+        for (int64_t k = 0; k < j->K; ++k) {
+            uint16_t bits = j->tA ? j->A[k * j->M + m] : j->A[m * j->K + k];
+            arow[k] = dec(j->ab, bits);
+        }
+        for (int64_t n = 0; n < j->N; ++n) {
+            double s = j->clear ? 0.0 : dec(j->cd, c_bits(j->C_in, j->cd, m * j->N + n));
+            const double *bc = j->bcol + n * j->K;
+            for (int64_t k = 0; k < j->K; ++k)
+                s += arow[k] * bc[k];
+            if (j->relu) s = (s > 0.0) ? s : 0.0;
+            j->out[(m - j->m0) * j->N + n] = s;
+        }
+    }
+    free(arow);
+    return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
+int oracle_gemm_rows(int64_t M, int64_t N, int64_t K, int ab_dtype, int c_dtype,
+                     int transpose_A, int transpose_B, int clear_accum, int relu,
+                     const uint16_t *A, const uint16_t *B, const void *C_in,
+                     int64_t m0, int64_t m1, double *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || m0 < 0 || m1 < m0 || m1 > M) return -1;
+    if (ab_dtype != ORACLE_F16 && ab_dtype != ORACLE_BF16) return -1;
+    if (!valid_dtype(c_dtype)) return -1;
+    if (!clear_accum && !C_in && M * N > 0) return -1;
+    if (m1 == m0 || N == 0) return 0;
+    if (K > 0 && (!A || !B)) return -1;
+    if (nthreads < 1) nthreads = 1;
+
+    double *bcol = (double *)malloc(sizeof(double) * (size_t)(N * (K > 0 ? K : 1)));
+    if (!bcol) return -2;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t bits = transpose_B ? B[n * K + k] : B[k * N + n];
+            bcol[n * K + k] = dec(ab_dtype, bits);
+        }
+
+    int64_t rows = m1 - m0;
+    if (nthreads > rows) nthreads = (int)rows;
+    struct job *jobs = (struct job *)calloc((size_t)nthreads, sizeof(struct job));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(bcol); free(jobs); free(th); return -2; }
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        struct job *j = &jobs[t];
+        j->M = M; j->N = N; j->K = K; j->m0 = m0; j->m1 = m1;
+        j->ab = ab_dtype; j->cd = c_dtype; j->tA = transpose_A; j->tB = transpose_B;
+        j->clear = clear_accum; j->relu = relu;
+        j->A = A; j->bcol = bcol; j->C_in = C_in; j->out = out;
+        j->r_begin = m0 + rows * t / nthreads;
+        j->r_end = m0 + rows * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[t], NULL, run_rows, &jobs[t]) != 0) { rc = -2; th[t] = 0; }
+    if (run_rows(&jobs[0]) != NULL) rc = -2;
+    for (int t = 1; t < nthreads; ++t) {
+        void *ret = NULL;
+        if (th[t]) { pthread_join(th[t], &ret); if (ret) rc = -2; }
+        else run_rows(&jobs[t]);
+    }
+    free(bcol); free(jobs); free(th);
+    return rc;
+}
+
+int oracle_gemm(int64_t M, int64_t N, int64_t K, int ab_dtype, int c_dtype,
+                int transpose_A, int transpose_B, int clear_accum, int relu,
+                const uint16_t *A, const uint16_t *B, const void *C_in,
+                double *out, int nthreads)
+{
+    return oracle_gemm_rows(M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B,
+                            clear_accum, relu, A, B, C_in, 0, M, out, nthreads);
+}
+
+/* The same definition evaluated at selected output coordinates (pm[i], pn[i]),
+ * decoding each operand element where it is used. */
+int oracle_gemm_points(int64_t M, int64_t N, int64_t K, int ab_dtype, int c_dtype,
+                       int transpose_A, int transpose_B, int clear_accum, int relu,
+                       const uint16_t *A, const uint16_t *B, const void *C_in,
+                       int64_t npts, const int64_t *pm, const int64_t *pn, double *out)
+{
+    if (M < 0 || N < 0 || K < 0 || npts < 0) return -1;
+    if (ab_dtype != ORACLE_F16 && ab_dtype != ORACLE_BF16) return -1;
+    if (!valid_dtype(c_dtype)) return -1;
+    for (int64_t i = 0; i < npts; ++i) {
+        int64_t m = pm[i], n = pn[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) return -1;
+        double s = clear_accum ? 0.0 : dec(c_dtype, c_bits(C_in, c_dtype, m * N + n));
+        for (int64_t k = 0; k < K; ++k) {
+            uint16_t ab = transpose_A ? A[k * M + m] : A[m * K + k];
+            uint16_t bb = transpose_B ? B[n * K + k] : B[k * N + n];
+            s += dec(ab_dtype, ab) * dec(ab_dtype, bb);
+        }
+        if (relu) s = (s > 0.0) ? s : 0.0;
+        out[i] = s;
+    }
+    return 0;
+}
+
+/* Element-wise format conversions exposed for the comparisons. */
+int oracle_decode(int dtype, const uint32_t *bits, int64_t n, double *out)
+{
+    if (!valid_dtype(dtype) || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = dec(dtype, bits[i]);
+    return 0;
+}
+
+int oracle_encode(int dtype, const double *x, int64_t n, uint32_t *bits)
+{
+    if (!valid_dtype(dtype) || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) bits[i] = enc(dtype, x[i]);
+    return 0;
+}

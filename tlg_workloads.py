@@ -1,0 +1,139 @@
+"""Seeded synthetic inputs for the tiled GEMM C = act(A·B).
+
+This module only draws random operands and describes the workload shapes.  It
+holds none of the GEMM arithmetic: both the HIP path (through the Python
+binding) and the CPU oracle consume the bits it produces, and neither imports
+the other.
+
+Recipe (the pages fix no seed or generator; this is the reading used here):
+  * CPU ``torch.Generator().manual_seed(seed)``, drawing A first, then B, then
+    (when needed) the prior contents of C, each as float32;
+  * ``uniform``: ``2 * torch.rand(shape) - 1`` (values in [-1, 1));
+    ``normal``: ``torch.randn(shape) / sqrt(K)``;
+    ``smallint``: integers drawn uniformly from [lo, hi];
+  * then a round-to-nearest-even cast to float16 / bfloat16 on the CPU.  The
+    rounded bits are the inputs of both sides.
+  * Operands are drawn directly in their stored shape: A is M×K (K×M when
+    transpose_A), B is K×N (N×K when transpose_B).  The entries are i.i.d., so
+    the distribution does not depend on the storage order.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@dataclass(frozen=True)
+class GemmCase:
+    name: str
+    M: int
+    N: int
+    K: int
+    ab: str = "f16"          # operand dtype: "f16" | "bf16"
+    c: str = "f16"           # output dtype: "f16" | "bf16" | "f32"
+    transpose_A: int = 0
+    transpose_B: int = 0
+    relu: int = 0
+    clear_accum: int = 1
+    dist: str = "uniform"    # "uniform" | "normal" | "smallint"
+    seed: int = 0
+    lo: int = -4             # smallint range
+    hi: int = 4
+    note: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def a_shape(self):
+        return (self.K, self.M) if self.transpose_A else (self.M, self.K)
+
+    @property
+    def b_shape(self):
+        return (self.N, self.K) if self.transpose_B else (self.K, self.N)
+
+    def elem_bytes(self, which: str) -> int:
+        d = self.c if which == "c" else self.ab
+        return 4 if d == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """One read of A and B and one write of C (plus a read of C when accumulating)."""
+        sa = self.elem_bytes("a")
+        sc = self.elem_bytes("c")
+        c_reads = 0 if self.clear_accum else sc * self.M * self.N
+        return sa * self.M * self.K + sa * self.K * self.N + sc * self.M * self.N + c_reads
+
+    def with_(self, **kw) -> "GemmCase":
+        return replace(self, **kw)
+
+
+# The five workloads of the method (the fifth is a pair).  Seeds are 1000 + index.
+CONFIGS = {
+    "c1": GemmCase("c1", 256, 256, 256, relu=1, dist="uniform", seed=1001,
+                   note="C=ReLU(A·B) 256^3 fp16, uniform [-1,1]"),
+    "c2": GemmCase("c2", 1024, 1024, 1024, relu=0, dist="uniform", seed=1002,
+                   note="C=A·B 1024^3 fp16, uniform [-1,1] (quickstart tile example)"),
+    "c3": GemmCase("c3", 4096, 4096, 4096, relu=1, dist="normal", seed=1003,
+                   note="C=ReLU(A·B) 4096^3 fp16, normal(0,1)/sqrt(K)"),
+    "c4": GemmCase("c4", 1000, 1500, 777, ab="bf16", c="f32", transpose_B=1,
+                   dist="uniform", seed=1004,
+                   note="ragged 1000x1500x777 bf16, B stored NxK, fp32 out"),
+    "c5a": GemmCase("c5a", 8192, 8192, 8192, dist="normal", seed=1005,
+                    note="8192^3 fp16, normal(0,1)/sqrt(K)"),
+    "c5b": GemmCase("c5b", 16, 16384, 8192, transpose_B=1, dist="uniform", seed=1006,
+                    note="skinny 16x16384x8192 fp16, B stored NxK (HBM-bound)"),
+}
+
+
+def _draw(shape, case: GemmCase, g: torch.Generator) -> torch.Tensor:
+    if case.dist == "uniform":
+        x = torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+    elif case.dist == "normal":
+        x = torch.randn(shape, generator=g, dtype=torch.float32) / math.sqrt(max(case.K, 1))
+    elif case.dist == "smallint":
+        x = torch.randint(case.lo, case.hi + 1, shape, generator=g, dtype=torch.int64).to(torch.float32)
+    else:
+        raise ValueError(f"unknown distribution {case.dist!r}")
+    return x
+
+
+def make_inputs(case: GemmCase, with_c: bool | None = None):
+    """Return CPU tensors (A, B, C_in) in stored shapes; C_in is None when clear_accum."""
+    g = torch.Generator().manual_seed(case.seed)
+    dt = DTYPES[case.ab]
+    A = _draw(case.a_shape, case, g).to(dt).contiguous()
+    B = _draw(case.b_shape, case, g).to(dt).contiguous()
+    need_c = (not case.clear_accum) if with_c is None else with_c
+    C = _draw((case.M, case.N), case, g).to(DTYPES[case.c]).contiguous() if need_c else None
+    return A, B, C
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    """Raw 16-bit patterns of a CPU fp16/bf16 tensor as a flat uint16 array (no copy of values' meaning)."""
+    assert t.dtype in (torch.float16, torch.bfloat16)
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1)
+
+
+def raw_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bit patterns of an fp16/bf16/fp32 CPU tensor (uint16 or uint32 flat array)."""
+    if t.dtype == torch.float32:
+        return t.contiguous().view(torch.int32).numpy().view(np.uint32).reshape(-1)
+    return bits16(t)
+
+
+def sample_points(M: int, N: int, count: int, seed: int = 7):
+    """Output coordinates for sampled checks: the four corners, the last row/column, plus random points."""
+    rng = np.random.default_rng(seed)
+    ms = [0, 0, M - 1, M - 1]
+    ns = [0, N - 1, 0, N - 1]
+    extra = max(count - 4, 0)
+    ms += list(rng.integers(0, M, extra))
+    ns += list(rng.integers(0, N, extra))
+    return np.asarray(ms, dtype=np.int64), np.asarray(ns, dtype=np.int64)
