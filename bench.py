@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled GEMM C = act(A·B) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5a|c3|c2|c5b|c1|c4]
+                    [--no-cpu-baseline] [--no-secondary] [--copy-calibration]
+
+A step is one launch of the whole hot path (global->LDS tile copies, the
+pipelined MFMA K loop and the fused epilogue) over one batch of seeded synthetic
+inputs already resident in HBM.  The headline workload is the 8192^3 fp16 GEMM
+(fp32 accumulate, fp16 out); the 4096^3 ReLU GEMM and the memory-bound skinny
+16x16384x8192 case are reported alongside in "secondary".  Operand sets are
+rotated so that the inputs of consecutive launches are not the same buffers
+(keeps the ~256 MB Infinity Cache from serving repeat reads).
+
+Timing: W untimed launches, then exactly K launches between a barrier +
+device synchronisation on both sides, bracketed by HIP events recorded on the
+stream the kernels run on.  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s (fp16, fp32 acc) and % of MFMA peak; skinny: HBM GB/s %"
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}     # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "tile": ["gemm_tile.hpp", "tlg_device.hpp"],
+    "skinny": ["gemm_skinny.hip", "tlg_device.hpp"],
+}
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "tiled_dense_gemm_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_hash") != kernel_hash(kind):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5a")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one 1 GiB device copy (FETCH/WRITE counter calibration)")
+    return ap.parse_args()
+
+
+def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None):
+    """Time `steps` launches of `case`.  Returns a dict with the timing and the plan."""
+    import torch
+    import tiled_dense_gemm_02_amd as tlg
+    import tlg_workloads as W
+
+    dev = torch.device("cuda:0")
+    A, B, _ = W.make_inputs(case)
+    plan = tlg.Gemm(case.M, case.N, case.K, A.dtype, {"f16": torch.float16, "bf16": torch.bfloat16,
+                                                        "f32": torch.float32}[case.c],
+                    transpose_A=bool(case.transpose_A), transpose_B=bool(case.transpose_B),
+                    epilogue="relu" if case.relu else "none")
+    set_bytes = (A.numel() + B.numel()) * 2
+    nsets = max(1, min(8, math.ceil(rotate_bytes / max(set_bytes, 1))))
+    Ad = [A.to(dev) for _ in range(nsets)]
+    Bd = [B.to(dev) for _ in range(nsets)]
+    C = torch.empty((case.M, case.N), dtype=plan_out_dtype(case), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        plan.run(Ad[i % nsets], Bd[i % nsets], C, stream)
+    torch.cuda.synchronize()
+    if log:
+        log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        plan.run(Ad[i % nsets], Bd[i % nsets], C, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    return {"ms": ms, "wall_s": wall, "plan": plan, "C": C, "A": A, "B": B, "nsets": nsets}
+
+
+def plan_out_dtype(case):
+    import torch
+    return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.c]
+
+
+def cpu_baseline(case, C_gpu, rows):
+    """Time the oracle (as it stands) on the first `rows` output rows; check those rows
+    against the GPU output as a side effect."""
+    import numpy as np
+    import tlg_workloads as W
+    from oracle import build_oracle, oracle as O
+    if not os.path.exists(O.LIB_PATH):
+        build_oracle.build()
+    A, B, _ = W.make_inputs(case)
+    nthreads = min(os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    o = O.gemm(case.M, case.N, case.K, W.bits16(A), W.bits16(B), ab=case.ab, c=case.c,
+               transpose_A=case.transpose_A, transpose_B=case.transpose_B, relu=case.relu,
+               rows=(0, rows), nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * case.N * case.K
+    gpu = C_gpu[:rows].float().cpu().numpy().astype(np.float64)
+    tol = O.tolerance(o, case.K, case.c)
+    ok = bool((np.abs(gpu - o) <= tol).all())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {rows} of {case.M} output rows of {case.name} "
+                      f"({flops / 1e9:.1f} GFLOP, fp64 triple loop, {dt:.1f} s)",
+            "seconds": dt, "sample_matches_gpu": ok}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              f"multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tlg_workloads as W
+
+    def log(m):
+        print(m, file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
+        del x, y
+
+    case = W.CONFIGS[args.workload]
+    kind = "skinny" if case.M <= 16 and case.transpose_B else "tile"
+    r = measure(case, args.steps, args.warmup, log=log)
+    plan = r["plan"]
+    info = plan.info
+    ms = r["ms"]
+    tflops = case.flops / (ms * 1e-3) / 1e12
+    gbs = case.algorithmic_bytes / (ms * 1e-3) / 1e9
+    if kind == "skinny":
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS}
+        value, unit = gbs, "GB/s"
+    else:
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[case.ab], "unit": "TFLOP/s",
+                "frac": tflops / PEAK_TFLOPS[case.ab]}
+        value, unit = tflops, "TFLOP/s"
+    roof["traffic"] = stored_traffic(args.workload, kind)
+    roof["kernel"] = plan.describe().split()[0]
+    roof["per_launch"] = {"flops": case.flops, "algorithmic_bytes": case.algorithmic_bytes,
+                          "avg_kernel_ms": ms}
+
+    out = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": case.ab, "data": "synthetic (seeded, see tlg_workloads.py)",
+           "config": {"workload": f"{case.name}: {case.note}", "M": case.M, "N": case.N, "K": case.K,
+                      "ab_dtype": case.ab, "c_dtype": case.c, "transpose_A": case.transpose_A,
+                      "transpose_B": case.transpose_B, "epilogue": "relu" if case.relu else "none",
+                      "plan": plan.describe(), "operand_sets_rotated": r["nsets"]},
+           "roofline": roof}
+
+    if not args.no_secondary:
+        sec = []
+        for name in ("c3", "c5b"):
+            if name == args.workload:
+                continue
+            c2 = W.CONFIGS[name]
+            rr = measure(c2, max(10, args.steps // 2), 5, log=log)
+            t = rr["ms"] * 1e-3
+            entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
+                     "GB/s": c2.algorithmic_bytes / t / 1e9, "plan": rr["plan"].describe()}
+            entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.ab]
+            entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS
+            sec.append(entry)
+            del rr
+        out["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        rows = {"c5a": 2048, "c3": 4096, "c2": 1024, "c1": 256, "c4": 1000, "c5b": 16}[args.workload]
+        cb = cpu_baseline(case, r["C"], rows)
+        out["cpu_baseline"] = cb
+        if unit == "GB/s":
+            cb["value_gbs"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

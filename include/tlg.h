@@ -1,0 +1,150 @@
+/*
+ * tlg — tiled, software-pipelined dense GEMM  C = act(A·B)  for AMD MI355X (gfx950).
+ *
+ * C-ABI boundary of libtlg.so.  Plain pointers and sizes only.
+ *
+ * The operation is the tile program of the TileLang quickstart GEMM(+ReLU):
+ *   - "NVIDIA backend codegen" chapter, section 1: a grid of block_M x block_N
+ *     output tiles, a K loop of block_K steps run as a software pipeline
+ *     (T.Pipelined, num_stages), global->shared copies of the A and B tiles, a
+ *     block GEMM into an fp32 register fragment, then a copy back to C;
+ *   - handbook page "TileLang: a tile language one level below Triton",
+ *     section "first kernel: GEMM" (block 128x128x64, 3 stages, fp16 in, fp32
+ *     accumulate, fp16 out);
+ *   - "core primitives" chapter, section 3.3 (T.gemm): transpose_A means A is
+ *     stored [K, M], transpose_B means B is stored [N, K]; clear_accum starts
+ *     the accumulator at zero instead of C's prior contents; the accumulator
+ *     type is C's fragment type (fp32 here, always);
+ *   - "core primitives" chapter, sections 3.8 and 4.6: the ReLU epilogue is
+ *     max(x, 0) on the fp32 tile before the write-out;
+ *   - "core primitives" chapter, section 4.2: out-of-bounds source elements
+ *     read as 0, stores outside C are skipped.
+ *
+ * Value computed, for 0 <= m < M, 0 <= n < N:
+ *   acc(m,n) = (clear_accum ? 0 : (float)C[m*N + n]) + sum_k a(m,k) * b(k,n)   (fp32 accumulate)
+ *   C[m*N + n] = convert_rne(epilogue == RELU ? max(acc, +0) : acc)
+ * with a(m,k) = transpose_A ? A[k*M + m] : A[m*K + k]
+ *      b(k,n) = transpose_B ? B[n*K + k] : B[k*N + n].
+ * The order of the fp32 additions is unspecified but fixed for a plan: two runs
+ * of one plan on the same inputs give bit-identical C.
+ *
+ * Layout: all matrices are dense and packed (leading dimension = row length).
+ * Dtypes: A and B share ab_dtype in {TLG_F16, TLG_BF16}; c_dtype in {TLG_F16,
+ * TLG_BF16, TLG_F32}.
+ *
+ * Ownership: the caller owns A, B and C (device memory) and keeps them alive
+ * until the work queued on the stream has finished.  The library owns the
+ * plan.  tlg_gemm_run allocates nothing, does not synchronise, and enqueues at
+ * most one kernel on the given stream.  A plan is immutable after create, so
+ * concurrent runs of one plan on different streams are safe.
+ */
+#ifndef TLG_H
+#define TLG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tlg_gemm_s *tlg_gemm_t;
+
+typedef enum { TLG_F16 = 1, TLG_BF16 = 2, TLG_F32 = 3 } tlg_dtype;
+
+typedef enum { TLG_EPI_NONE = 0, TLG_EPI_RELU = 1 } tlg_epilogue;
+
+/* Kernel variants.  AUTO lets create choose; the others force one (tests). */
+typedef enum {
+    TLG_VARIANT_AUTO = 0,
+    TLG_VARIANT_TILE_256 = 1,  /* 256x256x64 block tile, 4 wave64s, 2-stage LDS ring */
+    TLG_VARIANT_TILE_128 = 2,  /* 128x128x64 block tile, 2 wave64s, 2-stage LDS ring */
+    TLG_VARIANT_SKINNY = 3,    /* M <= 16 rows per block, B stored [N,K], streaming  */
+    TLG_VARIANT_EMPTY = 4      /* M == 0 or N == 0: nothing to launch (chosen by create) */
+} tlg_variant;
+
+typedef enum {
+    TLG_OK = 0,
+    TLG_ERR_INVALID_ARG = -1,  /* bad dimension, enum or flag; C overlaps A or B   */
+    TLG_ERR_UNSUPPORTED = -2,  /* valid request this library does not implement  */
+    TLG_ERR_NULL = -3,         /* null plan, output handle or data pointer        */
+    TLG_ERR_MISALIGNED = -4,   /* pointer not aligned as the plan requires        */
+    TLG_ERR_HIP = -5,          /* the HIP runtime reported an error at launch     */
+    TLG_ERR_NOMEM = -6         /* host allocation of the plan failed              */
+} tlg_status;
+
+/* Plan facts, for tests and the benchmark. */
+typedef struct {
+    int32_t variant;       /* tlg_variant actually chosen                            */
+    int32_t block_m, block_n, block_k;
+    int32_t stages;        /* LDS ring depth                                          */
+    int32_t threads;       /* work-items per workgroup                                */
+    int32_t vec_a, vec_b;  /* elements per global load of A / B (8 = 128-bit, 1 = 16-bit) */
+    int64_t grid;          /* workgroups per launch                                   */
+    int64_t lds_bytes;     /* LDS bytes per workgroup                                 */
+    int32_t k_tiles;       /* trips of the K loop per workgroup                       */
+    int32_t reserved;
+} tlg_plan_info;
+
+/*
+ * Create a plan for C[M,N] = act(A·B).
+ *   M, N, K      : 0 <= M, N <= 2^24, 0 <= K <= 2^22.  M or N == 0 is a no-op plan;
+ *                  K == 0 gives C = act(clear_accum ? 0 : C) (the empty sum).
+ *   ab_dtype     : TLG_F16 or TLG_BF16 (A and B).
+ *   c_dtype      : TLG_F16, TLG_BF16 or TLG_F32.
+ *   transpose_A  : 0 -> A stored [M,K];  1 -> A stored [K,M].
+ *   transpose_B  : 0 -> B stored [K,N];  1 -> B stored [N,K].
+ *   clear_accum  : 1 -> start from zero; 0 -> add onto C's prior contents.
+ *   epilogue     : TLG_EPI_NONE or TLG_EPI_RELU.
+ * Returns TLG_ERR_NULL if out is NULL, TLG_ERR_INVALID_ARG for a bad dimension,
+ * enum or flag, TLG_ERR_UNSUPPORTED for an operand dtype other than F16/BF16,
+ * TLG_ERR_NOMEM if the plan cannot be allocated.  No device work happens here.
+ * On failure *out is set to NULL.
+ */
+tlg_status tlg_gemm_create(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
+                           int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
+                           int32_t transpose_B, int32_t clear_accum, int32_t epilogue);
+
+/*
+ * As tlg_gemm_create, but forces a kernel variant (tlg_variant).  Returns
+ * TLG_ERR_UNSUPPORTED when the forced variant cannot run the request (the
+ * skinny variant needs transpose_A == 0, transpose_B == 1 and K % 8 == 0).
+ */
+tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
+                                   int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
+                                   int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
+                                   int32_t variant);
+
+/*
+ * Enqueue C = act(A·B) on `stream` (a hipStream_t; NULL is the null stream).
+ *   A, B : device pointers to the packed operands (read only).  May be NULL only
+ *          when K == 0 or M*N == 0.
+ *   C    : device pointer to the packed M x N output (read when clear_accum == 0).
+ * A and B must be aligned to their element size, and to 16 bytes when the plan
+ * uses 128-bit loads for them (tlg_plan_info.vec_a / vec_b == 8); C to its
+ * element size.  C must not overlap A or B.
+ * Returns TLG_ERR_NULL, TLG_ERR_MISALIGNED, TLG_ERR_INVALID_ARG (overlap) or
+ * TLG_ERR_HIP (launch failure); TLG_OK once the kernel is queued.  Execution
+ * errors surface on the stream, as for any HIP kernel.
+ */
+tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, void *stream);
+
+/* Release a plan.  NULL is accepted (no-op, TLG_OK). */
+tlg_status tlg_gemm_destroy(tlg_gemm_t plan);
+
+/* Fill *info with the plan's launch facts.  TLG_ERR_NULL for a NULL argument. */
+tlg_status tlg_gemm_query(tlg_gemm_t plan, tlg_plan_info *info);
+
+/* Human-readable one-line description of a plan (static storage owned by the plan). */
+const char *tlg_gemm_describe(tlg_gemm_t plan);
+
+/* Name of a status code (static string). */
+const char *tlg_status_string(int32_t status);
+
+/* Library version string (static). */
+const char *tlg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TLG_H */

@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path (through the C-ABI binding) against the CPU oracle on the
+same seeded inputs.  Tolerance |gpu - oracle| <= 2^-10 |oracle| + 1e-4 sqrt(K) for
+inputs in [-1, 1]; exact (after the oracle's own rounding) for small-integer inputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import tlg_workloads as W
+from parity import (assert_exact, assert_within_tolerance, log, oracle_full, oracle_points, out_values,
+                    run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import tiled_dense_gemm_02_amd as tlg
+    tlg.load_library()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    yield
+
+
+def _full_check(case, variant="auto", guard=0, exact=False):
+    log(f"[case] {case.name} M={case.M} N={case.N} K={case.K} ab={case.ab} c={case.c} "
+        f"tA={case.transpose_A} tB={case.transpose_B} relu={case.relu} clear={case.clear_accum} "
+        f"dist={case.dist} variant={variant}")
+    A, B, C_in = W.make_inputs(case)
+    C, plan, buf, g = run_gpu(case, A, B, C_in, variant=variant, guard=guard)
+    gpu = out_values(C)
+    o = oracle_full(case, A, B, C_in)
+    if exact:
+        assert_exact(gpu, o, case, plan.describe())
+    else:
+        err = assert_within_tolerance(gpu, o, case, plan.describe())
+        log(f"    max|err| = {err:.3e}  ({plan.describe()})")
+    if guard:
+        raw = buf.view(torch.uint8).cpu()
+        esz = 4 if case.c == "f32" else 2
+        head = raw[:g * esz]
+        tail = raw[(g + case.M * case.N) * esz:]
+        assert bool((head == 0x5A).all()) and bool((tail == 0x5A).all()), "store outside C"
+    return plan
+
+
+# ---------------------------------------------------------------- the five workloads
+def test_config1_relu_256():
+    _full_check(W.CONFIGS["c1"], guard=4096)
+
+
+def test_config2_1024():
+    plan = _full_check(W.CONFIGS["c2"])
+    assert plan.info.k_tiles == 16          # 1024 / 64, the pages' K trip count
+
+
+def test_config4_ragged_bf16_bt_f32out():
+    _full_check(W.CONFIGS["c4"], guard=4096)
+
+
+def _sampled_check(case, count):
+    log(f"[case] {case.name} sampled ({count} points) M={case.M} N={case.N} K={case.K}")
+    A, B, C_in = W.make_inputs(case)
+    C, plan, _, _ = run_gpu(case, A, B, C_in)
+    ms, ns = W.sample_points(case.M, case.N, count)
+    gpu = out_values(C)
+    o = oracle_points(case, A, B, C_in, ms, ns)
+    err = assert_within_tolerance(gpu[ms, ns], o, case, plan.describe())
+    log(f"    max|err| = {err:.3e}  ({plan.describe()})")
+    # properties that hold everywhere: finite, ReLU output non-negative
+    assert np.isfinite(gpu).all()
+    if case.relu:
+        assert (gpu >= 0).all()
+    return plan, gpu
+
+
+def test_config3_relu_4096_sampled():
+    plan, gpu = _sampled_check(W.CONFIGS["c3"], 4096)
+    assert plan.info.variant == 1 and plan.info.grid == 256
+
+
+def test_config5a_8192_sampled():
+    plan, _ = _sampled_check(W.CONFIGS["c5a"], 4096)
+    assert plan.info.grid == 1024
+
+
+def test_config5b_skinny_full():
+    plan = _full_check(W.CONFIGS["c5b"])
+    assert plan.info.variant == 3
+
+
+# ---------------------------------------------------------------- exactness
+@pytest.mark.parametrize("variant", ["tile256", "tile128", "skinny"])
+@pytest.mark.parametrize("ab", ["f16", "bf16"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_small_integers_exact(variant, ab, tA, tB):
+    if variant == "skinny" and (tA, tB) != (0, 1):
+        pytest.skip("the skinny kernel takes A stored [M,K] and B stored [N,K] only")
+    # 300 rows: ragged for the 128 tile; the 256 tile needs 128-bit loads, so with A
+    # stored [K, M] its M must be a multiple of 8 (304)
+    M = {"skinny": 16, "tile128": 300, "tile256": 304}[variant]
+    case = W.GemmCase("smallint", M, 264, 200, ab=ab, c="f32", transpose_A=tA, transpose_B=tB,
+                      dist="smallint", seed=77, relu=1)
+    _full_check(case, variant=variant, exact=True)
+
+
+# ---------------------------------------------------------------- edges
+RAGGED = [1, 15, 17, 31, 33, 64, 65, 127, 129, 257]
+
+
+@pytest.mark.parametrize("variant", ["tile128", "tile256"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_ragged_sweep(variant, tA, tB):
+    rng = np.random.default_rng(1000 + 10 * tA + tB + (100 if variant == "tile256" else 0))
+    for it in range(6):
+        M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
+        if variant == "tile256":       # 128-bit loads need the contiguous extent % 8 == 0
+            M, N, K = ((x + 7) // 8 * 8 for x in (M, N, K))
+        ab = "f16" if it % 2 == 0 else "bf16"
+        c = ["f16", "f32", "bf16"][it % 3]
+        case = W.GemmCase(f"ragged{it}", M, N, K, ab=ab, c=c, transpose_A=tA, transpose_B=tB,
+                          relu=it % 2, seed=500 + it)
+        _full_check(case, variant=variant, guard=1024)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 17, 32])
+def test_skinny_rows(M):
+    case = W.GemmCase(f"skinny{M}", M, 1000, 520, transpose_B=1, seed=900 + M, relu=M % 2)
+    plan = _full_check(case, variant="skinny", guard=1024)
+    assert plan.info.variant == 3
+
+
+def test_accumulate_onto_c():
+    for variant, tB in (("tile128", 0), ("tile256", 0), ("skinny", 1)):
+        for c in ("f16", "f32"):
+            case = W.GemmCase(f"accum-{variant}-{c}", 16 if variant == "skinny" else 264, 200, 136,
+                              c=c, transpose_B=tB, clear_accum=0, relu=1, seed=31)
+            _full_check(case, variant=variant)
+
+
+def test_empty_k_and_empty_output():
+    case = W.GemmCase("k0", 70, 90, 0, c="f32", clear_accum=0, seed=5)
+    _full_check(case)
+    case = W.GemmCase("k0relu", 70, 90, 0, c="f16", relu=1, seed=6)
+    _full_check(case)
+    import tiled_dense_gemm_02_amd as tlg
+    plan = tlg.Gemm(0, 5, 7)
+    assert plan.info.variant == 4
+    A = torch.empty((0, 7), dtype=torch.float16, device="cuda")
+    B = torch.empty((7, 5), dtype=torch.float16, device="cuda")
+    C = torch.empty((0, 5), dtype=torch.float16, device="cuda")
+    plan.run(A, B, C)
+
+
+def test_deterministic():
+    case = W.CONFIGS["c2"].with_(name="determinism", relu=1)
+    A, B, _ = W.make_inputs(case)
+    C1, _, _, _ = run_gpu(case, A, B, None)
+    C2, _, _, _ = run_gpu(case, A, B, None)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    case = W.CONFIGS["c5b"].with_(name="determinism-skinny", N=2048, K=4096)
+    A, B, _ = W.make_inputs(case)
+    C1, _, _, _ = run_gpu(case, A, B, None)
+    C2, _, _, _ = run_gpu(case, A, B, None)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+def test_zero_padding_invariant_on_gpu():
+    """The ragged-K workload equals the same GEMM with K zero-padded to 832 = 13 * 64."""
+    case = W.CONFIGS["c4"]
+    A, B, _ = W.make_inputs(case)
+    Kp = 832
+    Ap = torch.zeros((case.M, Kp), dtype=A.dtype); Ap[:, :case.K] = A
+    Bp = torch.zeros((case.N, Kp), dtype=B.dtype); Bp[:, :case.K] = B
+    C1, _, _, _ = run_gpu(case, A, B, None)
+    C2, _, _, _ = run_gpu(case.with_(K=Kp), Ap, Bp, None)
+    assert torch.equal(C1, C2)

@@ -1,0 +1,192 @@
+"""tlg — tiled, software-pipelined dense GEMM C = act(A·B) on AMD MI355X (gfx950).
+
+Thin ctypes binding over the C-ABI of ``libtlg.so`` (declared in include/tlg.h).
+It only marshals arguments: PyTorch provides device buffers and the current
+stream; every step of the computation runs in the library's HIP kernels.  If
+the library is not built, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["Gemm", "gemm", "PlanInfo", "TlgError", "lib_path", "load_library", "status_name",
+           "VARIANTS", "F16", "BF16", "F32"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libtlg.so")
+
+F16, BF16, F32 = 1, 2, 3
+_TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4}
+EPILOGUES = {"none": 0, "relu": 1}
+
+STATUS = {0: "TLG_OK", -1: "TLG_ERR_INVALID_ARG", -2: "TLG_ERR_UNSUPPORTED", -3: "TLG_ERR_NULL",
+          -4: "TLG_ERR_MISALIGNED", -5: "TLG_ERR_HIP", -6: "TLG_ERR_NOMEM"}
+
+
+class TlgError(RuntimeError):
+    def __init__(self, what: str, status: int):
+        super().__init__(f"{what}: {STATUS.get(status, status)}")
+        self.status = status
+
+
+def status_name(s: int) -> str:
+    return STATUS.get(s, f"unknown({s})")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("block_k", ctypes.c_int32), ("stages", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("lds_bytes", ctypes.c_int64), ("k_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library():
+    """Load libtlg.so from the package directory; raise if it has not been built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with "
+                               f"`python -m tiled_dense_gemm_02_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(lib_path)
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+        lib.tlg_gemm_create.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, i32, i32, i32]
+        lib.tlg_gemm_create.restype = i32
+        lib.tlg_gemm_create_variant.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, i32,
+                                                i32, i32, i32]
+        lib.tlg_gemm_create_variant.restype = i32
+        lib.tlg_gemm_run.argtypes = [vp, vp, vp, vp, vp]
+        lib.tlg_gemm_run.restype = i32
+        lib.tlg_gemm_destroy.argtypes = [vp]
+        lib.tlg_gemm_destroy.restype = i32
+        lib.tlg_gemm_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        lib.tlg_gemm_query.restype = i32
+        lib.tlg_gemm_describe.argtypes = [vp]
+        lib.tlg_gemm_describe.restype = ctypes.c_char_p
+        lib.tlg_status_string.argtypes = [i32]
+        lib.tlg_status_string.restype = ctypes.c_char_p
+        lib.tlg_version.argtypes = []
+        lib.tlg_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    if isinstance(dt, str):
+        return {"f16": F16, "bf16": BF16, "f32": F32}[dt]
+    return _TORCH_TO_CODE[dt]
+
+
+class Gemm:
+    """A plan for C[M,N] = act(A·B) (tlg_gemm_create).  Immutable; reusable on any stream."""
+
+    def __init__(self, M: int, N: int, K: int, ab_dtype=torch.float16, out_dtype=torch.float16, *,
+                 transpose_A: bool = False, transpose_B: bool = False, clear_accum: bool = True,
+                 epilogue: str = "none", variant: str = "auto"):
+        lib = load_library()
+        self.M, self.N, self.K = int(M), int(N), int(K)
+        self.ab_code, self.c_code = _code(ab_dtype), _code(out_dtype)
+        self.transpose_A, self.transpose_B = bool(transpose_A), bool(transpose_B)
+        self.clear_accum = bool(clear_accum)
+        self.epilogue = epilogue
+        self._h = ctypes.c_void_p()
+        args = (self.M, self.N, self.K, self.ab_code, self.c_code, int(self.transpose_A),
+                int(self.transpose_B), int(self.clear_accum), EPILOGUES[epilogue])
+        if variant == "auto":
+            st = lib.tlg_gemm_create(ctypes.byref(self._h), *args)
+        else:
+            st = lib.tlg_gemm_create_variant(ctypes.byref(self._h), *args, VARIANTS[variant])
+        if st != 0:
+            self._h = None
+            raise TlgError("tlg_gemm_create", st)
+        self._lib = lib
+
+    @property
+    def info(self) -> PlanInfo:
+        info = PlanInfo()
+        st = self._lib.tlg_gemm_query(self._h, ctypes.byref(info))
+        if st != 0:
+            raise TlgError("tlg_gemm_query", st)
+        return info
+
+    def describe(self) -> str:
+        return self._lib.tlg_gemm_describe(self._h).decode()
+
+    def _check(self, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor):
+        M, N, K = self.M, self.N, self.K
+        a_shape = (K, M) if self.transpose_A else (M, K)
+        b_shape = (N, K) if self.transpose_B else (K, N)
+        for name, t, shape, code in (("A", A, a_shape, self.ab_code), ("B", B, b_shape, self.ab_code),
+                                     ("C", C, (M, N), self.c_code)):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be a device tensor, got {t.device}")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+            if _TORCH_TO_CODE.get(t.dtype) != code:
+                raise ValueError(f"{name} has dtype {t.dtype}, plan expects code {code}")
+            if t.numel() and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+
+    def run(self, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
+        """Enqueue the GEMM on `stream` (default: torch's current stream).  Returns C."""
+        self._check(A, B, C)
+        if stream is None:
+            stream = torch.cuda.current_stream(C.device)
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        st = self._lib.tlg_gemm_run(self._h, A.data_ptr() or None, B.data_ptr() or None,
+                                    C.data_ptr() or None, ctypes.c_void_p(s))
+        if st != 0:
+            raise TlgError("tlg_gemm_run", st)
+        return C
+
+    def run_ptrs(self, a_ptr: int, b_ptr: int, c_ptr: int, stream_handle: int = 0) -> int:
+        """Raw-pointer form of run (no checks beyond the library's own); returns the status."""
+        return self._lib.tlg_gemm_run(self._h, a_ptr or None, b_ptr or None, c_ptr or None,
+                                      ctypes.c_void_p(stream_handle))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.tlg_gemm_destroy(h)
+            self._h = None
+
+
+_plan_cache: dict = {}
+
+
+def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, *, transpose_A: bool = False,
+         transpose_B: bool = False, clear_accum: bool = True, epilogue: str = "none",
+         out_dtype=torch.float16, variant: str = "auto") -> torch.Tensor:
+    """C = act(A·B) (or act(C + A·B) with clear_accum=False).  A, B, C are device tensors."""
+    M = A.shape[1] if transpose_A else A.shape[0]
+    K = A.shape[0] if transpose_A else A.shape[1]
+    N = B.shape[0] if transpose_B else B.shape[1]
+    if C is None:
+        if not clear_accum:
+            raise ValueError("clear_accum=False needs C")
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    key = (M, N, K, A.dtype, C.dtype, bool(transpose_A), bool(transpose_B), bool(clear_accum), epilogue,
+           variant)
+    plan = _plan_cache.get(key)
+    if plan is None:
+        plan = Gemm(M, N, K, A.dtype, C.dtype, transpose_A=transpose_A, transpose_B=transpose_B,
+                    clear_accum=clear_accum, epilogue=epilogue, variant=variant)
+        _plan_cache[key] = plan
+    return plan.run(A, B, C)

@@ -1,0 +1,247 @@
+// C-ABI layer of libtlg.so: argument validation, plan (variant) selection and
+// launch.  Mirrors the pages' generated host wrapper (an extern "C" call that
+// launches the kernel on the caller's stream: "NVIDIA backend codegen"
+// chapter, section 4.2) and its host-side checks of pointers, dtypes and
+// shapes before launch (overview page, "JIT and ABI" section).  Invalid or
+// unsupported requests are rejected with a status code; nothing falls back
+// silently.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <new>
+
+#include "../../include/tlg.h"
+#include "tlg_internal.h"
+
+using namespace tlg;
+
+struct tlg_gemm_s {
+    int64_t M, N, K;
+    int ab, c, tA, tB, clear, relu;
+    int variant;
+    int vec_a, vec_b;
+    tlg_plan_info info;
+    char desc[256];
+};
+
+namespace {
+
+constexpr int64_t kMaxMN = int64_t(1) << 24;
+constexpr int64_t kMaxK = int64_t(1) << 22;
+
+int elem_bytes(int dt) { return dt == TLG_F32 ? 4 : 2; }
+
+const char* dt_name(int dt)
+{
+    switch (dt) {
+    case TLG_F16: return "f16";
+    case TLG_BF16: return "bf16";
+    case TLG_F32: return "f32";
+    default: return "?";
+    }
+}
+
+const char* variant_name(int v)
+{
+    switch (v) {
+    case TLG_VARIANT_TILE_256: return "tile256";
+    case TLG_VARIANT_TILE_128: return "tile128";
+    case TLG_VARIANT_SKINNY: return "skinny";
+    case TLG_VARIANT_EMPTY: return "empty";
+    default: return "?";
+    }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 128-bit loads need the contiguous dimension of the operand to be a multiple
+// of 8 elements (every 16-byte chunk lies inside one row and is 16-byte aligned
+// when the base is); otherwise the operand is loaded element by element (the
+// narrow-load fallback for unaligned rows, "core primitives" chapter, T.copy
+// notes on alignment).
+int vec_for(int64_t contiguous_len) { return contiguous_len % 8 == 0 ? 8 : 1; }
+
+bool flag_ok(int v) { return v == 0 || v == 1; }
+
+tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB,
+                       int clear, int epi, int forced)
+{
+    if (!out) return TLG_ERR_NULL;
+    *out = nullptr;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
+    if (!flag_ok(tA) || !flag_ok(tB) || !flag_ok(clear)) return TLG_ERR_INVALID_ARG;
+    if (epi != TLG_EPI_NONE && epi != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
+    if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32) return TLG_ERR_INVALID_ARG;
+    if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
+    if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_SKINNY) return TLG_ERR_INVALID_ARG;
+
+    const int va = vec_for(tA ? M : K);
+    const int vb = vec_for(tB ? K : N);
+    const bool skinny_ok = !tA && tB && K % 8 == 0;
+
+    int variant;
+    if (M == 0 || N == 0) {
+        variant = TLG_VARIANT_EMPTY;
+    } else if (forced != TLG_VARIANT_AUTO) {
+        variant = forced;
+        if (forced == TLG_VARIANT_SKINNY && !skinny_ok) return TLG_ERR_UNSUPPORTED;
+        if (forced == TLG_VARIANT_TILE_256 && (va != 8 || vb != 8)) return TLG_ERR_UNSUPPORTED;
+    } else if (M <= kSkinnyRows && skinny_ok) {
+        variant = TLG_VARIANT_SKINNY;
+    } else if (va == 8 && vb == 8 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) {
+        variant = TLG_VARIANT_TILE_256;
+    } else {
+        variant = TLG_VARIANT_TILE_128;
+    }
+
+    // Launch-grid limits: the tile kernels use a 1-D grid of tile ids (int), the
+    // skinny kernel a 2-D grid with row blocks in y.
+    if (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_128) {
+        const int64_t b = variant == TLG_VARIANT_TILE_256 ? 256 : 128;
+        if (ceil_div(M, b) * ceil_div(N, b) > INT32_MAX) return TLG_ERR_INVALID_ARG;
+    } else if (variant == TLG_VARIANT_SKINNY) {
+        if (ceil_div(M, kSkinnyRows) > 65535 || ceil_div(N, kSkinnyNB) > INT32_MAX) return TLG_ERR_INVALID_ARG;
+    }
+
+    tlg_gemm_s* p = new (std::nothrow) tlg_gemm_s();
+    if (!p) return TLG_ERR_NOMEM;
+    p->M = M; p->N = N; p->K = K;
+    p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
+    p->variant = variant;
+    p->vec_a = variant == TLG_VARIANT_SKINNY ? 8 : va;
+    p->vec_b = variant == TLG_VARIANT_SKINNY ? 8 : vb;
+
+    tlg_plan_info& in = p->info;
+    in.variant = variant;
+    in.vec_a = p->vec_a;
+    in.vec_b = p->vec_b;
+    if (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_128) {
+        const TileShape ts = tile_shape(variant == TLG_VARIANT_TILE_256 ? TILE_256 : TILE_128);
+        in.block_m = ts.bm; in.block_n = ts.bn; in.block_k = ts.bk;
+        in.stages = ts.stages;
+        in.threads = ts.threads();
+        in.grid = ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
+        in.lds_bytes = (int64_t)ts.stages * (ts.bm + ts.bn) * ts.bk * 2;
+        in.k_tiles = (int32_t)ceil_div(K, ts.bk);
+    } else if (variant == TLG_VARIANT_SKINNY) {
+        in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = 32;
+        in.stages = 2;
+        in.threads = kSkinnyThreads;
+        in.grid = ceil_div(M, kSkinnyRows) * ceil_div(N, kSkinnyNB);
+        in.lds_bytes = (int64_t)(kSkinnyThreads / 64) * (kSkinnyNB / 16) * 4 * 64 * 4;
+        in.k_tiles = (int32_t)ceil_div(K, 32);
+    }
+    std::snprintf(p->desc, sizeof(p->desc),
+                  "%s M=%lld N=%lld K=%lld ab=%s c=%s tA=%d tB=%d clear=%d relu=%d block=%dx%dx%d "
+                  "stages=%d threads=%d grid=%lld lds=%lld vec=%d/%d",
+                  variant_name(variant), (long long)M, (long long)N, (long long)K, dt_name(ab), dt_name(c), tA,
+                  tB, clear, p->relu, in.block_m, in.block_n, in.block_k, in.stages, in.threads,
+                  (long long)in.grid, (long long)in.lds_bytes, in.vec_a, in.vec_b);
+    *out = p;
+    return TLG_OK;
+}
+
+bool ranges_overlap(uintptr_t a, uint64_t an, uintptr_t b, uint64_t bn)
+{
+    if (an == 0 || bn == 0) return false;
+    return a < b + bn && b < a + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+tlg_status tlg_gemm_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                           int32_t transpose_A, int32_t transpose_B, int32_t clear_accum, int32_t epilogue)
+{
+    return plan_create(out, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                       TLG_VARIANT_AUTO);
+}
+
+tlg_status tlg_gemm_create_variant(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int32_t ab_dtype,
+                                   int32_t c_dtype, int32_t transpose_A, int32_t transpose_B,
+                                   int32_t clear_accum, int32_t epilogue, int32_t variant)
+{
+    return plan_create(out, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                       variant);
+}
+
+tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, void* stream)
+{
+    if (!plan) return TLG_ERR_NULL;
+    const tlg_gemm_s& p = *plan;
+    if (p.variant == TLG_VARIANT_EMPTY) return TLG_OK;
+    if (!C) return TLG_ERR_NULL;
+    if (p.K > 0 && (!A || !B)) return TLG_ERR_NULL;
+
+    const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
+    const int cb = elem_bytes(p.c);
+    if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
+    if (p.K > 0) {
+        if ((a % 2) || (b % 2)) return TLG_ERR_MISALIGNED;
+        if ((p.vec_a == 8 && a % 16) || (p.vec_b == 8 && b % 16)) return TLG_ERR_MISALIGNED;
+    }
+    const uint64_t a_bytes = p.K > 0 ? (uint64_t)p.M * (uint64_t)p.K * 2u : 0;
+    const uint64_t b_bytes = p.K > 0 ? (uint64_t)p.K * (uint64_t)p.N * 2u : 0;
+    const uint64_t c_bytes = (uint64_t)p.M * (uint64_t)p.N * (uint64_t)cb;
+    if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, b, b_bytes))
+        return TLG_ERR_INVALID_ARG;
+
+    GemmParams gp{};
+    gp.A = A; gp.B = B; gp.C = C;
+    gp.M = (int)p.M; gp.N = (int)p.N; gp.K = (int)p.K;
+    gp.relu = p.relu;
+    gp.clear_accum = p.clear;
+    gp.c_dtype = p.c;
+    gp.c_vec = (p.N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+
+    hipError_t err;
+    if (p.variant == TLG_VARIANT_SKINNY) {
+        gp.tiles_m = (int)ceil_div(p.M, kSkinnyRows);
+        gp.tiles_n = (int)ceil_div(p.N, kSkinnyNB);
+        err = launch_skinny(gp, p.ab, (hipStream_t)stream);
+    } else {
+        const int cfg = p.variant == TLG_VARIANT_TILE_256 ? TILE_256 : TILE_128;
+        const TileShape ts = tile_shape(cfg);
+        gp.tiles_m = (int)ceil_div(p.M, ts.bm);
+        gp.tiles_n = (int)ceil_div(p.N, ts.bn);
+        err = launch_tile(cfg, gp, p.ab, p.tA, p.tB, p.vec_a, p.vec_b, (hipStream_t)stream);
+    }
+    return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
+tlg_status tlg_gemm_destroy(tlg_gemm_t plan)
+{
+    delete plan;
+    return TLG_OK;
+}
+
+tlg_status tlg_gemm_query(tlg_gemm_t plan, tlg_plan_info* info)
+{
+    if (!plan || !info) return TLG_ERR_NULL;
+    *info = plan->info;
+    return TLG_OK;
+}
+
+const char* tlg_gemm_describe(tlg_gemm_t plan) { return plan ? plan->desc : "(null plan)"; }
+
+const char* tlg_status_string(int32_t status)
+{
+    switch (status) {
+    case TLG_OK: return "TLG_OK";
+    case TLG_ERR_INVALID_ARG: return "TLG_ERR_INVALID_ARG";
+    case TLG_ERR_UNSUPPORTED: return "TLG_ERR_UNSUPPORTED";
+    case TLG_ERR_NULL: return "TLG_ERR_NULL";
+    case TLG_ERR_MISALIGNED: return "TLG_ERR_MISALIGNED";
+    case TLG_ERR_HIP: return "TLG_ERR_HIP";
+    case TLG_ERR_NOMEM: return "TLG_ERR_NOMEM";
+    default: return "TLG_ERR_UNKNOWN";
+    }
+}
+
+const char* tlg_version(void) { return "tlg 0.1.0 (gfx950)"; }
+
+}  // extern "C"

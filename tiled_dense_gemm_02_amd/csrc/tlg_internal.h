@@ -1,0 +1,71 @@
+// Internal interface between the C-ABI layer (tlg_api.cpp) and the kernel
+// translation units.  Not installed; not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tlg {
+
+enum : int { DT_F16 = 1, DT_BF16 = 2, DT_F32 = 3 };
+
+// Arguments of one launch (passed by value to the kernels).
+struct GemmParams {
+    const void* A;
+    const void* B;
+    void* C;
+    int M, N, K;
+    int relu;         // 1: ReLU epilogue
+    int clear_accum;  // 0: add onto C's prior contents
+    int c_dtype;      // DT_F16 / DT_BF16 / DT_F32
+    int c_vec;        // 1: N % 4 == 0 and C aligned to 4 elements (vector stores allowed)
+    int tiles_m;      // output tiles along M (tile kernels) / row blocks (skinny)
+    int tiles_n;      // output tiles along N
+};
+
+// Block-tile configurations of the tiled kernel.
+enum TileConfig : int { TILE_256 = 1, TILE_128 = 2 };
+
+struct TileShape {
+    int bm, bn, bk, waves_m, waves_n, stages;
+    int threads() const { return 64 * waves_m * waves_n; }
+};
+
+inline TileShape tile_shape(int cfg)
+{
+    if (cfg == TILE_256) return TileShape{256, 256, 64, 2, 2, 2};
+    return TileShape{128, 128, 64, 2, 1, 2};
+}
+
+// Skinny kernel geometry: 16 rows x kSkinnyNB columns per workgroup, 4 waves
+// splitting K.
+constexpr int kSkinnyRows = 16;
+constexpr int kSkinnyNB = 64;
+constexpr int kSkinnyThreads = 256;
+
+// Launchers (defined in the kernel translation units).  vec_a / vec_b: 8 for
+// 128-bit global loads, 1 for 16-bit loads.
+hipError_t launch_tile_256_f16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
+                              int vec_b, hipStream_t stream);
+hipError_t launch_tile_256_bf16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
+                               int vec_b, hipStream_t stream);
+hipError_t launch_tile_128_f16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
+                              int vec_b, hipStream_t stream);
+hipError_t launch_tile_128_bf16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
+                               int vec_b, hipStream_t stream);
+
+inline hipError_t launch_tile(int cfg, const GemmParams& p, int ab_dtype, int transpose_A,
+                              int transpose_B, int vec_a, int vec_b, hipStream_t stream)
+{
+    const bool f16 = ab_dtype == DT_F16;
+    if (cfg == TILE_256)
+        return f16 ? launch_tile_256_f16(p, transpose_A, transpose_B, vec_a, vec_b, stream)
+                   : launch_tile_256_bf16(p, transpose_A, transpose_B, vec_a, vec_b, stream);
+    if (cfg == TILE_128)
+        return f16 ? launch_tile_128_f16(p, transpose_A, transpose_B, vec_a, vec_b, stream)
+                   : launch_tile_128_bf16(p, transpose_A, transpose_B, vec_a, vec_b, stream);
+    return hipErrorInvalidValue;
+}
+hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
+
+}  // namespace tlg
