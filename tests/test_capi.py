@@ -82,11 +82,11 @@ def test_variant_choice_and_geometry_for_the_workloads():
     i = plan(C["c2"]).info
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (2, 128, 128, 64, 64, 16)
     i = plan(C["c3"]).info
-    assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes) == (1, 256, 256, 64, 131072)
+    assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (5, 256, 256, 64, 131072, 512)
     i = plan(C["c4"]).info
     assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles) == (2, 1, 1, 8 * 12, 13)
     i = plan(C["c5a"]).info
-    assert (i.variant, i.grid, i.k_tiles) == (1, 1024, 128)
+    assert (i.variant, i.grid, i.k_tiles) == (5, 1024, 128)
     i = plan(C["c5b"]).info
     assert (i.variant, i.grid, i.vec_a, i.vec_b) == (3, 256, 8, 8)
     assert "skinny" in plan(C["c5b"]).describe()

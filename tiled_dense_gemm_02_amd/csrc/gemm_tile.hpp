@@ -97,23 +97,30 @@ struct TileLoader<true, VEC, R, THREADS> {
 };
 
 // Operand stored [K][rows_total] (its M or N index contiguous): A with
-// transpose_A = 1, B with transpose_B = 0.  Each work-item loads one 8 (K) x 8
-// (rows) block as eight 16-byte row pieces (lanes 0..31 of a wave cover 512
-// contiguous bytes of one K row), transposes it in registers and writes eight
-// K-contiguous 16-byte chunks.
+// transpose_A = 1, B with transpose_B = 0.  Each work-item loads blocks of KR
+// K rows x 8 contiguous elements (lanes 0..31 of a wave cover 512 contiguous
+// bytes of one K row), transposes each block in registers and writes eight
+// K-contiguous pieces of KR elements (16 or 8 bytes).  KR is 8 when there are
+// enough 8x8 blocks for every work-item, else 4.
+template <int R, int THREADS>
+struct MnBlock {
+    static constexpr int kKR = ((R / 8) * (kBK / 8)) % THREADS == 0 ? 8 : 4;
+};
+
 template <int VEC, int R, int THREADS>
 struct TileLoader<false, VEC, R, THREADS> {
+    static constexpr int KR = MnBlock<R, THREADS>::kKR;
     static constexpr int kBlocksR = R / 8;
-    static constexpr int kBlocks = kBlocksR * (kBK / 8);
+    static constexpr int kBlocks = kBlocksR * (kBK / KR);
     static constexpr int kPer = kBlocks / THREADS;
-    static_assert(kBlocks % THREADS == 0 && kPer >= 1, "8x8 blocks must divide evenly over the workgroup");
+    static_assert(kBlocks % THREADS == 0 && kPer >= 1, "KR x 8 blocks must divide evenly over the workgroup");
 
     const char* base;        // element (0, r0)
     uint64_t base_bytes;     // bytes from base to the end of the matrix
     uint32_t ld_bytes;       // rows_total * 2
     int rows_valid;          // rows_total - r0
     int K;
-    u32x4 v[kPer][8];
+    u32x4 v[kPer][KR];
 
     __device__ void init(const void* ptr, int r0, int rows_total, int K_)
     {
@@ -131,10 +138,10 @@ struct TileLoader<false, VEC, R, THREADS> {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int q = i * THREADS + (int)threadIdx.x;
-            const int rc = q % kBlocksR, kg = q / kBlocksR;
+            const int rc = q % kBlocksR, kb = q / kBlocksR;
 #pragma unroll
-            for (int kr = 0; kr < 8; ++kr) {
-                const int kl = kg * 8 + kr;
+            for (int kr = 0; kr < KR; ++kr) {
+                const int kl = kb * KR + kr;
                 const bool k_ok = k0 + kl < K;
                 if constexpr (VEC == 8) {
                     const bool ok = k_ok && (rc * 8 < rows_valid);
@@ -158,17 +165,22 @@ struct TileLoader<false, VEC, R, THREADS> {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
             const int q = i * THREADS + (int)threadIdx.x;
-            const int rc = q % kBlocksR, kg = q / kBlocksR;
+            const int rc = q % kBlocksR, kb = q / kBlocksR;
+            const int chunk = (kb * KR) >> 3, sub = (kb * KR) & 7;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                // column j of the block: element j of each of the eight K rows
-                u32x4 o;
+                // column j of the block: element j of each of the KR K rows
+                uint32_t o[KR / 2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < KR / 2; ++e) {
                     const uint32_t lo = v[i][2 * e][j >> 1], hi = v[i][2 * e + 1][j >> 1];
                     o[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
                 }
-                *(u32x4*)(lds + lds_elem(rc * 8 + j, kg)) = o;
+                uint16_t* dst = lds + lds_elem(rc * 8 + j, chunk) + sub;
+                if constexpr (KR == 8)
+                    *(u32x4*)dst = u32x4{o[0], o[1], o[2], o[3]};
+                else
+                    *(u32x2*)dst = u32x2{o[0], o[1]};
             }
         }
     }
@@ -235,7 +247,31 @@ gemm_tile_kernel(GemmParams p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // Prologue: stage 0.
+    // Fragment rows of this lane and the chunk half (K 0..7 or 8..15 of a 16-K step).
+    const int a_row = wm * WTM + (lane & 31);
+    const int b_row = wn * WTN + (lane & 31);
+    const int khalf = lane >> 5;
+
+    // One 16-wide K step: FM A fragments and FN B fragments (one 16-byte LDS read each).
+    auto load_frags = [&](const uint16_t* st, int kk, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+        const int c = kk * 2 + khalf;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = *(const u32x4*)(st + lds_elem(a_row + i * 32, c));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf[j] = *(const u32x4*)(st + A_ELEMS + lds_elem(b_row + j * 32, c));
+    };
+    auto mma = [&](const u32x4 (&af)[FM], const u32x4 (&bf)[FN]) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16<T_IN>(bf[j], af[i], acc[i][j]);
+    };
+
+    // Software pipeline over K tiles (two LDS buffers).  The fragments of the
+    // next 16-wide K step are read while the current step's MFMAs run; the next
+    // K tile's global loads are issued at the top of an iteration and land in
+    // the other LDS buffer before its closing barrier.
+    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
     if (KT > 0) {
         la.load(0);
         lb.load(0);
@@ -243,39 +279,42 @@ gemm_tile_kernel(GemmParams p)
         lb.store(smem[0] + A_ELEMS);
     }
     __syncthreads();
+    if (KT > 0) load_frags(smem[0], 0, fa0, fb0);
 
-    // Fragment rows of this lane and the chunk half (K 0..7 or 8..15 of a 16-K step).
-    const int a_row = wm * WTM + (lane & 31);
-    const int b_row = wn * WTN + (lane & 31);
-    const int khalf = lane >> 5;
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool has_next = kt + 1 < KT;
-        if (has_next) {
-            la.load((kt + 1) * kBK);
-            lb.load((kt + 1) * kBK);
-        }
-        const uint16_t* sa = smem[cur];
-        const uint16_t* sb = smem[cur] + A_ELEMS;
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int c = kk * 2 + khalf;
-            u32x4 af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; ++i) af[i] = *(const u32x4*)(sa + lds_elem(a_row + i * 32, c));
-#pragma unroll
-            for (int j = 0; j < FN; ++j) bf[j] = *(const u32x4*)(sb + lds_elem(b_row + j * 32, c));
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16<T_IN>(bf[j], af[i], acc[i][j]);
-        }
-        if (has_next) {
-            la.store(smem[cur ^ 1]);
-            lb.store(smem[cur ^ 1] + A_ELEMS);
-        }
+    // sched_barrier(0) fences keep the compiler from sinking the global loads
+    // next to their use (which would serialise the pipeline) and keep each
+    // phase's fragment reads ahead of the MFMAs that overlap them.
+    for (int kt = 0; kt < KT - 1; ++kt) {
+        const uint16_t* cur = smem[kt & 1];
+        uint16_t* nxt = smem[(kt & 1) ^ 1];
+        la.load((kt + 1) * kBK);
+        lb.load((kt + 1) * kBK);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 1, fa1, fb1);
+        mma(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 2, fa0, fb0);
+        mma(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(cur, 3, fa1, fb1);
+        mma(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        la.store(nxt);
+        lb.store(nxt + A_ELEMS);
+        mma(fa1, fb1);
         __syncthreads();
+        load_frags(nxt, 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (KT > 0) {
+        const uint16_t* cur = smem[(KT - 1) & 1];
+        load_frags(cur, 1, fa1, fb1);
+        mma(fa0, fb0);
+        load_frags(cur, 2, fa0, fb0);
+        mma(fa1, fb1);
+        load_frags(cur, 3, fa1, fb1);
+        mma(fa0, fb0);
+        mma(fa1, fb1);
     }
 
     // Epilogue.  acc[i][j][4g + e] is C[m][n + e] with

@@ -50,6 +50,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_TILE_128: return "tile128";
     case TLG_VARIANT_SKINNY: return "skinny";
     case TLG_VARIANT_EMPTY: return "empty";
+    case TLG_VARIANT_TILE_256_W8: return "tile256w8";
     default: return "?";
     }
 }
@@ -65,6 +66,18 @@ int vec_for(int64_t contiguous_len) { return contiguous_len % 8 == 0 ? 8 : 1; }
 
 bool flag_ok(int v) { return v == 0 || v == 1; }
 
+bool is_tile(int v)
+{
+    return v == TLG_VARIANT_TILE_256 || v == TLG_VARIANT_TILE_128 || v == TLG_VARIANT_TILE_256_W8;
+}
+
+int tile_config(int v)
+{
+    if (v == TLG_VARIANT_TILE_256) return TILE_256;
+    if (v == TLG_VARIANT_TILE_256_W8) return TILE_256_W8;
+    return TILE_128;
+}
+
 tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB,
                        int clear, int epi, int forced)
 {
@@ -76,7 +89,8 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_SKINNY) return TLG_ERR_INVALID_ARG;
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_256_W8 || forced == TLG_VARIANT_EMPTY)
+        return TLG_ERR_INVALID_ARG;
 
     const int va = vec_for(tA ? M : K);
     const int vb = vec_for(tB ? K : N);
@@ -88,19 +102,20 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     } else if (forced != TLG_VARIANT_AUTO) {
         variant = forced;
         if (forced == TLG_VARIANT_SKINNY && !skinny_ok) return TLG_ERR_UNSUPPORTED;
-        if (forced == TLG_VARIANT_TILE_256 && (va != 8 || vb != 8)) return TLG_ERR_UNSUPPORTED;
+        if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
+            return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
         variant = TLG_VARIANT_SKINNY;
     } else if (va == 8 && vb == 8 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) {
-        variant = TLG_VARIANT_TILE_256;
+        variant = TLG_VARIANT_TILE_256_W8;
     } else {
         variant = TLG_VARIANT_TILE_128;
     }
 
     // Launch-grid limits: the tile kernels use a 1-D grid of tile ids (int), the
     // skinny kernel a 2-D grid with row blocks in y.
-    if (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_128) {
-        const int64_t b = variant == TLG_VARIANT_TILE_256 ? 256 : 128;
+    if (is_tile(variant)) {
+        const int64_t b = variant == TLG_VARIANT_TILE_128 ? 128 : 256;
         if (ceil_div(M, b) * ceil_div(N, b) > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
         if (ceil_div(M, kSkinnyRows) > 65535 || ceil_div(N, kSkinnyNB) > INT32_MAX) return TLG_ERR_INVALID_ARG;
@@ -118,8 +133,8 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     in.variant = variant;
     in.vec_a = p->vec_a;
     in.vec_b = p->vec_b;
-    if (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_128) {
-        const TileShape ts = tile_shape(variant == TLG_VARIANT_TILE_256 ? TILE_256 : TILE_128);
+    if (is_tile(variant)) {
+        const TileShape ts = tile_shape(tile_config(variant));
         in.block_m = ts.bm; in.block_n = ts.bn; in.block_k = ts.bk;
         in.stages = ts.stages;
         in.threads = ts.threads();
@@ -204,7 +219,7 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_n = (int)ceil_div(p.N, kSkinnyNB);
         err = launch_skinny(gp, p.ab, (hipStream_t)stream);
     } else {
-        const int cfg = p.variant == TLG_VARIANT_TILE_256 ? TILE_256 : TILE_128;
+        const int cfg = tile_config(p.variant);
         const TileShape ts = tile_shape(cfg);
         gp.tiles_m = (int)ceil_div(p.M, ts.bm);
         gp.tiles_n = (int)ceil_div(p.N, ts.bn);

@@ -24,7 +24,7 @@ struct GemmParams {
 };
 
 // Block-tile configurations of the tiled kernel.
-enum TileConfig : int { TILE_256 = 1, TILE_128 = 2 };
+enum TileConfig : int { TILE_256 = 1, TILE_128 = 2, TILE_256_W8 = 3 };
 
 struct TileShape {
     int bm, bn, bk, waves_m, waves_n, stages;
@@ -34,6 +34,7 @@ struct TileShape {
 inline TileShape tile_shape(int cfg)
 {
     if (cfg == TILE_256) return TileShape{256, 256, 64, 2, 2, 2};
+    if (cfg == TILE_256_W8) return TileShape{256, 256, 64, 2, 4, 2};
     return TileShape{128, 128, 64, 2, 1, 2};
 }
 
@@ -49,6 +50,10 @@ hipError_t launch_tile_256_f16(const GemmParams& p, int transpose_A, int transpo
                               int vec_b, hipStream_t stream);
 hipError_t launch_tile_256_bf16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
                                int vec_b, hipStream_t stream);
+hipError_t launch_tile_256w8_f16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
+                                int vec_b, hipStream_t stream);
+hipError_t launch_tile_256w8_bf16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
+                                 int vec_b, hipStream_t stream);
 hipError_t launch_tile_128_f16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
                               int vec_b, hipStream_t stream);
 hipError_t launch_tile_128_bf16(const GemmParams& p, int transpose_A, int transpose_B, int vec_a,
@@ -61,6 +66,9 @@ inline hipError_t launch_tile(int cfg, const GemmParams& p, int ab_dtype, int tr
     if (cfg == TILE_256)
         return f16 ? launch_tile_256_f16(p, transpose_A, transpose_B, vec_a, vec_b, stream)
                    : launch_tile_256_bf16(p, transpose_A, transpose_B, vec_a, vec_b, stream);
+    if (cfg == TILE_256_W8)
+        return f16 ? launch_tile_256w8_f16(p, transpose_A, transpose_B, vec_a, vec_b, stream)
+                   : launch_tile_256w8_bf16(p, transpose_A, transpose_B, vec_a, vec_b, stream);
     if (cfg == TILE_128)
         return f16 ? launch_tile_128_f16(p, transpose_A, transpose_B, vec_a, vec_b, stream)
                    : launch_tile_128_bf16(p, transpose_A, transpose_B, vec_a, vec_b, stream);
