@@ -61,6 +61,8 @@ def test_create_rejects_bad_arguments():
     assert _create(16, 64, 777, tB=1, variant=3)[0] == UNSUPPORTED      # skinny needs K % 8 == 0
     assert _create(16, 64, 64, tB=0, variant=3)[0] == UNSUPPORTED       # skinny needs B stored [N,K]
     assert _create(100, 100, 777, variant=1)[0] == UNSUPPORTED          # 256 tile needs 128-bit loads
+    assert _create(100, 100, 777, variant=6)[0] == UNSUPPORTED
+    assert _create(100, 100, 96, variant=4)[0] == INVALID               # EMPTY is chosen, never forced
     assert lib.tlg_gemm_destroy(None) == OK
 
 
@@ -82,11 +84,11 @@ def test_variant_choice_and_geometry_for_the_workloads():
     i = plan(C["c2"]).info
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (2, 128, 128, 64, 64, 16)
     i = plan(C["c3"]).info
-    assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (5, 256, 256, 64, 131072, 512)
+    assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (6, 256, 256, 64, 131072, 512)
     i = plan(C["c4"]).info
     assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles) == (2, 1, 1, 8 * 12, 13)
     i = plan(C["c5a"]).info
-    assert (i.variant, i.grid, i.k_tiles) == (5, 1024, 128)
+    assert (i.variant, i.grid, i.k_tiles) == (6, 1024, 128)
     i = plan(C["c5b"]).info
     assert (i.variant, i.grid, i.vec_a, i.vec_b) == (3, 256, 8, 8)
     assert "skinny" in plan(C["c5b"]).describe()

@@ -51,6 +51,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_SKINNY: return "skinny";
     case TLG_VARIANT_EMPTY: return "empty";
     case TLG_VARIANT_TILE_256_W8: return "tile256w8";
+    case TLG_VARIANT_TILE_256_DMA: return "tile256dma";
     default: return "?";
     }
 }
@@ -89,7 +90,7 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_256_W8 || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
 
     const int va = vec_for(tA ? M : K);
@@ -102,19 +103,20 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     } else if (forced != TLG_VARIANT_AUTO) {
         variant = forced;
         if (forced == TLG_VARIANT_SKINNY && !skinny_ok) return TLG_ERR_UNSUPPORTED;
-        if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
+        if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8 ||
+             forced == TLG_VARIANT_TILE_256_DMA) && (va != 8 || vb != 8))
             return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
         variant = TLG_VARIANT_SKINNY;
     } else if (va == 8 && vb == 8 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) {
-        variant = TLG_VARIANT_TILE_256_W8;
+        variant = TLG_VARIANT_TILE_256_DMA;
     } else {
         variant = TLG_VARIANT_TILE_128;
     }
 
     // Launch-grid limits: the tile kernels use a 1-D grid of tile ids (int), the
     // skinny kernel a 2-D grid with row blocks in y.
-    if (is_tile(variant)) {
+    if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA) {
         const int64_t b = variant == TLG_VARIANT_TILE_128 ? 128 : 256;
         if (ceil_div(M, b) * ceil_div(N, b) > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
@@ -141,6 +143,13 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         in.grid = ceil_div(M, ts.bm) * ceil_div(N, ts.bn);
         in.lds_bytes = (int64_t)ts.stages * (ts.bm + ts.bn) * ts.bk * 2;
         in.k_tiles = (int32_t)ceil_div(K, ts.bk);
+    } else if (variant == TLG_VARIANT_TILE_256_DMA) {
+        in.block_m = kLdsBM; in.block_n = kLdsBN; in.block_k = kLdsBK;
+        in.stages = kLdsStages;
+        in.threads = kLdsThreads;
+        in.grid = ceil_div(M, kLdsBM) * ceil_div(N, kLdsBN);
+        in.lds_bytes = (int64_t)kLdsStages * (kLdsBM + kLdsBN) * kLdsBK * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
     } else if (variant == TLG_VARIANT_SKINNY) {
         in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = 32;
         in.stages = 2;
@@ -218,6 +227,11 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_m = (int)ceil_div(p.M, kSkinnyRows);
         gp.tiles_n = (int)ceil_div(p.N, kSkinnyNB);
         err = launch_skinny(gp, p.ab, (hipStream_t)stream);
+    } else if (p.variant == TLG_VARIANT_TILE_256_DMA) {
+        gp.tiles_m = (int)ceil_div(p.M, kLdsBM);
+        gp.tiles_n = (int)ceil_div(p.N, kLdsBN);
+        err = p.ab == TLG_F16 ? launch_lds_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                              : launch_lds_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else {
         const int cfg = tile_config(p.variant);
         const TileShape ts = tile_shape(cfg);

@@ -76,4 +76,9 @@ inline hipError_t launch_tile(int cfg, const GemmParams& p, int ab_dtype, int tr
 }
 hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
 
+// Direct-load ring kernel (256x256x64 tile, 8 waves); 128-bit loads only.
+constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64, kLdsStages = 2, kLdsThreads = 512;
+hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+
 }  // namespace tlg
