@@ -91,6 +91,19 @@ __device__ inline u32x2 lds_read_tr16(const char* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
+// Scheduling groups for one K step: MPS MFMAs, each followed by its share of the
+// RPS LDS reads of the next step (sched_group_barrier masks: 0x008 MFMA, 0x100 DS read).
+template <int RPS, int MPS, int R>
+__device__ inline void sched_mfma_with_reads()
+{
+    if constexpr (R < MPS) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        constexpr int nr = RPS * (R + 1) / MPS - RPS * R / MPS;
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
+        sched_mfma_with_reads<RPS, MPS, R + 1>();
+    }
+}
+
 template <int BK>
 __device__ __host__ constexpr int swz_kc(int row)
 {
@@ -98,48 +111,55 @@ __device__ __host__ constexpr int swz_kc(int row)
     return (row / (16 / CH)) % CH;
 }
 
-// One operand of the 256 x 256 tile: 256 rows of its M/N index x BK of K.
-template <int BK, bool KC>
+// One operand of the 256 x 256 tile: 256 rows of its M/N index x BK of K,
+// filled by NW waves (each direct load fills one 1 KiB block).
+template <int BK, bool KC, int NW>
 struct LdsOperand {
     static constexpr int R = 256;
     static constexpr int BYTES = R * BK * 2;
-    static constexpr int L = BYTES / (512 * 16);  // direct loads per lane per tile
+    static constexpr int L = BYTES / (NW * 64 * 16);  // direct loads per lane per tile
+    static_assert(BYTES % (NW * 1024) == 0, "blocks must divide evenly over the waves");
     static constexpr int RB = BK * 2, CH = BK / 8;
+
+    // Load i of a lane covers block b = i * NW + wave.  Along i the lane's row
+    // (K-contiguous) or k (M/N-contiguous) advances by a constant step, and the
+    // swizzle term is unchanged by that step, so one base offset per lane
+    // describes all L loads.
+    static constexpr int DROW = NW * (1024 / RB);   // K-contiguous: rows per load step
+    static constexpr int DK = 2 * NW;               // M/N-contiguous: k rows per load step
+    static_assert(!KC || (4 * NW) % CH == 0, "swizzle must be invariant along the load step");
+    static_assert(KC || NW % 2 == 0, "swizzle must be invariant along the load step");
 
     const char* base;       // element (row r0, k 0)       [K-contig]  /  (k 0, row r0)  [M/N-contig]
     uint64_t base_bytes;    // bytes from base to the end of the matrix
     uint32_t ld;            // row pitch in bytes
-    uint32_t off[L];
-    int kpos[L];            // K offset of the lane's chunk within a tile
-    bool ok[L];
+    uint32_t off0;          // byte offset of load 0 relative to base
+    int idx0;               // K-contig: row of load 0 (relative to r0); M/N-contig: k of load 0
+    int kc;                 // K-contig: first K element of the lane's chunk
+    int rows_left;          // rows_total - r0
+    bool col_ok;            // M/N-contig: the lane's 8 columns lie inside the matrix
 
     __device__ void init(const void* ptr, int r0, int rows_total, int K, int lane, int wave)
     {
+        rows_left = rows_total - r0;
         if constexpr (KC) {
             ld = (uint32_t)K * 2u;
             base = (const char*)ptr + (uint64_t)r0 * ld;
             base_bytes = (uint64_t)(rows_total - r0) * ld;
+            idx0 = wave * (1024 / RB) + lane / CH;
+            const int c = (lane % CH) ^ swz_kc<BK>(idx0);
+            off0 = (uint32_t)idx0 * ld + (uint32_t)c * 16u;
+            kc = c * 8;
+            col_ok = true;
         } else {
             ld = (uint32_t)rows_total * 2u;
             base = (const char*)ptr + (uint64_t)r0 * 2u;
             base_bytes = (uint64_t)K * ld - (uint64_t)r0 * 2u;
-        }
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
-            const int b = i * 8 + wave;  // 1 KiB block of the slot filled by this load
-            if constexpr (KC) {
-                const int row = b * (1024 / RB) + lane / CH;
-                const int c = (lane % CH) ^ swz_kc<BK>(row);
-                ok[i] = r0 + row < rows_total;
-                off[i] = (uint32_t)row * ld + (uint32_t)c * 16u;
-                kpos[i] = c * 8;
-            } else {
-                const int k = 2 * b + (lane >> 5);
-                const int c = (lane & 31) ^ ((k & 3) << 2);
-                ok[i] = r0 + c * 8 < rows_total;
-                off[i] = (uint32_t)k * ld + (uint32_t)c * 16u;
-                kpos[i] = k;
-            }
+            idx0 = 2 * wave + (lane >> 5);
+            const int c = (lane & 31) ^ ((idx0 & 3) << 2);
+            off0 = (uint32_t)idx0 * ld + (uint32_t)c * 16u;
+            kc = 0;
+            col_ok = c * 8 < rows_left;
         }
     }
 
@@ -147,11 +167,21 @@ struct LdsOperand {
     __device__ void issue(int k0, int K, uint32_t lds_region) const
     {
         const uint64_t o = KC ? (uint64_t)k0 * 2u : (uint64_t)k0 * ld;
-        const i32x4 r = rsrc_words(base + o, base_bytes - o);
+        // Slots past the end of K (padding of the last iteration) get an empty
+        // resource; all their lanes are out of range and receive zeros.
+        const i32x4 r = rsrc_words(base + o, o < base_bytes ? base_bytes - o : 0);
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            const bool valid = ok[i] && (k0 + kpos[i] < K);
-            dma16(r, valid ? off[i] : kOOB, lds_region + (uint32_t)(i * 8 * 1024));
+            bool valid;
+            uint32_t off;
+            if constexpr (KC) {
+                valid = (idx0 + i * DROW < rows_left) && (k0 + kc < K);
+                off = off0 + (uint32_t)(i * DROW) * ld;
+            } else {
+                valid = col_ok && (k0 + idx0 + i * DK < K);
+                off = off0 + (uint32_t)(i * DK) * ld;
+            }
+            dma16(r, valid ? off : kOOB, lds_region + (uint32_t)(i * NW * 1024));
         }
     }
 
@@ -175,21 +205,32 @@ struct LdsOperand {
     }
 };
 
-template <int BK, int S, int T_IN, bool A_KC, bool B_KC>
-__global__ void __launch_bounds__(512)
+// BKS: K width of one ring slot; SPI: slots consumed per barrier; S: ring slots.
+// Slot t holds K tile t (t % S).  Iteration j multiplies tiles j*SPI .. j*SPI+SPI-1
+// and requests tiles up to j*SPI + S - 1, so every request has S - SPI slots of
+// time to land while the barrier count stays at one per SPI*BKS of K.
+// PF (needs S >= 2*SPI + 1): an iteration's barrier also publishes the first
+// tile of the next iteration, whose first fragments are then read before the
+// next barrier, so no wave starts an iteration waiting on LDS.
+template <int BKS, int SPI, int S, bool PF, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_lds_kernel(GemmParams p)
 {
-    constexpr int BM = 256, BN = 256, WAVES_N = 4;
-    constexpr int WTM = 128, WTN = 64, FM = WTM / 32, FN = WTN / 32;
-    using OpA = LdsOperand<BK, A_KC>;
-    using OpB = LdsOperand<BK, B_KC>;
+    constexpr int BM = 256, BN = 256, NW = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 32, FN = WTN / 32;
+    using OpA = LdsOperand<BKS, A_KC, NW>;
+    using OpB = LdsOperand<BKS, B_KC, NW>;
     constexpr int STAGE = OpA::BYTES + OpB::BYTES;
-    constexpr int L = OpA::L + OpB::L;
-    constexpr int KSTEPS = BK / 16;
-    static_assert(BK == 32 || BK == 64, "BK");
-    static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
-    static_assert((S - 2) * L < 64, "vmcnt range");
-    static_assert(KSTEPS % 2 == 0, "fragment double buffering steps by two");
+    constexpr int L = OpA::L + OpB::L;              // direct loads per lane per slot
+    constexpr int KS = BKS / 16;                     // 16-wide K steps per slot
+    constexpr int STEPS = SPI * KS;                  // K steps per iteration
+    // Slots allowed in flight when an iteration starts (the ones it does not read).
+    constexpr int AHEAD = PF ? S - 2 * SPI - 1 : S - 2 * SPI;
+    static_assert(BKS == 32 || BKS == 64, "slot width");
+    static_assert(SPI >= 1 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
+    static_assert(AHEAD >= 0, "ring too short for the requested prefetch");
+    static_assert(AHEAD * L < 64, "vmcnt range");
+    static_assert(STEPS % 2 == 0, "fragment double buffering steps by two");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -201,7 +242,8 @@ gemm_lds_kernel(GemmParams p)
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;
-    const int KT = (K + BK - 1) / BK;
+    const int J = (K + SPI * BKS - 1) / (SPI * BKS);   // iterations
+    const int TP = J * SPI;                             // slots requested (tail slots zero-filled)
 
     OpA opa;
     OpB opb;
@@ -212,8 +254,8 @@ gemm_lds_kernel(GemmParams p)
     auto issue = [&](int t) {
         const uint32_t slot =
             __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t % S) * STAGE) + (uint32_t)wave * 1024u);
-        opa.issue(t * BK, K, slot);
-        opb.issue(t * BK, K, slot + (uint32_t)OpA::BYTES);
+        opa.issue(t * BKS, K, slot);
+        opb.issue(t * BKS, K, slot + (uint32_t)OpA::BYTES);
     };
     auto load_frags = [&](const char* slot, int kk, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
 #pragma unroll
@@ -240,34 +282,73 @@ gemm_lds_kernel(GemmParams p)
     };
 
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-        if (t < KT) issue(t);
+    for (int t = 0; t < S - SPI; ++t)
+        if (t < TP) issue(t);
 
-    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-    for (int kt = 0; kt < KT; ++kt) {
-        // Tile kt has landed once at most min(S-2, KT-1-kt) newer tiles are
-        // still in flight; the barrier then publishes every wave's part of it
-        // and retires all reads of the slot that the next request overwrites.
-        if (kt + S - 2 < KT)
-            wait_vmcnt<(S - 2) * L>();
+    // Wait until the slots read before the next barrier have landed: at most
+    // AHEAD newer slots may still be in flight (fewer near the end, where
+    // everything is drained).  The caller's barrier then publishes every wave's
+    // part and retires all reads of the slots that get overwritten next.
+    auto wait_ring = [&](int j) {
+        if ((j + 1) * SPI + (PF ? 1 : 0) + AHEAD <= TP)
+            wait_vmcnt<AHEAD * L>();
         else
             wait_vmcnt<0>();
-        __syncthreads();
-        if (kt + S - 1 < KT) issue(kt + S - 1);
-        const char* slot = smem + (kt % S) * STAGE;
+    };
+    auto slot_of = [&](int t) { return smem + (t % S) * STAGE; };
+
+    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    if constexpr (PF) {
+        if (J > 0) {
+            wait_ring(0);
+            __syncthreads();
+            load_frags(slot_of(0), 0, fa0, fb0);
+        }
+    }
+    for (int j = 0; j < J; ++j) {
+        if (!PF || j > 0) {
+            wait_ring(j);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int u = 0; u < SPI; ++u) {
+            const int t = j * SPI + S - SPI + u;
+            if (t < TP) issue(t);
+        }
+        const int t0 = j * SPI;
         // Waves raise their priority while issuing MFMAs so that a wave in its
         // MFMA run is not starved by the other wave's address/LDS instructions.
         __builtin_amdgcn_s_setprio(1);
-        load_frags(slot, 0, fa0, fb0);
+        if constexpr (!PF) load_frags(slot_of(t0), 0, fa0, fb0);
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; kk += 2) {
-            load_frags(slot, kk + 1, fa1, fb1);
+        for (int q = 0; q < STEPS; q += 2) {
+            load_frags(slot_of(t0 + (q + 1) / KS), (q + 1) % KS, fa1, fb1);
             mma(fa0, fb0);
-            if (kk + 2 < KSTEPS) load_frags(slot, kk + 2, fa0, fb0);
+            if (q + 2 < STEPS)
+                load_frags(slot_of(t0 + (q + 2) / KS), (q + 2) % KS, fa0, fb0);
+            else if constexpr (PF)
+                load_frags(slot_of(t0 + SPI), 0, fa0, fb0);   // next iteration's first step (stale after the last)
             mma(fa1, fb1);
+        }
+        // Issue order for the iteration: each step's MFMAs interleaved with the
+        // next step's fragment reads, so LDS latency hides behind MFMA issue
+        // instead of being waited on before each MFMA (left alone, the
+        // scheduler sinks every read next to its use).
+        {
+            constexpr int RPS = (A_KC ? FM : 2 * FM) + (B_KC ? FN : 2 * FN);   // LDS reads per K step
+            constexpr int MPS = FM * FN;                                       // MFMAs per K step
+            if constexpr (!PF) __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+#pragma unroll
+            for (int q = 0; q < STEPS - 1; ++q) sched_mfma_with_reads<RPS, MPS, 0>();
+            if constexpr (PF)
+                sched_mfma_with_reads<RPS, MPS, 0>();
+            else
+                __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0);
         }
         __builtin_amdgcn_s_setprio(0);
     }
+    // No direct load may still be writing LDS when the workgroup ends.
+    wait_vmcnt<0>();
 
     // Epilogue.  acc[i][j][4g + e] is C[m][n + e] with
     //   m = m0 + wm*WTM + i*32 + lane%32,  n = n0 + wn*WTN + j*32 + 8g + 4*(lane/32).
@@ -302,24 +383,25 @@ gemm_lds_kernel(GemmParams p)
     }
 }
 
-template <int BK, int S, int T, bool AKC, bool BKC>
+template <int BKS, int SPI, int S, bool PF, int WM, int WN, int T, bool AKC, bool BKC>
 inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
-    const dim3 block(512);
-    return hipLaunchKernel((const void*)&gemm_lds_kernel<BK, S, T, AKC, BKC>, grid, block, kargs, 0, stream);
+    const dim3 block(64 * WM * WN);
+    return hipLaunchKernel((const void*)&gemm_lds_kernel<BKS, SPI, S, PF, WM, WN, T, AKC, BKC>, grid, block,
+                           kargs, 0, stream);
 }
 
 // K-contiguous A <=> transpose_A == 0; K-contiguous B <=> transpose_B == 1.
-template <int BK, int S, int T>
+template <int BKS, int SPI, int S, bool PF, int WM, int WN, int T>
 inline hipError_t dispatch_lds(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    if (!tA && tB) return launch_lds_inst<BK, S, T, true, true>(p, s);
-    if (!tA && !tB) return launch_lds_inst<BK, S, T, true, false>(p, s);
-    if (tA && tB) return launch_lds_inst<BK, S, T, false, true>(p, s);
-    return launch_lds_inst<BK, S, T, false, false>(p, s);
+    if (!tA && tB) return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, true, true>(p, s);
+    if (!tA && !tB) return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, true, false>(p, s);
+    if (tA && tB) return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, false, true>(p, s);
+    return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, false, false>(p, s);
 }
 
 }  // namespace tlg

@@ -5,7 +5,7 @@ namespace tlg {
 
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream)
 {
-    return dispatch_lds<64, 2, DT_F16>(p, transpose_A, transpose_B, stream);
+    return dispatch_lds<64, 1, 2, false, 2, 4, DT_F16>(p, transpose_A, transpose_B, stream);
 }
 
 }  // namespace tlg
