@@ -5,13 +5,16 @@
 // section puts its arithmetic intensity near 16 FLOP/byte.
 //
 // Each workgroup owns 16 rows x kSkinnyNB columns of C and reads its B rows
-// exactly once.  The four waves split the K range into four contiguous
-// slices; each wave streams its slice with 16-byte buffer loads straight into
-// MFMA 16x16x32 operand registers (B rows are K-contiguous, which is the
-// operand layout, so no LDS staging is needed), two register groups in flight
-// so the next group's loads overlap the current group's MFMAs.  The A slice is
-// re-read from L2 (A is 16 x K).  The four partial 16 x NB tiles are summed in
-// LDS in a fixed order (deterministic), then the epilogue applies
+// exactly once.  The waves (kSkinnyThreads / 64 of them) split the K range into
+// contiguous slices; each wave streams its slice with 16-byte buffer loads
+// straight into MFMA 16x16x32 operand registers (B rows are K-contiguous, which
+// is the operand layout, so no LDS staging is needed), two register groups of U
+// K steps in flight so the next group's loads overlap the current group's
+// MFMAs.  The A slice is re-read from L2 (A is 16 x K).  Measured on MI355X for
+// 16 x 16384 x 8192: 8 waves with U = 2 stream B at ~4.8 TB/s against ~4.0 TB/s
+// for 4 waves with U = 4 (more waves keep more loads in flight per CU).  The
+// partial 16 x NB tiles are summed in LDS in a fixed order (deterministic),
+// then the epilogue applies
 // (+ prior C) -> ReLU -> rounding -> guarded stores.
 //
 // Out-of-range rows, columns and K steps read as zero through the buffer
@@ -136,7 +139,7 @@ static hipError_t launch_skinny_t(const GemmParams& p, hipStream_t stream)
     void* kargs[] = {&args};
     const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
     const dim3 block(kSkinnyThreads);
-    return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, kSkinnyNB, 4>, grid, block, kargs, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, kSkinnyNB, 2>, grid, block, kargs, 0, stream);
 }
 
 hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream)

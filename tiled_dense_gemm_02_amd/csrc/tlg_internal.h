@@ -38,11 +38,11 @@ inline TileShape tile_shape(int cfg)
     return TileShape{128, 128, 64, 2, 1, 2};
 }
 
-// Skinny kernel geometry: 16 rows x kSkinnyNB columns per workgroup, 4 waves
+// Skinny kernel geometry: 16 rows x kSkinnyNB columns per workgroup, 8 waves
 // splitting K.
 constexpr int kSkinnyRows = 16;
 constexpr int kSkinnyNB = 64;
-constexpr int kSkinnyThreads = 256;
+constexpr int kSkinnyThreads = 512;  // 8 waves split K
 
 // Launchers (defined in the kernel translation units).  vec_a / vec_b: 8 for
 // 128-bit global loads, 1 for 16-bit loads.
