@@ -32,28 +32,32 @@ sys.path.insert(0, ROOT)
 METRIC = "GEMM TFLOP/s (fp16, fp32 acc) and % of MFMA peak; skinny: HBM GB/s %"
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}     # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
+# Sources of each kernel family, keyed by the plan's variant number (tlg.h).
 KERNEL_SOURCES = {
-    "tile": ["gemm_tile.hpp", "tlg_device.hpp"],
-    "skinny": ["gemm_skinny.hip", "tlg_device.hpp"],
+    1: ["gemm_tile.hpp", "tlg_device.hpp"],
+    2: ["gemm_tile.hpp", "tlg_device.hpp"],
+    5: ["gemm_tile.hpp", "tlg_device.hpp"],
+    3: ["gemm_skinny.hip", "gemm_lds.hpp", "tlg_device.hpp"],
+    6: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
 }
 
 
-def kernel_hash(kind: str) -> str:
+def kernel_hash(variant: int) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kind]:
+    for f in KERNEL_SOURCES[variant]:
         with open(os.path.join(ROOT, "tiled_dense_gemm_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, kind: str):
+def stored_traffic(workload: str, variant: int):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken
     on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_hash") != kernel_hash(kind):
+    if rec.get("kernel_hash") != kernel_hash(variant):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -159,10 +163,10 @@ def main():
         del x, y
 
     case = W.CONFIGS[args.workload]
-    kind = "skinny" if case.M <= 16 and case.transpose_B else "tile"
     r = measure(case, args.steps, args.warmup, log=log)
     plan = r["plan"]
     info = plan.info
+    kind = "skinny" if info.variant == 3 else "tile"   # HBM-bound vs MFMA-bound kernel
     ms = r["ms"]
     tflops = case.flops / (ms * 1e-3) / 1e12
     gbs = case.algorithmic_bytes / (ms * 1e-3) / 1e9
@@ -174,7 +178,7 @@ def main():
         roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[case.ab], "unit": "TFLOP/s",
                 "frac": tflops / PEAK_TFLOPS[case.ab]}
         value, unit = tflops, "TFLOP/s"
-    roof["traffic"] = stored_traffic(args.workload, kind)
+    roof["traffic"] = stored_traffic(args.workload, info.variant)
     roof["kernel"] = plan.describe().split()[0]
     roof["per_launch"] = {"flops": case.flops, "algorithmic_bytes": case.algorithmic_bytes,
                           "avg_kernel_ms": ms}

@@ -4,113 +4,139 @@
 // P <= min(P_peak, I * B_mem) of the overview page's "performance model"
 // section puts its arithmetic intensity near 16 FLOP/byte.
 //
-// Each workgroup owns 16 rows x kSkinnyNB columns of C and reads its B rows
-// exactly once.  The waves (kSkinnyThreads / 64 of them) split the K range into
-// contiguous slices; each wave streams its slice with 16-byte buffer loads
-// straight into MFMA 16x16x32 operand registers (B rows are K-contiguous, which
-// is the operand layout, so no LDS staging is needed), two register groups of U
-// K steps in flight so the next group's loads overlap the current group's
-// MFMAs.  The A slice is re-read from L2 (A is 16 x K).  Measured on MI355X for
-// 16 x 16384 x 8192: 8 waves with U = 2 stream B at ~4.8 TB/s against ~4.0 TB/s
-// for 4 waves with U = 4 (more waves keep more loads in flight per CU).  The
+// Each workgroup owns 16 rows x kSkinnyNB columns of C, i.e. kSkinnyNB
+// consecutive rows of B, and streams them exactly once through an S-stage LDS
+// ring.  One stage holds KST elements of K of every B row of the workgroup and
+// of the 16 A rows.  Stages are filled with global->LDS direct loads in which
+// each instruction reads 1 KiB of B (or A) rows contiguously, so HBM sees long
+// row segments rather than 64-byte pieces of many rows.  The eight waves take
+// different 32-wide K steps of a stage and multiply with MFMA 16x16x32; their
 // partial 16 x NB tiles are summed in LDS in a fixed order (deterministic),
-// then the epilogue applies
-// (+ prior C) -> ReLU -> rounding -> guarded stores.
+// then the epilogue applies (+ prior C) -> ReLU -> rounding -> guarded stores.
 //
-// Out-of-range rows, columns and K steps read as zero through the buffer
-// resource's range check ("core primitives" chapter, section 4.2).
+// Row layout in a stage: 16-byte chunk c of row r sits at c ^ (r & 15), so the
+// sixteen lanes that read sixteen consecutive rows of one chunk for an MFMA
+// operand hit 64 distinct banks.  Out-of-range rows, columns and K chunks read
+// as zero through the buffer resource's range check ("core primitives"
+// chapter, section 4.2).
+//
+// Measured on MI355X for 16 x 16384 x 8192 fp16: ~5.0 TB/s; the previous
+// design that loaded MFMA operands straight from HBM into registers (16 rows
+// x 64 bytes per load instruction) reached ~4.8 TB/s with 8 waves.
 
-#include "tlg_device.hpp"
+#include "gemm_lds.hpp"
 
 namespace tlg {
 
-template <int T_IN, int NB, int U>
+template <int T_IN, int NB, int KST, int S>
 __global__ void __launch_bounds__(kSkinnyThreads)
 gemm_skinny_kernel(GemmParams p)
 {
-    constexpr int NS = NB / 16;     // 16-column MFMA tiles per workgroup
-    constexpr int WAVES = kSkinnyThreads / 64;
-    static_assert(NB % 16 == 0, "NB must be a multiple of 16");
+    constexpr int WAVES = kSkinnyThreads / 64, MR = kSkinnyRows;
+    constexpr int RB = KST * 2;                      // bytes per row segment of a stage
+    constexpr int ROWS = NB + MR;                    // B rows, then A rows
+    constexpr int STAGE = ROWS * RB;
+    constexpr int NS = NB / 16;                      // 16-column MFMA tiles
+    constexpr int KSTEPS = KST / 32;                 // 32-wide MFMA K steps per stage
+    constexpr int SPW = KSTEPS / WAVES;              // K steps per wave per stage
+    constexpr int CHUNKS = RB / 16;                  // 16-byte chunks per row segment
+    constexpr int LPI = 1024 / RB;                   // rows per 1 KiB direct load
+    constexpr int LOADS = ROWS / LPI;                // direct loads per stage
+    constexpr int LPW = LOADS / WAVES;               // per wave
+    static_assert(NB % 16 == 0 && NB % LPI == 0, "NB");
+    static_assert(KSTEPS % WAVES == 0 && SPW >= 1, "every wave needs whole K steps of a stage");
+    static_assert(LOADS % WAVES == 0, "direct loads must divide evenly over the waves");
+    static_assert(CHUNKS >= 16 && 1024 % RB == 0, "row segment of 256 B .. 1 KiB");
+    static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
+    static_assert((S - 2) * LPW < 64, "vmcnt range");
+    static_assert(WAVES * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
 
-    __shared__ float red[WAVES][NS][4][64];
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int m0 = blockIdx.y * kSkinnyRows;
-    const int n0 = blockIdx.x * NB;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m0 = blockIdx.y * MR, n0 = blockIdx.x * NB;
     const int K = p.K;
-    const int KS = (K + 31) / 32;                       // 32-wide K steps
-    const int s_begin = wave * KS / WAVES;
-    const int s_end = (wave + 1) * KS / WAVES;
-
+    const int NST = (K + KST - 1) / KST;
     const uint32_t ld = (uint32_t)K * 2u;
-    const uint32_t kbyte = (uint32_t)(lane >> 4) * 16u;  // this lane's 8-element K piece
-    const int r = lane & 15;
-
-    // A rows m0.., B rows n0..; resources start at those rows.
-    const char* a_base = (const char*)p.A + (uint64_t)m0 * ld;
+    const uint32_t lds0 = lds_addr_of(smem);
     const char* b_base = (const char*)p.B + (uint64_t)n0 * ld;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base, (uint64_t)(p.M - m0) * ld);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base, (uint64_t)(p.N - n0) * ld);
-    const bool a_ok = m0 + r < p.M;
-    const uint32_t a_row = (uint32_t)r * ld;
-    bool b_ok[NS];
-    uint32_t b_row[NS];
+    const char* a_base = (const char*)p.A + (uint64_t)m0 * ld;
+    const uint64_t b_bytes = (uint64_t)(p.N - n0) * ld;
+    const uint64_t a_bytes = (uint64_t)(p.M - m0) * ld;
+
+    // Load i of this wave fills LDS rows q*LPI .. q*LPI + LPI - 1 of the stage
+    // (q = i * WAVES + wave); lane -> row q*LPI + lane / CHUNKS, position lane % CHUNKS.
+    auto issue = [&](int st) {
+        const int k0 = st * KST;
+        const uint64_t o = (uint64_t)k0 * 2u;
+        const uint32_t slot = lds0 + (uint32_t)((st % S) * STAGE);
+        const i32x4 rb = rsrc_words(b_base + o, b_bytes > o ? b_bytes - o : 0);
+        const i32x4 ra = rsrc_words(a_base + o, a_bytes > o ? a_bytes - o : 0);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        b_ok[j] = n0 + j * 16 + r < p.N;
-        b_row[j] = (uint32_t)(j * 16 + r) * ld;
-    }
+        for (int i = 0; i < LPW; ++i) {
+            const int q = i * WAVES + wave;
+            const int row = q * LPI + lane / CHUNKS;
+            const int c = (lane % CHUNKS) ^ (row & 15);
+            const bool is_b = q * LPI < NB;          // a load is all B rows or all A rows
+            const int r = is_b ? row : row - NB;
+            const bool ok = (is_b ? (n0 + r < p.N) : (m0 + r < p.M)) && (k0 + c * 8 < K);
+            i32x4 rs;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) rs[w] = __builtin_amdgcn_readfirstlane(is_b ? rb[w] : ra[w]);
+            dma16(rs, ok ? (uint32_t)r * ld + (uint32_t)c * 16u : kOOB,
+                  __builtin_amdgcn_readfirstlane(slot + (uint32_t)(q * 1024)));
+        }
+    };
+    auto frag = [&](const char* slot, int row, int c) -> u32x4 {
+        return *(const u32x4*)(slot + row * RB + ((c ^ (row & 15)) << 4));
+    };
 
     f32x4 acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 a0[U], b0[U][NS], a1[U], b1[U][NS];
-
-    auto issue = [&](int s, u32x4 (&av)[U], u32x4 (&bv)[U][NS]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int st = s + u;
-            const bool k_ok = st < s_end && (st * 32 + (lane >> 4) * 8) < K;
-            const uint32_t kofs = (uint32_t)st * 64u + kbyte;
-            av[u] = buf_load16(ra, (k_ok && a_ok) ? a_row + kofs : kOOB);
+    for (int st = 0; st < S - 1; ++st)
+        if (st < NST) issue(st);
+    for (int st = 0; st < NST; ++st) {
+        // Stage st has landed once at most S-2 newer stages are in flight; the
+        // barrier publishes every wave's part and frees the slot refilled next.
+        if (st + S - 2 < NST)
+            wait_vmcnt<(S - 2) * LPW>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (st + S - 1 < NST) issue(st + S - 1);
+        const char* slot = smem + (st % S) * STAGE;
 #pragma unroll
-            for (int j = 0; j < NS; ++j) bv[u][j] = buf_load16(rb, (k_ok && b_ok[j]) ? b_row[j] + kofs : kOOB);
+        for (int u = 0; u < SPW; ++u) {
+            const int c = (wave * SPW + u) * 4 + (lane >> 4);
+            const u32x4 af = frag(slot, NB + (lane & 15), c);
+            // B fragment first: the hardware tile is C's transpose, so acc[j][e]
+            // is C[m0 + lane%16][n0 + 16j + 4*(lane/16) + e].
+#pragma unroll
+            for (int j = 0; j < NS; ++j) acc[j] = mfma16x16x32<T_IN>(frag(slot, j * 16 + (lane & 15), c), af, acc[j]);
         }
-    };
-    // MFMA with the B fragment first: the hardware tile is C's transpose, so
-    // acc[j][e] is C[m0 + lane%16][n0 + 16j + 4*(lane/16) + e].
-    auto compute = [&](const u32x4 (&av)[U], const u32x4 (&bv)[U][NS]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int j = 0; j < NS; ++j) acc[j] = mfma16x16x32<T_IN>(bv[u][j], av[u], acc[j]);
-    };
-
-    issue(s_begin, a0, b0);
-    for (int s = s_begin; s < s_end; s += 2 * U) {
-        issue(s + U, a1, b1);
-        compute(a0, b0);
-        issue(s + 2 * U, a0, b0);
-        compute(a1, b1);
     }
+    wait_vmcnt<0>();
+    __syncthreads();
 
+    float* red = (float*)smem;   // [WAVES][NS][4][64]
 #pragma unroll
     for (int j = 0; j < NS; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave][j][e][lane] = acc[j][e];
+        for (int e = 0; e < 4; ++e) red[((wave * NS + j) * 4 + e) * 64 + lane] = acc[j][e];
     __syncthreads();
 
-    const int m = m0 + r;
+    const int m = m0 + (lane & 15);
     const bool vec_cols = p.c_vec != 0;
     for (int j = wave; j < NS; j += WAVES) {
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float s = red[0][j][e][lane];
+            float s = red[(j * 4 + e) * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < WAVES; ++w) s += red[w][j][e][lane];
+            for (int w = 1; w < WAVES; ++w) s += red[((w * NS + j) * 4 + e) * 64 + lane];
             v[e] = s;
         }
         const int n = n0 + j * 16 + 4 * (lane >> 4);
@@ -139,7 +165,8 @@ static hipError_t launch_skinny_t(const GemmParams& p, hipStream_t stream)
     void* kargs[] = {&args};
     const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
     const dim3 block(kSkinnyThreads);
-    return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, kSkinnyNB, 2>, grid, block, kargs, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, kSkinnyNB, kSkinnyKST, kSkinnyStages>, grid,
+                           block, kargs, 0, stream);
 }
 
 hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream)

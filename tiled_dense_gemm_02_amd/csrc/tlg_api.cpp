@@ -151,12 +151,12 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         in.lds_bytes = (int64_t)kLdsStages * (kLdsBM + kLdsBN) * kLdsBK * 2;
         in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
     } else if (variant == TLG_VARIANT_SKINNY) {
-        in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = 32;
-        in.stages = 2;
+        in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
+        in.stages = kSkinnyStages;
         in.threads = kSkinnyThreads;
         in.grid = ceil_div(M, kSkinnyRows) * ceil_div(N, kSkinnyNB);
-        in.lds_bytes = (int64_t)(kSkinnyThreads / 64) * (kSkinnyNB / 16) * 4 * 64 * 4;
-        in.k_tiles = (int32_t)ceil_div(K, 32);
+        in.lds_bytes = (int64_t)kSkinnyStages * (kSkinnyNB + kSkinnyRows) * kSkinnyKST * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kSkinnyKST);
     }
     std::snprintf(p->desc, sizeof(p->desc),
                   "%s M=%lld N=%lld K=%lld ab=%s c=%s tA=%d tB=%d clear=%d relu=%d block=%dx%dx%d "

@@ -38,11 +38,13 @@ inline TileShape tile_shape(int cfg)
     return TileShape{128, 128, 64, 2, 1, 2};
 }
 
-// Skinny kernel geometry: 16 rows x kSkinnyNB columns per workgroup, 8 waves
-// splitting K.
+// Skinny kernel geometry: 16 rows x kSkinnyNB columns per workgroup, operands
+// staged through a kSkinnyStages-deep LDS ring of kSkinnyKST-wide K stages.
 constexpr int kSkinnyRows = 16;
 constexpr int kSkinnyNB = 64;
-constexpr int kSkinnyThreads = 512;  // 8 waves split K
+constexpr int kSkinnyThreads = 512;  // 8 waves split the K steps of each stage
+constexpr int kSkinnyKST = 256;      // K elements per LDS stage (512-byte row segments)
+constexpr int kSkinnyStages = 3;     // LDS ring depth
 
 // Launchers (defined in the kernel translation units).  vec_a / vec_b: 8 for
 // 128-bit global loads, 1 for 16-bit loads.
