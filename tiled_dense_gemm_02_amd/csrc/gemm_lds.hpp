@@ -1,35 +1,56 @@
-// Tiled GEMM with a multi-stage LDS ring fed by global->LDS direct loads.
+// Tiled GEMM with a two-slot LDS ring fed by global->LDS direct loads.
 //
-// The same tile program as gemm_tile.hpp (one 256 x 256 output tile per
-// workgroup, K loop over BK-wide tiles, MFMA 32x32x16 into fp32 fragments,
-// fused epilogue), with the software pipeline of the tile program's
-// T.Pipelined(num_stages = S) realised as an S-stage ring: tile k+S-1 is
-// requested while tile k is multiplied ("software pipelining" section of the
-// overview page; the handbook page's quickstart uses a 3-stage ring).
+// The tile program of the overview page's GEMM example (one 256 x 256 output
+// tile per workgroup, a K loop over 64-wide tiles, fp32 register fragments,
+// fused epilogue), with the software pipeline of T.Pipelined realised as a
+// ring: while tile j is multiplied, tile j+1 is in flight ("software
+// pipelining" section of the overview page).
 //
 // Global->LDS copies use buffer_load_dwordx4 ... lds: each lane's 16 bytes go
-// straight to LDS at (ring slot block + 16 * lane), with no VGPR staging, no LDS
-// write instructions and no VALU work.  Lanes whose chunk lies outside the
-// matrix take an out-of-range offset and the hardware writes zeros (the zero
-// safe value of out-of-bounds reads, "core primitives" chapter, section 4.2).
-// The swizzled LDS layout is produced by choosing which global chunk each lane
-// fetches.
+// straight to LDS at (1 KiB block + 16 * lane), with no VGPR staging and no LDS
+// write instructions.  Lanes whose chunk lies outside the matrix take an
+// out-of-range offset and the hardware writes zeros (the zero safe value of
+// out-of-bounds reads, "core primitives" chapter, section 4.2).  The swizzled
+// LDS layout is produced by choosing which global chunk each lane fetches.
 //
 // Operand layouts in LDS (one ring slot; "rows" are the operand's M or N index):
-//   K-contiguous operand (A stored [M,K], B stored [N,K]): 256 rows of BK
-//     elements (RB = 2*BK bytes); 16-byte chunk c of row r sits at position
-//     c ^ ((r / (16/CH)) % CH), CH = BK/8.  Sixteen lanes reading sixteen
-//     consecutive rows of one chunk then touch 64 distinct banks.  MFMA
-//     operands are single ds_read_b128s.
-//   M/N-contiguous operand (A stored [K,M], B stored [K,N]): BK rows of k, each
+//   K-contiguous operand (A stored [M,K], B stored [N,K]): 256 rows of 64
+//     elements (128 bytes); 16-byte chunk c of row r sits at c ^ ((r / 2) % 8).
+//     A fragment (16 consecutive rows, one chunk) is one ds_read_b128 per lane
+//     and touches every bank once.
+//   M/N-contiguous operand (A stored [K,M], B stored [K,N]): 64 rows of k, each
 //     256 contiguous M/N elements (512 bytes); chunk c of row k sits at
-//     c ^ ((k & 3) << 2).  MFMA operands are read with ds_read_b64_tr_b16, which
-//     transposes 4 x 16-bit values across each group of 16 lanes: lane i of a
-//     group receives element (i & 3) of the 8-byte pieces addressed by lanes
-//     (i >> 2) + 4j, j = 0..3.  Addressing row kb + (s >> 2), columns
-//     nb + 4 (s & 3) from lane s therefore delivers column nb + i, rows
-//     kb..kb+3 to lane i: a K-contiguous MFMA operand.
+//     c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 1).  Fragments are read with
+//     ds_read_b64_tr_b16, which transposes 4 x 16-bit values across each group
+//     of 16 lanes: lane i of a group receives element (i & 3) of the 8-byte
+//     pieces addressed by lanes (i >> 2) + 4j, j = 0..3.  Addressing row
+//     kb + (s >> 2), columns nb + 4 (s & 3) from lane s therefore delivers
+//     column nb + i, rows kb..kb+3 to lane i.  The second swizzle term keeps
+//     the lane groups that read rows 8 apart on different banks.
+//
+// MFMA shape.  The wave tiles are multiplied with v_mfma_f32_16x16x32 (f16 or
+// bf16 in, fp32 accumulate).  Under the MI355X power limit a stream of
+// 16x16x32 instructions on changing data sustains a ~14% higher clock than
+// the same FLOPs as 32x32x16 (measured ~1.93 vs ~1.68 GHz), and the kernel is
+// power-bound, so the smaller shape is the faster one.  Issuing the B fragment
+// as the first operand makes the hardware tile C's transpose: lane l holds
+// C[m0 + l%16][n0 + 4 (l/16) + e], e = 0..3 (four consecutive columns).
+//
+// Schedule (per K tile, per wave).  8 waves in a 2 x 4 grid, 128 x 64 outputs
+// each (8 x 4 fragments, 64 MFMAs per K tile).  The instruction order is fixed
+// at compile time, one MFMA at a time:
+//   - A fragment i is reloaded for the next K step right after its last use;
+//     B fragments are double-buffered and read during the preceding step;
+//   - the ring barrier sits inside the last K step, after SPLIT of its MFMAs:
+//     the remaining MFMAs cover the latency of the next tile's first fragment
+//     reads, so no wave starts a tile waiting on LDS;
+//   - right after that barrier the tile's slot is free and the loads of the
+//     tile two ahead are issued, one every R MFMAs, so each load has a full
+//     K tile of MFMA work to land and the vector-memory queue never blocks
+//     the MFMA stream.
 #pragma once
+
+#include <utility>
 
 #include "gemm_tile.hpp"
 
@@ -46,6 +67,14 @@ __device__ inline void wait_vmcnt()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0).
+template <int N>
+__device__ inline void wait_vmcnt_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
 // Buffer resource as four scalar words (for the inline-asm direct load below).
@@ -65,8 +94,9 @@ __device__ inline i32x4 rsrc_words(const void* base, uint64_t bytes_left)
 // Issued as inline assembly so that the compiler does not treat the slot being
 // filled as aliasing the slot being read (it would otherwise wait for every
 // outstanding direct load before each LDS read and serialise the ring).  The
-// kernel tracks completion itself with explicit vmcnt waits and issues no other
-// vector-memory instruction while direct loads are in flight.
+// kernels track completion themselves with explicit vmcnt waits and issue no
+// other vector-memory load while direct loads are in flight.  The whole offset
+// is in the VGPR operand, so the range check (zero fill) covers all of it.
 // m0 is a reserved register: the clobber tells the compiler that its value does
 // not survive the statement (the compiler re-initialises m0 wherever it needs it).
 #pragma clang diagnostic push
@@ -91,24 +121,17 @@ __device__ inline u32x2 lds_read_tr16(const char* p)
     return __builtin_bit_cast(u32x2, v);
 }
 
-// Scheduling groups for one K step: MPS MFMAs, each followed by its share of the
-// RPS LDS reads of the next step (sched_group_barrier masks: 0x008 MFMA, 0x100 DS read).
-template <int RPS, int MPS, int R>
-__device__ inline void sched_mfma_with_reads()
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}):
+// a loop whose index is a compile-time constant in every iteration.
+template <typename F, int... Ms>
+__device__ inline void static_for_impl(F&& f, std::integer_sequence<int, Ms...>)
 {
-    if constexpr (R < MPS) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        constexpr int nr = RPS * (R + 1) / MPS - RPS * R / MPS;
-        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
-        sched_mfma_with_reads<RPS, MPS, R + 1>();
-    }
+    (f(std::integral_constant<int, Ms>{}), ...);
 }
-
-template <int BK>
-__device__ __host__ constexpr int swz_kc(int row)
+template <int N, typename F>
+__device__ inline void static_for(F&& f)
 {
-    constexpr int CH = BK / 8;
-    return (row / (16 / CH)) % CH;
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // One operand of the 256 x 256 tile: 256 rows of its M/N index x BK of K,
@@ -128,7 +151,10 @@ struct LdsOperand {
     static constexpr int DROW = NW * (1024 / RB);   // K-contiguous: rows per load step
     static constexpr int DK = 2 * NW;               // M/N-contiguous: k rows per load step
     static_assert(!KC || (4 * NW) % CH == 0, "swizzle must be invariant along the load step");
-    static_assert(KC || NW % 2 == 0, "swizzle must be invariant along the load step");
+    static_assert(KC || DK % 16 == 0, "swizzle must be invariant along the load step");
+
+    __device__ static int swz_kc(int row) { return (row / (16 / CH)) % CH; }
+    __device__ static int swz_mn(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
 
     const char* base;       // element (row r0, k 0)       [K-contig]  /  (k 0, row r0)  [M/N-contig]
     uint64_t base_bytes;    // bytes from base to the end of the matrix
@@ -147,7 +173,7 @@ struct LdsOperand {
             base = (const char*)ptr + (uint64_t)r0 * ld;
             base_bytes = (uint64_t)(rows_total - r0) * ld;
             idx0 = wave * (1024 / RB) + lane / CH;
-            const int c = (lane % CH) ^ swz_kc<BK>(idx0);
+            const int c = (lane % CH) ^ swz_kc(idx0);
             off0 = (uint32_t)idx0 * ld + (uint32_t)c * 16u;
             kc = c * 8;
             col_ok = true;
@@ -156,81 +182,76 @@ struct LdsOperand {
             base = (const char*)ptr + (uint64_t)r0 * 2u;
             base_bytes = (uint64_t)K * ld - (uint64_t)r0 * 2u;
             idx0 = 2 * wave + (lane >> 5);
-            const int c = (lane & 31) ^ ((idx0 & 3) << 2);
+            const int c = (lane & 31) ^ swz_mn(idx0);
             off0 = (uint32_t)idx0 * ld + (uint32_t)c * 16u;
             kc = 0;
             col_ok = c * 8 < rows_left;
         }
     }
 
-    // Request the tile starting at k0 into the slot's operand region (wave's block included).
-    __device__ void issue(int k0, int K, uint32_t lds_region) const
+    // Resource for the tile starting at k0 (tiles at or past the end of K get an
+    // empty resource: every lane reads zeros).
+    __device__ i32x4 rsrc(int k0) const
     {
         const uint64_t o = KC ? (uint64_t)k0 * 2u : (uint64_t)k0 * ld;
-        // Slots past the end of K (padding of the last iteration) get an empty
-        // resource; all their lanes are out of range and receive zeros.
-        const i32x4 r = rsrc_words(base + o, o < base_bytes ? base_bytes - o : 0);
-#pragma unroll
-        for (int i = 0; i < L; ++i) {
-            bool valid;
-            uint32_t off;
-            if constexpr (KC) {
-                valid = (idx0 + i * DROW < rows_left) && (k0 + kc < K);
-                off = off0 + (uint32_t)(i * DROW) * ld;
-            } else {
-                valid = col_ok && (k0 + idx0 + i * DK < K);
-                off = off0 + (uint32_t)(i * DK) * ld;
-            }
-            dma16(r, valid ? off : kOOB, lds_region + (uint32_t)(i * NW * 1024));
+        return rsrc_words(base + o, o < base_bytes ? base_bytes - o : 0);
+    }
+
+    // Lane offset of load i of the tile starting at k0, or kOOB.
+    __device__ uint32_t voff(int i, int k0, int K) const
+    {
+        if constexpr (KC) {
+            const bool valid = (idx0 + i * DROW < rows_left) && (k0 + kc < K);
+            return valid ? off0 + (uint32_t)(i * DROW) * ld : kOOB;
+        } else {
+            const bool valid = col_ok && (k0 + idx0 + i * DK < K);
+            return valid ? off0 + (uint32_t)(i * DK) * ld : kOOB;
         }
     }
 
-    // MFMA operand of rows row0..row0+31 (row0 a multiple of 32), K step kk (16 wide):
-    // lane l holds row row0 + l%32 and K elements 8*(l/32) .. +7 of the step.
+    // MFMA 16x16x32 operand of rows row0..row0+15 (row0 a multiple of 16), K step
+    // kk (32 wide): lane l holds row row0 + l%16 and K elements 8*(l/16) .. +7.
     __device__ u32x4 frag(const char* region, int row0, int kk, int lane) const
     {
         if constexpr (KC) {
-            const int row = row0 + (lane & 31);
-            const int c = kk * 2 + (lane >> 5);
-            return *(const u32x4*)(region + row * RB + ((c ^ swz_kc<BK>(row)) << 4));
+            const int row = row0 + (lane & 15);
+            const int c = kk * 4 + (lane >> 4);
+            return *(const u32x4*)(region + row * RB + ((c ^ swz_kc(row)) << 4));
         } else {
             const int g = lane >> 4, s = lane & 15;
-            const int n = row0 + (g & 1) * 16 + 4 * (s & 3);
-            const int k = kk * 16 + (g >> 1) * 8 + (s >> 2);
-            const char* p = region + (((n >> 3) ^ ((k & 3) << 2)) << 4) + ((n >> 2) & 1) * 8;
-            const u32x2 lo = lds_read_tr16(p + k * 512);
-            const u32x2 hi = lds_read_tr16(p + (k + 4) * 512);
+            const int n = row0 + 4 * (s & 3);
+            const int k = kk * 32 + g * 8 + (s >> 2);
+            const int half = ((n >> 2) & 1) * 8;
+            const u32x2 lo = lds_read_tr16(region + k * 512 + (((n >> 3) ^ swz_mn(k)) << 4) + half);
+            const u32x2 hi = lds_read_tr16(region + (k + 4) * 512 + (((n >> 3) ^ swz_mn(k + 4)) << 4) + half);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
     }
 };
 
-// BKS: K width of one ring slot; SPI: slots consumed per barrier; S: ring slots.
-// Slot t holds K tile t (t % S).  Iteration j multiplies tiles j*SPI .. j*SPI+SPI-1
-// and requests tiles up to j*SPI + S - 1, so every request has S - SPI slots of
-// time to land while the barrier count stays at one per SPI*BKS of K.
-// PF (needs S >= 2*SPI + 1): an iteration's barrier also publishes the first
-// tile of the next iteration, whose first fragments are then read before the
-// next barrier, so no wave starts an iteration waiting on LDS.
-template <int BKS, int SPI, int S, bool PF, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC>
+template <int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_lds_kernel(GemmParams p)
 {
-    constexpr int BM = 256, BN = 256, NW = WAVES_M * WAVES_N;
-    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 32, FN = WTN / 32;
-    using OpA = LdsOperand<BKS, A_KC, NW>;
-    using OpB = LdsOperand<BKS, B_KC, NW>;
+    constexpr int BM = 256, BN = 256, BK = 64, S = 2, NW = WAVES_M * WAVES_N;
+    constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
+    using OpA = LdsOperand<BK, A_KC, NW>;
+    using OpB = LdsOperand<BK, B_KC, NW>;
     constexpr int STAGE = OpA::BYTES + OpB::BYTES;
-    constexpr int L = OpA::L + OpB::L;              // direct loads per lane per slot
-    constexpr int KS = BKS / 16;                     // 16-wide K steps per slot
-    constexpr int STEPS = SPI * KS;                  // K steps per iteration
-    // Slots allowed in flight when an iteration starts (the ones it does not read).
-    constexpr int AHEAD = PF ? S - 2 * SPI - 1 : S - 2 * SPI;
-    static_assert(BKS == 32 || BKS == 64, "slot width");
-    static_assert(SPI >= 1 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
-    static_assert(AHEAD >= 0, "ring too short for the requested prefetch");
-    static_assert(AHEAD * L < 64, "vmcnt range");
-    static_assert(STEPS % 2 == 0, "fragment double buffering steps by two");
+    constexpr int LA = OpA::L, LB = OpB::L, L = LA + LB;
+    constexpr int KS = BK / 32;                       // MFMA K steps per tile
+    constexpr int MPS = FM * FN;                      // MFMAs per K step
+    constexpr int MI = KS * MPS;                      // MFMAs per tile
+    constexpr int BPOS = (KS - 1) * MPS + SPLIT;      // the barrier precedes MFMA BPOS
+    // D loads of tile j+S are issued after tile j's barrier (their slot has just
+    // been freed), the other L-D at the start of the next tile.
+    constexpr int D0 = (MI - 1 - BPOS) / R + 1;
+    constexpr int D = D0 < L ? D0 : L;
+    static_assert(S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
+    static_assert(KS == 2, "fragment buffering assumes two K steps per tile");
+    static_assert(SPLIT >= 1 && SPLIT < MPS, "barrier inside the last K step");
+    static_assert(L - D == 0 || (L - D - 1) * R < BPOS, "early loads precede the barrier");
+    static_assert((S - 2) * L + D < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -242,8 +263,7 @@ gemm_lds_kernel(GemmParams p)
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;
-    const int J = (K + SPI * BKS - 1) / (SPI * BKS);   // iterations
-    const int TP = J * SPI;                             // slots requested (tail slots zero-filled)
+    const int TP = (K + BK - 1) / BK;                 // K tiles (the last one zero-padded)
 
     OpA opa;
     OpB opb;
@@ -251,157 +271,165 @@ gemm_lds_kernel(GemmParams p)
     opb.init(p.B, n0, p.N, K, lane, wave);
     const uint32_t lds0 = lds_addr_of(smem);
 
-    auto issue = [&](int t) {
-        const uint32_t slot =
-            __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t % S) * STAGE) + (uint32_t)wave * 1024u);
-        opa.issue(t * BKS, K, slot);
-        opb.issue(t * BKS, K, slot + (uint32_t)OpA::BYTES);
+    // Load i of tile t into its slot.  Every tile index gets its loads, also the
+    // ones past the end of K (their resource is empty and they write zeros into a
+    // slot nobody reads again), so every K tile issues exactly L loads and the
+    // vmcnt bookkeeping below needs no special cases.
+    struct TileRes {
+        i32x4 ra, rb;
+        int k0;
+        uint32_t slot;
     };
-    auto load_frags = [&](const char* slot, int kk, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[i] = opa.frag(slot, wm * WTM + i * 32, kk, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bf[j] = opb.frag(slot + OpA::BYTES, wn * WTN + j * 32, kk, lane);
+    auto tile_res = [&](int t) {
+        TileRes r;
+        r.k0 = t * BK;
+        r.ra = opa.rsrc(r.k0);
+        r.rb = opb.rsrc(r.k0);
+        r.slot = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t % S) * STAGE) + (uint32_t)wave * 1024u);
+        return r;
+    };
+    auto issue_one = [&](const TileRes& r, int i) {
+        if (i < LA)
+            dma16(r.ra, opa.voff(i, r.k0, K), r.slot + (uint32_t)(i * NW * 1024));
+        else
+            dma16(r.rb, opb.voff(i - LA, r.k0, K), r.slot + (uint32_t)OpA::BYTES + (uint32_t)((i - LA) * NW * 1024));
     };
 
-    f32x16 acc[FM][FN];
+    f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // MFMA with the B fragment first: the hardware tile is C's transpose, so
-    // acc[i][j][4g + e] is C[m][n + e] (see the epilogue).
-    auto mma = [&](const u32x4 (&af)[FM], const u32x4 (&bf)[FN]) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16<T_IN>(bf[j], af[i], acc[i][j]);
-    };
+    u32x4 fa[FM], fb[2][FN];
+    const int arow = wm * WTM, bcol = wn * WTN;
 
+    // Prologue: tile 0 whole, the first D loads of tile 1; wait for tile 0.
+    {
+        const TileRes r0 = tile_res(0);
 #pragma unroll
-    for (int t = 0; t < S - SPI; ++t)
-        if (t < TP) issue(t);
-
-    // Wait until the slots read before the next barrier have landed: at most
-    // AHEAD newer slots may still be in flight (fewer near the end, where
-    // everything is drained).  The caller's barrier then publishes every wave's
-    // part and retires all reads of the slots that get overwritten next.
-    auto wait_ring = [&](int j) {
-        if ((j + 1) * SPI + (PF ? 1 : 0) + AHEAD <= TP)
-            wait_vmcnt<AHEAD * L>();
-        else
-            wait_vmcnt<0>();
-    };
-    auto slot_of = [&](int t) { return smem + (t % S) * STAGE; };
-
-    u32x4 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-    if constexpr (PF) {
-        if (J > 0) {
-            wait_ring(0);
-            __syncthreads();
-            load_frags(slot_of(0), 0, fa0, fb0);
-        }
+        for (int i = 0; i < L; ++i) issue_one(r0, i);
+        const TileRes r1 = tile_res(1);
+#pragma unroll
+        for (int i = 0; i < D; ++i) issue_one(r1, i);
     }
-    for (int j = 0; j < J; ++j) {
-        if (!PF || j > 0) {
-            wait_ring(j);
-            __syncthreads();
-        }
+    wait_vmcnt<D>();
+    __syncthreads();
 #pragma unroll
-        for (int u = 0; u < SPI; ++u) {
-            const int t = j * SPI + S - SPI + u;
-            if (t < TP) issue(t);
-        }
-        const int t0 = j * SPI;
+    for (int i = 0; i < FM; ++i) fa[i] = opa.frag(smem, arow + i * 16, 0, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = opb.frag(smem + OpA::BYTES, bcol + j * 16, 0, lane);
+
+    for (int j = 0; j < TP; ++j) {
+        const char* cur = smem + (j % S) * STAGE;
+        const char* nxt = smem + ((j + 1) % S) * STAGE;
+        const TileRes re = tile_res(j + S - 1);     // the rest of this tile's loads
+        const TileRes rl = tile_res(j + S);         // loads issued after this tile's barrier
         // Waves raise their priority while issuing MFMAs so that a wave in its
         // MFMA run is not starved by the other wave's address/LDS instructions.
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (!PF) load_frags(slot_of(t0), 0, fa0, fb0);
-#pragma unroll
-        for (int q = 0; q < STEPS; q += 2) {
-            load_frags(slot_of(t0 + (q + 1) / KS), (q + 1) % KS, fa1, fb1);
-            mma(fa0, fb0);
-            if (q + 2 < STEPS)
-                load_frags(slot_of(t0 + (q + 2) / KS), (q + 2) % KS, fa0, fb0);
-            else if constexpr (PF)
-                load_frags(slot_of(t0 + SPI), 0, fa0, fb0);   // next iteration's first step (stale after the last)
-            mma(fa1, fb1);
-        }
-        // Issue order for the iteration: each step's MFMAs interleaved with the
-        // next step's fragment reads, so LDS latency hides behind MFMA issue
-        // instead of being waited on before each MFMA (left alone, the
-        // scheduler sinks every read next to its use).
-        {
-            constexpr int RPS = (A_KC ? FM : 2 * FM) + (B_KC ? FN : 2 * FN);   // LDS reads per K step
-            constexpr int MPS = FM * FN;                                       // MFMAs per K step
-            if constexpr (!PF) __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
-#pragma unroll
-            for (int q = 0; q < STEPS - 1; ++q) sched_mfma_with_reads<RPS, MPS, 0>();
-            if constexpr (PF)
-                sched_mfma_with_reads<RPS, MPS, 0>();
-            else
-                __builtin_amdgcn_sched_group_barrier(0x008, MPS, 0);
-        }
+        // Events placed before MFMA m (m = MI: after the last one).
+        static_for<MI + 1>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            constexpr int q = m / MPS, r = m % MPS;
+            if constexpr (m == BPOS) {
+                // Own fragment reads of this slot retired and tile j+1 landed (at
+                // most the (S-2) newer tiles in flight); the barrier then publishes
+                // every wave's part of tile j+1 and frees tile j's slot.
+                __builtin_amdgcn_s_setprio(0);
+                wait_vmcnt_lgkm0<(S - 2) * L>();
+                __syncthreads();
+                __builtin_amdgcn_s_setprio(1);
+            }
+            if constexpr (m % R == 0 && m / R < L - D) issue_one(re, D + m / R);
+            if constexpr (m >= BPOS && (m - BPOS) % R == 0 && (m - BPOS) / R < D) issue_one(rl, (m - BPOS) / R);
+            // A fragment i: its last use in step qs is MFMA qs*MPS + i*FN + FN - 1; it
+            // is reloaded right after that (for the next tile: not before the barrier).
+            if constexpr (m > 0) {
+                constexpr int qs = (m - 1) / MPS;
+                static_for<FM>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    constexpr int pos = qs * MPS + i * FN + FN;
+                    if constexpr (qs + 1 < KS) {
+                        if constexpr (m == pos) fa[i] = opa.frag(cur, arow + i * 16, qs + 1, lane);
+                    } else {
+                        constexpr int pos2 = pos > BPOS ? pos : BPOS;
+                        if constexpr (m == pos2) fa[i] = opa.frag(nxt, arow + i * 16, 0, lane);
+                    }
+                });
+            }
+            if constexpr (m < MI) {
+                // B fragments of the next step into the other buffer, spread over the step.
+                static_for<FN>([&](auto jc) {
+                    constexpr int jj = decltype(jc)::value;
+                    if constexpr (q + 1 < KS) {
+                        if constexpr (r == jj * (MPS / FN) + 1)
+                            fb[(q + 1) % 2][jj] = opb.frag(cur + OpA::BYTES, bcol + jj * 16, q + 1, lane);
+                    } else {
+                        if constexpr (r == SPLIT + (jj * (MPS - SPLIT)) / FN)
+                            fb[0][jj] = opb.frag(nxt + OpA::BYTES, bcol + jj * 16, 0, lane);
+                    }
+                });
+                constexpr int i = r / FN, jj = r % FN;
+                acc[i][jj] = mfma16x16x32<T_IN>(fb[q % 2][jj], fa[i], acc[i][jj]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
         __builtin_amdgcn_s_setprio(0);
     }
     // No direct load may still be writing LDS when the workgroup ends.
     wait_vmcnt<0>();
 
-    // Epilogue.  acc[i][j][4g + e] is C[m][n + e] with
-    //   m = m0 + wm*WTM + i*32 + lane%32,  n = n0 + wn*WTN + j*32 + 8g + 4*(lane/32).
+    // Epilogue.  acc[i][j][e] is C[m][n + e] with
+    //   m = m0 + wm*WTM + i*16 + lane%16,  n = n0 + wn*WTN + j*16 + 4*(lane/16).
     const bool vec_cols = p.c_vec != 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+        const int m = m0 + arow + i * 16 + (lane & 15);
         if (m >= p.M) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+        for (int jj = 0; jj < FN; ++jj) {
+            const int n = n0 + bcol + jj * 16 + 4 * (lane >> 4);
+            if (n >= p.N) continue;
+            const int count = min(4, p.N - n);
+            const bool vec_ok = vec_cols && count == 4;
+            const int64_t idx = (int64_t)m * p.N + n;
+            float v[4] = {acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
+            if (!p.clear_accum) {
+                float c[4] = {0.f, 0.f, 0.f, 0.f};
+                load_c4(p.C, p.c_dtype, idx, vec_ok, c, count);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-                if (n >= p.N) continue;
-                const int count = min(4, p.N - n);
-                const bool vec_ok = vec_cols && count == 4;
-                const int64_t idx = (int64_t)m * p.N + n;
-                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                if (!p.clear_accum) {
-                    float c[4] = {0.f, 0.f, 0.f, 0.f};
-                    load_c4(p.C, p.c_dtype, idx, vec_ok, c, count);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = c[e] + v[e];
-                }
-                if (p.relu) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = relu(v[e]);
-                }
-                store_c4(p.C, p.c_dtype, idx, vec_ok, v, count);
+                for (int e = 0; e < 4; ++e) v[e] = c[e] + v[e];
             }
+            if (p.relu) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = relu(v[e]);
+            }
+            store_c4(p.C, p.c_dtype, idx, vec_ok, v, count);
         }
     }
 }
 
-template <int BKS, int SPI, int S, bool PF, int WM, int WN, int T, bool AKC, bool BKC>
+template <int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC>
 inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     const dim3 block(64 * WM * WN);
-    return hipLaunchKernel((const void*)&gemm_lds_kernel<BKS, SPI, S, PF, WM, WN, T, AKC, BKC>, grid, block,
-                           kargs, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_lds_kernel<SPLIT, R, WM, WN, T, AKC, BKC>, grid, block, kargs, 0,
+                           stream);
 }
 
 // K-contiguous A <=> transpose_A == 0; K-contiguous B <=> transpose_B == 1.
-template <int BKS, int SPI, int S, bool PF, int WM, int WN, int T>
+// Barrier after 8 of the last K step's 32 MFMAs, one direct load every 2 MFMAs.
+template <int T>
 inline hipError_t dispatch_lds(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    if (!tA && tB) return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, true, true>(p, s);
-    if (!tA && !tB) return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, true, false>(p, s);
-    if (tA && tB) return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, false, true>(p, s);
-    return launch_lds_inst<BKS, SPI, S, PF, WM, WN, T, false, false>(p, s);
+    if (!tA && tB) return launch_lds_inst<8, 2, 2, 4, T, true, true>(p, s);
+    if (!tA && !tB) return launch_lds_inst<8, 2, 2, 4, T, true, false>(p, s);
+    if (tA && tB) return launch_lds_inst<8, 2, 2, 4, T, false, true>(p, s);
+    return launch_lds_inst<8, 2, 2, 4, T, false, false>(p, s);
 }
 
 }  // namespace tlg
