@@ -66,7 +66,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~40 ms of launches: the clock settles only after tens of ms of MFMA load
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c5a")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -198,7 +199,7 @@ def main():
             if name == args.workload:
                 continue
             c2 = W.CONFIGS[name]
-            rr = measure(c2, max(10, args.steps // 2), 5, log=log)
+            rr = measure(c2, max(10, args.steps // 2), 40, log=log)
             t = rr["ms"] * 1e-3
             entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
                      "GB/s": c2.algorithmic_bytes / t / 1e9, "plan": rr["plan"].describe()}
