@@ -61,7 +61,8 @@ typedef enum {
     TLG_VARIANT_SKINNY = 3,    /* M <= 16 rows per block, B stored [N,K], streaming  */
     TLG_VARIANT_EMPTY = 4,     /* M == 0 or N == 0: nothing to launch (chosen by create) */
     TLG_VARIANT_TILE_256_W8 = 5, /* 256x256x64 block tile, 8 wave64s (2 per SIMD), 2-stage ring */
-    TLG_VARIANT_TILE_256_DMA = 6 /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
+    TLG_VARIANT_TILE_256_DMA = 6, /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
+    TLG_VARIANT_TILE_128_DMA = 7  /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
 } tlg_variant;
 
 typedef enum {

@@ -80,9 +80,10 @@ def test_variant_choice_and_geometry_for_the_workloads():
                         transpose_B=case.transpose_B, epilogue="relu" if case.relu else "none")
 
     i = plan(C["c1"]).info
-    assert (i.variant, i.block_m, i.grid, i.k_tiles) == (2, 128, 4, 4)
+    assert (i.variant, i.block_m, i.grid, i.k_tiles) == (7, 128, 4, 4)
     i = plan(C["c2"]).info
-    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (2, 128, 128, 64, 64, 16)
+    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (7, 128, 128, 64, 64, 16)
+    assert (i.stages, i.threads, i.lds_bytes) == (4, 512, 4 * 2 * 128 * 64 * 2)
     i = plan(C["c3"]).info
     assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (6, 256, 256, 64, 131072, 512)
     i = plan(C["c4"]).info
@@ -97,13 +98,15 @@ def test_variant_choice_and_geometry_for_the_workloads():
 def test_plan_geometry_matches_the_pages_worked_figures():
     """LDS bytes and K trips of the 128x128x64 fp16 tile against the handbook's exercise answers."""
     rows = [l.split() for l in open(os.path.join(GOLDEN, "page_geometry.txt")) if l.strip() and l[0] != "#"]
-    two_stage = [r for r in rows if int(r[3]) == 2][0]
-    bm, bn, bk, stages, eb, K, per_op, per_stage, total, b_off, trips = map(int, two_stage)
-    g = tlg.Gemm(1024, 1024, K)
-    i = g.info
-    assert (i.block_m, i.block_n, i.block_k, i.stages) == (bm, bn, bk, stages)
-    assert i.lds_bytes == total and i.k_tiles == trips
-    assert bm * bk * eb == per_op and per_stage == 2 * per_op
+    # the default plan at 1024^3 is the 4-slot direct-load ring, the register-staged
+    # 128x128 variant keeps two stages
+    for variant, stages_wanted in (("auto", 4), ("tile128", 2)):
+        row = [r for r in rows if int(r[3]) == stages_wanted][0]
+        bm, bn, bk, stages, eb, K, per_op, per_stage, total, b_off, trips = map(int, row)
+        i = tlg.Gemm(1024, 1024, K, variant=variant).info
+        assert (i.block_m, i.block_n, i.block_k, i.stages) == (bm, bn, bk, stages)
+        assert i.lds_bytes == total and i.k_tiles == trips
+        assert bm * bk * eb == per_op and per_stage == 2 * per_op
     # the three-stage figures follow from the same per-stage size
     for r in rows:
         st, tot, boff = int(r[3]), int(r[8]), int(r[9])

@@ -91,7 +91,7 @@ def test_config5b_skinny_full():
 
 
 # ---------------------------------------------------------------- exactness
-@pytest.mark.parametrize("variant", ["tile256", "tile256w8", "tile256dma", "tile128", "skinny"])
+@pytest.mark.parametrize("variant", ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128", "skinny"])
 @pytest.mark.parametrize("ab", ["f16", "bf16"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_small_integers_exact(variant, ab, tA, tB):
@@ -99,7 +99,7 @@ def test_small_integers_exact(variant, ab, tA, tB):
         pytest.skip("the skinny kernel takes A stored [M,K] and B stored [N,K] only")
     # 300 rows: ragged for the 128 tile; the 256 tile needs 128-bit loads, so with A
     # stored [K, M] its M must be a multiple of 8 (304)
-    M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304}[variant]
+    M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304, "tile128dma": 304}[variant]
     case = W.GemmCase("smallint", M, 264, 200, ab=ab, c="f32", transpose_A=tA, transpose_B=tB,
                       dist="smallint", seed=77, relu=1)
     _full_check(case, variant=variant, exact=True)
@@ -109,10 +109,11 @@ def test_small_integers_exact(variant, ab, tA, tB):
 RAGGED = [1, 15, 17, 31, 33, 64, 65, 127, 129, 257]
 
 
-@pytest.mark.parametrize("variant", ["tile128", "tile256", "tile256w8", "tile256dma"])
+@pytest.mark.parametrize("variant", ["tile128", "tile256", "tile256w8", "tile256dma", "tile128dma"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_ragged_sweep(variant, tA, tB):
-    rng = np.random.default_rng(1000 + 10 * tA + tB + {"tile128": 0, "tile256": 100, "tile256w8": 200, "tile256dma": 300}[variant])
+    rng = np.random.default_rng(1000 + 10 * tA + tB + {"tile128": 0, "tile256": 100, "tile256w8": 200, "tile256dma": 300,
+                                                       "tile128dma": 400}[variant])
     for it in range(6):
         M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
         if variant != "tile128":       # 128-bit loads need the contiguous extent % 8 == 0
@@ -133,7 +134,7 @@ def test_skinny_rows(M):
 
 def test_accumulate_onto_c():
     for variant, tB in (("tile128", 0), ("tile256", 0), ("tile256w8", 0), ("tile256dma", 0), ("tile256dma", 1),
-                        ("skinny", 1)):
+                        ("tile128dma", 0), ("tile128dma", 1), ("skinny", 1)):
         for c in ("f16", "f32"):
             case = W.GemmCase(f"accum-{variant}-{c}", 16 if variant == "skinny" else 264, 200, 136,
                               c=c, transpose_B=tB, clear_accum=0, relu=1, seed=31)

@@ -22,7 +22,7 @@ lib_path = os.path.join(_PKG, "libtlg.so")
 F16, BF16, F32 = 1, 2, 3
 _TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "tile256w8": 5,
-            "tile256dma": 6}
+            "tile256dma": 6, "tile128dma": 7}
 EPILOGUES = {"none": 0, "relu": 1}
 
 STATUS = {0: "TLG_OK", -1: "TLG_ERR_INVALID_ARG", -2: "TLG_ERR_UNSUPPORTED", -3: "TLG_ERR_NULL",

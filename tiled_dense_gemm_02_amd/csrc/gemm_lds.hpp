@@ -134,22 +134,24 @@ __device__ inline void static_for(F&& f)
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// One operand of the 256 x 256 tile: 256 rows of its M/N index x BK of K,
-// filled by NW waves (each direct load fills one 1 KiB block).
-template <int BK, bool KC, int NW>
+// One operand of a tile: R rows of its M/N index x BK of K, filled by NW waves
+// (each direct load fills one 1 KiB block).
+template <int R, int BK, bool KC, int NW>
 struct LdsOperand {
-    static constexpr int R = 256;
     static constexpr int BYTES = R * BK * 2;
     static constexpr int L = BYTES / (NW * 64 * 16);  // direct loads per lane per tile
     static_assert(BYTES % (NW * 1024) == 0, "blocks must divide evenly over the waves");
-    static constexpr int RB = BK * 2, CH = BK / 8;
+    static constexpr int RB = BK * 2, CH = BK / 8;   // K-contiguous: row bytes, chunks per row
+    static constexpr int KRB = R * 2, KCH = R / 8;   // M/N-contiguous: bytes and chunks per row of k
+    static constexpr int KPB = 1024 / KRB;           // M/N-contiguous: rows of k per 1 KiB block
+    static_assert(KC || (KPB >= 1 && KCH >= 16), "M/N-contiguous rows of 128..512 elements");
 
     // Load i of a lane covers block b = i * NW + wave.  Along i the lane's row
     // (K-contiguous) or k (M/N-contiguous) advances by a constant step, and the
     // swizzle term is unchanged by that step, so one base offset per lane
     // describes all L loads.
     static constexpr int DROW = NW * (1024 / RB);   // K-contiguous: rows per load step
-    static constexpr int DK = 2 * NW;               // M/N-contiguous: k rows per load step
+    static constexpr int DK = NW * KPB;             // M/N-contiguous: k rows per load step
     static_assert(!KC || (4 * NW) % CH == 0, "swizzle must be invariant along the load step");
     static_assert(KC || DK % 16 == 0, "swizzle must be invariant along the load step");
 
@@ -181,8 +183,8 @@ struct LdsOperand {
             ld = (uint32_t)rows_total * 2u;
             base = (const char*)ptr + (uint64_t)r0 * 2u;
             base_bytes = (uint64_t)K * ld - (uint64_t)r0 * 2u;
-            idx0 = 2 * wave + (lane >> 5);
-            const int c = (lane & 31) ^ swz_mn(idx0);
+            idx0 = KPB * wave + lane / KCH;
+            const int c = (lane % KCH) ^ swz_mn(idx0);
             off0 = (uint32_t)idx0 * ld + (uint32_t)c * 16u;
             kc = 0;
             col_ok = c * 8 < rows_left;
@@ -222,21 +224,21 @@ struct LdsOperand {
             const int n = row0 + 4 * (s & 3);
             const int k = kk * 32 + g * 8 + (s >> 2);
             const int half = ((n >> 2) & 1) * 8;
-            const u32x2 lo = lds_read_tr16(region + k * 512 + (((n >> 3) ^ swz_mn(k)) << 4) + half);
-            const u32x2 hi = lds_read_tr16(region + (k + 4) * 512 + (((n >> 3) ^ swz_mn(k + 4)) << 4) + half);
+            const u32x2 lo = lds_read_tr16(region + k * KRB + (((n >> 3) ^ swz_mn(k)) << 4) + half);
+            const u32x2 hi = lds_read_tr16(region + (k + 4) * KRB + (((n >> 3) ^ swz_mn(k + 4)) << 4) + half);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
     }
 };
 
-template <int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC>
+template <int BM, int BN, int S, int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_lds_kernel(GemmParams p)
 {
-    constexpr int BM = 256, BN = 256, BK = 64, S = 2, NW = WAVES_M * WAVES_N;
+    constexpr int BK = 64, NW = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
-    using OpA = LdsOperand<BK, A_KC, NW>;
-    using OpB = LdsOperand<BK, B_KC, NW>;
+    using OpA = LdsOperand<BM, BK, A_KC, NW>;
+    using OpB = LdsOperand<BN, BK, B_KC, NW>;
     constexpr int STAGE = OpA::BYTES + OpB::BYTES;
     constexpr int LA = OpA::L, LB = OpB::L, L = LA + LB;
     constexpr int KS = BK / 32;                       // MFMA K steps per tile
@@ -247,7 +249,7 @@ gemm_lds_kernel(GemmParams p)
     // been freed), the other L-D at the start of the next tile.
     constexpr int D0 = (MI - 1 - BPOS) / R + 1;
     constexpr int D = D0 < L ? D0 : L;
-    static_assert(S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
+    static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
     static_assert(KS == 2, "fragment buffering assumes two K steps per tile");
     static_assert(SPLIT >= 1 && SPLIT < MPS, "barrier inside the last K step");
     static_assert(L - D == 0 || (L - D - 1) * R < BPOS, "early loads precede the barrier");
@@ -304,16 +306,19 @@ gemm_lds_kernel(GemmParams p)
     u32x4 fa[FM], fb[2][FN];
     const int arow = wm * WTM, bcol = wn * WTN;
 
-    // Prologue: tile 0 whole, the first D loads of tile 1; wait for tile 0.
-    {
-        const TileRes r0 = tile_res(0);
+    // Prologue: tiles 0 .. S-2 whole, the first D loads of tile S-1; wait for tile 0.
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) {
+        const TileRes r0 = tile_res(t);
 #pragma unroll
         for (int i = 0; i < L; ++i) issue_one(r0, i);
-        const TileRes r1 = tile_res(1);
+    }
+    {
+        const TileRes r1 = tile_res(S - 1);
 #pragma unroll
         for (int i = 0; i < D; ++i) issue_one(r1, i);
     }
-    wait_vmcnt<D>();
+    wait_vmcnt<(S - 2) * L + D>();
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[i] = opa.frag(smem, arow + i * 16, 0, lane);
@@ -410,26 +415,41 @@ gemm_lds_kernel(GemmParams p)
     }
 }
 
-template <int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC>
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC>
 inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
     const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
     const dim3 block(64 * WM * WN);
-    return hipLaunchKernel((const void*)&gemm_lds_kernel<SPLIT, R, WM, WN, T, AKC, BKC>, grid, block, kargs, 0,
-                           stream);
+    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC>, grid, block,
+                           kargs, 0, stream);
 }
 
 // K-contiguous A <=> transpose_A == 0; K-contiguous B <=> transpose_B == 1.
-// Barrier after 8 of the last K step's 32 MFMAs, one direct load every 2 MFMAs.
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T>
+inline hipError_t dispatch_lds_layout(const GemmParams& p, int tA, int tB, hipStream_t s)
+{
+    if (!tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, true>(p, s);
+    if (!tA && !tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, false>(p, s);
+    if (tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, true>(p, s);
+    return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, false>(p, s);
+}
+
+// 256 x 256 tiles: 8 waves of 128 x 64, 2-slot ring, barrier after 8 of the last
+// K step's 32 MFMAs, one direct load every 2 MFMAs.
 template <int T>
 inline hipError_t dispatch_lds(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    if (!tA && tB) return launch_lds_inst<8, 2, 2, 4, T, true, true>(p, s);
-    if (!tA && !tB) return launch_lds_inst<8, 2, 2, 4, T, true, false>(p, s);
-    if (tA && tB) return launch_lds_inst<8, 2, 2, 4, T, false, true>(p, s);
-    return launch_lds_inst<8, 2, 2, 4, T, false, false>(p, s);
+    return dispatch_lds_layout<256, 256, 2, 8, 2, 2, 4, T>(p, tA, tB, s);
+}
+
+// 128 x 128 tiles (grids too small for 256 x 256): 8 waves of 64 x 32, 4-slot ring,
+// barrier after 4 of the last K step's 8 MFMAs, one direct load every 2 MFMAs.
+template <int T>
+inline hipError_t dispatch_lds128(const GemmParams& p, int tA, int tB, hipStream_t s)
+{
+    return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T>(p, tA, tB, s);
 }
 
 }  // namespace tlg

@@ -1,4 +1,5 @@
-// Instances of the direct-load ring GEMM kernel: 256x256x64 tile, 2-slot LDS ring, 8 wave64s, MFMA 16x16x32, f16 operands.
+// Instances of the direct-load ring GEMM kernels (MFMA 16x16x32, 8 wave64s, f16 operands):
+// 256x256x64 tiles with a 2-slot LDS ring and 128x128x64 tiles with a 4-slot ring.
 #include "gemm_lds.hpp"
 
 namespace tlg {
@@ -6,6 +7,11 @@ namespace tlg {
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream)
 {
     return dispatch_lds<DT_F16>(p, transpose_A, transpose_B, stream);
+}
+
+hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream)
+{
+    return dispatch_lds128<DT_F16>(p, transpose_A, transpose_B, stream);
 }
 
 }  // namespace tlg

@@ -52,6 +52,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_EMPTY: return "empty";
     case TLG_VARIANT_TILE_256_W8: return "tile256w8";
     case TLG_VARIANT_TILE_256_DMA: return "tile256dma";
+    case TLG_VARIANT_TILE_128_DMA: return "tile128dma";
     default: return "?";
     }
 }
@@ -90,7 +91,7 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
 
     const int va = vec_for(tA ? M : K);
@@ -104,20 +105,21 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         variant = forced;
         if (forced == TLG_VARIANT_SKINNY && !skinny_ok) return TLG_ERR_UNSUPPORTED;
         if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8 ||
-             forced == TLG_VARIANT_TILE_256_DMA) && (va != 8 || vb != 8))
+             forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA) && (va != 8 || vb != 8))
             return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
         variant = TLG_VARIANT_SKINNY;
-    } else if (va == 8 && vb == 8 && ceil_div(M, 256) * ceil_div(N, 256) >= 256) {
-        variant = TLG_VARIANT_TILE_256_DMA;
+    } else if (va == 8 && vb == 8) {
+        // 256x256 tiles once they fill every CU, else 128x128 tiles (4x the workgroups).
+        variant = ceil_div(M, 256) * ceil_div(N, 256) >= 256 ? TLG_VARIANT_TILE_256_DMA : TLG_VARIANT_TILE_128_DMA;
     } else {
         variant = TLG_VARIANT_TILE_128;
     }
 
     // Launch-grid limits: the tile kernels use a 1-D grid of tile ids (int), the
     // skinny kernel a 2-D grid with row blocks in y.
-    if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA) {
-        const int64_t b = variant == TLG_VARIANT_TILE_128 ? 128 : 256;
+    if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA) {
+        const int64_t b = (variant == TLG_VARIANT_TILE_128 || variant == TLG_VARIANT_TILE_128_DMA) ? 128 : 256;
         if (ceil_div(M, b) * ceil_div(N, b) > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
         if (ceil_div(M, kSkinnyRows) > 65535 || ceil_div(N, kSkinnyNB) > INT32_MAX) return TLG_ERR_INVALID_ARG;
@@ -149,6 +151,13 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         in.threads = kLdsThreads;
         in.grid = ceil_div(M, kLdsBM) * ceil_div(N, kLdsBN);
         in.lds_bytes = (int64_t)kLdsStages * (kLdsBM + kLdsBN) * kLdsBK * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
+    } else if (variant == TLG_VARIANT_TILE_128_DMA) {
+        in.block_m = kLds128BM; in.block_n = kLds128BN; in.block_k = kLdsBK;
+        in.stages = kLds128Stages;
+        in.threads = kLdsThreads;
+        in.grid = ceil_div(M, kLds128BM) * ceil_div(N, kLds128BN);
+        in.lds_bytes = (int64_t)kLds128Stages * (kLds128BM + kLds128BN) * kLdsBK * 2;
         in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
     } else if (variant == TLG_VARIANT_SKINNY) {
         in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
@@ -232,6 +241,11 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_n = (int)ceil_div(p.N, kLdsBN);
         err = p.ab == TLG_F16 ? launch_lds_f16(gp, p.tA, p.tB, (hipStream_t)stream)
                               : launch_lds_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
+    } else if (p.variant == TLG_VARIANT_TILE_128_DMA) {
+        gp.tiles_m = (int)ceil_div(p.M, kLds128BM);
+        gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
+        err = p.ab == TLG_F16 ? launch_lds128_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                              : launch_lds128_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else {
         const int cfg = tile_config(p.variant);
         const TileShape ts = tile_shape(cfg);

@@ -78,9 +78,14 @@ inline hipError_t launch_tile(int cfg, const GemmParams& p, int ab_dtype, int tr
 }
 hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
 
-// Direct-load ring kernel (256x256x64 tile, 8 waves); 128-bit loads only.
+// Direct-load ring kernels (8 waves, 128-bit loads only): 256x256x64 tiles with
+// a 2-slot ring, and 128x128x64 tiles with a 4-slot ring for grids too small to
+// fill the chip with 256x256 tiles.
 constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64, kLdsStages = 2, kLdsThreads = 512;
+constexpr int kLds128BM = 128, kLds128BN = 128, kLds128Stages = 4;
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds128_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 
 }  // namespace tlg
