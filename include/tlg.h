@@ -123,8 +123,10 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  *          when K == 0 or M*N == 0.
  *   C    : device pointer to the packed M x N output (read when clear_accum == 0).
  * A and B must be aligned to their element size, and to 16 bytes when the plan
- * uses 128-bit loads for them (tlg_plan_info.vec_a / vec_b == 8); C to its
- * element size.  C must not overlap A or B.
+ * uses 128-bit loads for them (tlg_plan_info.vec_a / vec_b == 8), except that
+ * the direct-load variants (TILE_256_DMA, TILE_128_DMA) take K-contiguous
+ * operands (A with transpose_A == 0, B with transpose_B == 1) at element
+ * alignment and any K; C to its element size.  C must not overlap A or B.
  * Returns TLG_ERR_NULL, TLG_ERR_MISALIGNED, TLG_ERR_INVALID_ARG (overlap) or
  * TLG_ERR_HIP (launch failure); TLG_OK once the kernel is queued.  Execution
  * errors surface on the stream, as for any HIP kernel.

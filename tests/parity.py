@@ -27,17 +27,29 @@ def out_values(C: torch.Tensor) -> np.ndarray:
     return O.decode(W.bits16(Cc), code).reshape(Cc.shape)
 
 
+def _placed(X: torch.Tensor, offset: int, dev) -> torch.Tensor:
+    """X on the device, starting `offset` elements into a fresh allocation (offset 1 gives a
+    base address that is 2-byte but not 4-byte aligned)."""
+    if not offset:
+        return X.to(dev)
+    buf = torch.zeros(offset + X.numel(), dtype=X.dtype, device=dev)
+    view = buf[offset:offset + X.numel()].view(X.shape)
+    view.copy_(X.to(dev))
+    return view
+
+
 def run_gpu(case: W.GemmCase, A: torch.Tensor, B: torch.Tensor, C_in: torch.Tensor | None,
-            variant: str = "auto", guard: int = 0):
+            variant: str = "auto", guard: int = 0, a_offset: int = 0, b_offset: int = 0):
     """Run through tlg.Gemm; returns (C on device, plan).  With guard > 0, C lives inside a
-    larger buffer whose guard bands must come back untouched (checked by the caller)."""
+    larger buffer whose guard bands must come back untouched (checked by the caller).
+    a_offset / b_offset place A / B that many elements into their allocations."""
     import tiled_dense_gemm_02_amd as tlg
     dev = torch.device("cuda:0")
     plan = tlg.Gemm(case.M, case.N, case.K, _TORCH[case.ab], _TORCH[case.c],
                     transpose_A=bool(case.transpose_A), transpose_B=bool(case.transpose_B),
                     clear_accum=bool(case.clear_accum), epilogue="relu" if case.relu else "none",
                     variant=variant)
-    Ad, Bd = A.to(dev), B.to(dev)
+    Ad, Bd = _placed(A, a_offset, dev), _placed(B, b_offset, dev)
     n = case.M * case.N
     if guard:
         esz = 4 if case.c == "f32" else 2

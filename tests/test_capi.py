@@ -61,7 +61,11 @@ def test_create_rejects_bad_arguments():
     assert _create(16, 64, 777, tB=1, variant=3)[0] == UNSUPPORTED      # skinny needs K % 8 == 0
     assert _create(16, 64, 64, tB=0, variant=3)[0] == UNSUPPORTED       # skinny needs B stored [N,K]
     assert _create(100, 100, 777, variant=1)[0] == UNSUPPORTED          # 256 tile needs 128-bit loads
+    # direct loads: B stored [K, N] needs N % 8 == 0; K-contiguous operands take any K
     assert _create(100, 100, 777, variant=6)[0] == UNSUPPORTED
+    assert _create(100, 100, 777, tA=1, tB=1, variant=7)[0] == UNSUPPORTED
+    assert _create(100, 104, 777, variant=6)[0] == OK
+    assert _create(100, 100, 777, tB=1, variant=7)[0] == OK
     assert _create(100, 100, 96, variant=4)[0] == INVALID               # EMPTY is chosen, never forced
     assert lib.tlg_gemm_destroy(None) == OK
 
@@ -87,7 +91,7 @@ def test_variant_choice_and_geometry_for_the_workloads():
     i = plan(C["c3"]).info
     assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (6, 256, 256, 64, 131072, 512)
     i = plan(C["c4"]).info
-    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles) == (2, 1, 1, 8 * 12, 13)
+    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles) == (7, 8, 8, 8 * 12, 13)
     i = plan(C["c5a"]).info
     assert (i.variant, i.grid, i.k_tiles) == (6, 1024, 128)
     i = plan(C["c5b"]).info
@@ -120,13 +124,19 @@ def test_run_validation_happens_before_any_launch():
     assert g.run_ptrs(0, 4096, 8192) == NULL
     assert g.run_ptrs(4096, 0, 8192) == NULL
     assert g.run_ptrs(4096, 8192, 0) == NULL
-    assert g.run_ptrs(4096 + 8, 1 << 20, 1 << 21) == MISALIGNED     # 128-bit loads need 16-byte A
-    assert g.run_ptrs(4096, (1 << 20) + 2, 1 << 21) == MISALIGNED
+    # (every pointer set below fails validation: nothing is ever launched on them)
+    # direct loads: K-contiguous A at element alignment, B stored [K, N] at 16 bytes
+    assert g.info.variant == 7
+    assert g.run_ptrs(4096 + 1, 1 << 20, 1 << 21) == MISALIGNED     # A not element-aligned
+    assert g.run_ptrs(4096, (1 << 20) + 2, 1 << 21) == MISALIGNED   # B not 16-byte aligned
+    assert g.run_ptrs(4096, (1 << 20) + 8, 1 << 21) == MISALIGNED
     assert g.run_ptrs(4096, 1 << 20, (1 << 21) + 1) == MISALIGNED   # C not element-aligned
+    staged = tlg.Gemm(64, 64, 64, variant="tile128")                 # register-staged 128-bit loads
+    assert staged.run_ptrs(4096 + 8, 1 << 20, 1 << 21) == MISALIGNED
     # C overlapping A or B
     assert g.run_ptrs(1 << 20, 1 << 24, (1 << 20) + 4096) == INVALID
     assert g.run_ptrs(1 << 24, 1 << 20, (1 << 20) - 64) == INVALID
-    narrow = tlg.Gemm(64, 64, 63)                    # K % 8 != 0: 16-bit loads, 2-byte alignment
+    narrow = tlg.Gemm(64, 64, 63, variant="tile128")  # K % 8 != 0: 16-bit loads, 2-byte alignment
     assert narrow.info.vec_a == 1
     assert narrow.run_ptrs(4096 + 1, 1 << 20, 1 << 21) == MISALIGNED
     f32 = tlg.Gemm(64, 64, 64, out_dtype="f32")

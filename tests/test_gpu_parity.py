@@ -23,12 +23,13 @@ def _device():
     yield
 
 
-def _full_check(case, variant="auto", guard=0, exact=False):
+def _full_check(case, variant="auto", guard=0, exact=False, a_offset=0, b_offset=0):
     log(f"[case] {case.name} M={case.M} N={case.N} K={case.K} ab={case.ab} c={case.c} "
         f"tA={case.transpose_A} tB={case.transpose_B} relu={case.relu} clear={case.clear_accum} "
-        f"dist={case.dist} variant={variant}")
+        f"dist={case.dist} variant={variant} offsets={a_offset}/{b_offset}")
     A, B, C_in = W.make_inputs(case)
-    C, plan, buf, g = run_gpu(case, A, B, C_in, variant=variant, guard=guard)
+    C, plan, buf, g = run_gpu(case, A, B, C_in, variant=variant, guard=guard, a_offset=a_offset,
+                              b_offset=b_offset)
     gpu = out_values(C)
     o = oracle_full(case, A, B, C_in)
     if exact:
@@ -116,13 +117,35 @@ def test_ragged_sweep(variant, tA, tB):
                                                        "tile128dma": 400}[variant])
     for it in range(6):
         M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
-        if variant != "tile128":       # 128-bit loads need the contiguous extent % 8 == 0
-            M, N, K = ((x + 7) // 8 * 8 for x in (M, N, K))
+        r8 = lambda x: (x + 7) // 8 * 8
+        if variant in ("tile256", "tile256w8"):     # 128-bit register-staged loads: every extent % 8 == 0
+            M, N, K = r8(M), r8(N), r8(K)
+        elif variant in ("tile256dma", "tile128dma"):   # only M/N-contiguous rows need % 8 == 0
+            M = r8(M) if tA else M
+            N = N if tB else r8(N)
         ab = "f16" if it % 2 == 0 else "bf16"
         c = ["f16", "f32", "bf16"][it % 3]
         case = W.GemmCase(f"ragged{it}", M, N, K, ab=ab, c=c, transpose_A=tA, transpose_B=tB,
                           relu=it % 2, seed=500 + it)
         _full_check(case, variant=variant, guard=1024)
+
+
+@pytest.mark.parametrize("variant", ["tile256dma", "tile128dma"])
+@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 1)])
+def test_direct_loads_unaligned_k_and_base(variant, tA, tB):
+    """K-contiguous operands at any K and at a base address 2 bytes off 16-byte alignment:
+    unaligned 128-bit loads plus the trimmed K tail."""
+    for it, K in enumerate((1, 7, 9, 63, 65, 200, 777)):
+        M = 136 if tA else 130
+        N = 77 if tB else 96
+        case = W.GemmCase(f"unaligned-k{K}", M, N, K, ab="f16" if it % 2 == 0 else "bf16",
+                          c=["f16", "f32"][it % 2], transpose_A=tA, transpose_B=tB, relu=it % 2,
+                          seed=700 + it)
+        _full_check(case, variant=variant, guard=1024, a_offset=0 if tA else 1, b_offset=1 if tB else 0)
+    # small integers: exact
+    case = W.GemmCase("unaligned-int", 130 if not tA else 136, 77 if tB else 96, 333, ab="bf16", c="f32",
+                      transpose_A=tA, transpose_B=tB, dist="smallint", seed=790)
+    _full_check(case, variant=variant, exact=True, a_offset=0 if tA else 1, b_offset=1 if tB else 0)
 
 
 @pytest.mark.parametrize("M", [1, 8, 16, 17, 32])

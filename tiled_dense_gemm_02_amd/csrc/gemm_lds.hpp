@@ -12,6 +12,11 @@
 // out-of-range offset and the hardware writes zeros (the zero safe value of
 // out-of-bounds reads, "core primitives" chapter, section 4.2).  The swizzled
 // LDS layout is produced by choosing which global chunk each lane fetches.
+// K-contiguous rows need not be 16-byte aligned (K % 8 != 0): gfx950 buffer
+// loads accept 2-byte aligned addresses, and the one chunk per row that
+// straddles K is trimmed in LDS before the last K tile is published (for the
+// matrix's last row, whose chunk runs past the buffer, it is refetched).
+// M/N-contiguous rows must hold a multiple of 8 elements.
 //
 // Operand layouts in LDS (one ring slot; "rows" are the operand's M or N index):
 //   K-contiguous operand (A stored [M,K], B stored [N,K]): 256 rows of 64
@@ -211,6 +216,41 @@ struct LdsOperand {
         }
     }
 
+    // K-contiguous operand with K % 8 != 0: in the last K tile the chunk holding
+    // element K-1 also holds up to 7 elements past K (the next row's first ones).
+    // Once the lane's own loads of that tile have landed, it zeroes them in LDS
+    // (wave_base: the tile's slot region of this operand + 1 KiB * wave).  The
+    // matrix's last row is different: its chunk runs past the end of the buffer,
+    // and the range check returns the whole 16-byte load as zeros, so its valid
+    // elements (at most 7) are fetched again with 16-bit loads.
+    __device__ void fix_k_tail(char* wave_base, int k0, int K, int lane) const
+    {
+        if constexpr (KC) {
+            const int nvalid = K - (k0 + kc);
+            if (nvalid > 0 && nvalid < 8) {
+                u32x4 keep;
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    keep[w] = 2 * w + 1 < nvalid ? 0xffffffffu : (2 * w < nvalid ? 0x0000ffffu : 0u);
+                const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (uint64_t)k0 * 2u, base_bytes - (uint64_t)k0 * 2u);
+#pragma unroll
+                for (int i = 0; i < L; ++i) {
+                    const int row = idx0 + i * DROW;
+                    u32x4* q = (u32x4*)(wave_base + i * NW * 1024 + lane * 16);
+                    u32x4 v = *q & keep;
+                    if (row == rows_left - 1) {
+                        uint32_t h[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            h[e] = e < nvalid ? buf_load2(r, (uint32_t)row * ld + (uint32_t)(kc + e) * 2u) : 0u;
+                        v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+                    }
+                    *q = v;
+                }
+            }
+        }
+    }
+
     // MFMA 16x16x32 operand of rows row0..row0+15 (row0 a multiple of 16), K step
     // kk (32 wide): lane l holds row row0 + l%16 and K elements 8*(l/16) .. +7.
     __device__ u32x4 frag(const char* region, int row0, int kk, int lane) const
@@ -297,6 +337,19 @@ gemm_lds_kernel(GemmParams p)
             dma16(r.rb, opb.voff(i - LA, r.k0, K), r.slot + (uint32_t)OpA::BYTES + (uint32_t)((i - LA) * NW * 1024));
     };
 
+    // Last K tile with K % 8 != 0: trim the elements past K that this lane's
+    // loads brought into LDS (called after they landed, before the barrier that
+    // publishes the tile).  The asm statements keep the compiler from moving LDS
+    // accesses across the preceding wait.
+    const bool k_tail = (K & 7) != 0;
+    auto fix_k_tail = [&](int t) {
+        asm volatile("" ::: "memory");
+        char* region = smem + (t % S) * STAGE + wave * 1024;
+        opa.fix_k_tail(region, t * BK, K, lane);
+        opb.fix_k_tail(region + OpA::BYTES, t * BK, K, lane);
+        asm volatile("" ::: "memory");
+    };
+
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -319,6 +372,10 @@ gemm_lds_kernel(GemmParams p)
         for (int i = 0; i < D; ++i) issue_one(r1, i);
     }
     wait_vmcnt<(S - 2) * L + D>();
+    if (k_tail && TP == 1) {
+        fix_k_tail(0);
+        wait_vmcnt_lgkm0<(S - 2) * L + D>();
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[i] = opa.frag(smem, arow + i * 16, 0, lane);
@@ -343,6 +400,10 @@ gemm_lds_kernel(GemmParams p)
                 // every wave's part of tile j+1 and frees tile j's slot.
                 __builtin_amdgcn_s_setprio(0);
                 wait_vmcnt_lgkm0<(S - 2) * L>();
+                if (k_tail && j + 2 == TP) {
+                    fix_k_tail(j + 1);
+                    wait_vmcnt_lgkm0<(S - 2) * L>();
+                }
                 __syncthreads();
                 __builtin_amdgcn_s_setprio(1);
             }

@@ -22,6 +22,7 @@ struct tlg_gemm_s {
     int ab, c, tA, tB, clear, relu;
     int variant;
     int vec_a, vec_b;
+    int align_a, align_b;  // byte alignment run() requires of A and B
     tlg_plan_info info;
     char desc[256];
 };
@@ -59,11 +60,12 @@ const char* variant_name(int v)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// 128-bit loads need the contiguous dimension of the operand to be a multiple
-// of 8 elements (every 16-byte chunk lies inside one row and is 16-byte aligned
-// when the base is); otherwise the operand is loaded element by element (the
-// narrow-load fallback for unaligned rows, "core primitives" chapter, T.copy
-// notes on alignment).
+// The register-staged kernels' 128-bit loads need the contiguous dimension of
+// the operand to be a multiple of 8 elements (every 16-byte chunk lies inside one
+// row and is 16-byte aligned when the base is); otherwise the operand is loaded
+// element by element (the narrow-load fallback for unaligned rows, "core
+// primitives" chapter, T.copy notes on alignment).  The direct-load kernels
+// relax this for K-contiguous operands (see dma_ok below).
 int vec_for(int64_t contiguous_len) { return contiguous_len % 8 == 0 ? 8 : 1; }
 
 bool flag_ok(int v) { return v == 0 || v == 1; }
@@ -97,6 +99,9 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     const int va = vec_for(tA ? M : K);
     const int vb = vec_for(tB ? K : N);
     const bool skinny_ok = !tA && tB && K % 8 == 0;
+    // Direct-load kernels: a K-contiguous operand may have any K (unaligned 128-bit
+    // loads, tail trimmed in LDS); an M/N-contiguous one needs rows of 8k elements.
+    const bool dma_ok = (!tA || M % 8 == 0) && (tB || N % 8 == 0);
 
     int variant;
     if (M == 0 || N == 0) {
@@ -104,12 +109,13 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     } else if (forced != TLG_VARIANT_AUTO) {
         variant = forced;
         if (forced == TLG_VARIANT_SKINNY && !skinny_ok) return TLG_ERR_UNSUPPORTED;
-        if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8 ||
-             forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA) && (va != 8 || vb != 8))
+        if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
+            return TLG_ERR_UNSUPPORTED;
+        if ((forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
         variant = TLG_VARIANT_SKINNY;
-    } else if (va == 8 && vb == 8) {
+    } else if (dma_ok) {
         // 256x256 tiles once they fill every CU, else 128x128 tiles (4x the workgroups).
         variant = ceil_div(M, 256) * ceil_div(N, 256) >= 256 ? TLG_VARIANT_TILE_256_DMA : TLG_VARIANT_TILE_128_DMA;
     } else {
@@ -130,8 +136,16 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
     p->M = M; p->N = N; p->K = K;
     p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
     p->variant = variant;
-    p->vec_a = variant == TLG_VARIANT_SKINNY ? 8 : va;
-    p->vec_b = variant == TLG_VARIANT_SKINNY ? 8 : vb;
+    const bool dma = variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA;
+    p->vec_a = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : va;
+    p->vec_b = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : vb;
+    if (dma) {
+        p->align_a = tA ? 16 : 2;   // K-contiguous operands take unaligned 128-bit loads
+        p->align_b = tB ? 2 : 16;
+    } else {
+        p->align_a = p->vec_a == 8 ? 16 : 2;
+        p->align_b = p->vec_b == 8 ? 16 : 2;
+    }
 
     tlg_plan_info& in = p->info;
     in.variant = variant;
@@ -214,8 +228,7 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
     const int cb = elem_bytes(p.c);
     if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
     if (p.K > 0) {
-        if ((a % 2) || (b % 2)) return TLG_ERR_MISALIGNED;
-        if ((p.vec_a == 8 && a % 16) || (p.vec_b == 8 && b % 16)) return TLG_ERR_MISALIGNED;
+        if ((a % (uintptr_t)p.align_a) || (b % (uintptr_t)p.align_b)) return TLG_ERR_MISALIGNED;
     }
     const uint64_t a_bytes = p.K > 0 ? (uint64_t)p.M * (uint64_t)p.K * 2u : 0;
     const uint64_t b_bytes = p.K > 0 ? (uint64_t)p.K * (uint64_t)p.N * 2u : 0;
