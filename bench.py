@@ -7,8 +7,9 @@
 A step is one launch of the whole hot path (global->LDS tile copies, the
 pipelined MFMA K loop and the fused epilogue) over one batch of seeded synthetic
 inputs already resident in HBM.  The headline workload is the 8192^3 fp16 GEMM
-(fp32 accumulate, fp16 out); the 4096^3 ReLU GEMM and the memory-bound skinny
-16x16384x8192 case are reported alongside in "secondary".  Operand sets are
+(fp32 accumulate, fp16 out); the 4096^3 ReLU GEMM, the memory-bound skinny
+16x16384x8192 case and the small 1024^3, 1000x1500x777 bf16 and 256^3 cases are
+reported alongside in "secondary".  Operand sets are
 rotated so that the inputs of consecutive launches are not the same buffers
 (keeps the ~256 MB Infinity Cache from serving repeat reads).
 
@@ -39,6 +40,7 @@ KERNEL_SOURCES = {
     5: ["gemm_tile.hpp", "tlg_device.hpp"],
     3: ["gemm_skinny.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     6: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
+    7: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
 }
 
 
@@ -94,8 +96,15 @@ def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None):
     Bd = [B.to(dev) for _ in range(nsets)]
     C = torch.empty((case.M, case.N), dtype=plan_out_dtype(case), device=dev)
     stream = torch.cuda.current_stream(dev)
+    # One checked launch through the tensor interface, then the raw-pointer form (the
+    # library's own argument checks still run on every call; the Python-side tensor
+    # checks would otherwise cost as much as a small kernel).
+    plan.run(Ad[0], Bd[0], C, stream)
+    ptrs = [(Ad[i].data_ptr(), Bd[i].data_ptr()) for i in range(nsets)]
+    c_ptr, sh = C.data_ptr(), stream.cuda_stream
+    status = 0
     for i in range(warmup):
-        plan.run(Ad[i % nsets], Bd[i % nsets], C, stream)
+        status |= plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh)
     torch.cuda.synchronize()
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
@@ -105,9 +114,11 @@ def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None):
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        plan.run(Ad[i % nsets], Bd[i % nsets], C, stream)
+        status |= plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh)
     end.record(stream)
     torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError(f"tlg_gemm_run failed during the timed launches (status {status})")
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
     return {"ms": ms, "wall_s": wall, "plan": plan, "C": C, "A": A, "B": B, "nsets": nsets}
@@ -195,7 +206,7 @@ def main():
 
     if not args.no_secondary:
         sec = []
-        for name in ("c3", "c5b"):
+        for name in ("c3", "c5b", "c2", "c4", "c1"):
             if name == args.workload:
                 continue
             c2 = W.CONFIGS[name]
