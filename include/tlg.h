@@ -34,9 +34,11 @@
  *
  * Ownership: the caller owns A, B and C (device memory) and keeps them alive
  * until the work queued on the stream has finished.  The library owns the
- * plan.  tlg_gemm_run allocates nothing, does not synchronise, and enqueues at
- * most one kernel on the given stream.  A plan is immutable after create, so
- * concurrent runs of one plan on different streams are safe.
+ * plan, and the device workspace of a split-K plan (see tlg_plan_info.splits).
+ * tlg_gemm_run allocates nothing, does not synchronise, and enqueues at most
+ * one kernel on the given stream.  A plan is immutable after create; runs of a
+ * plan without a workspace may overlap on different streams, runs of a split-K
+ * plan may not (they share its workspace).
  */
 #ifndef TLG_H
 #define TLG_H
@@ -62,7 +64,8 @@ typedef enum {
     TLG_VARIANT_EMPTY = 4,     /* M == 0 or N == 0: nothing to launch (chosen by create) */
     TLG_VARIANT_TILE_256_W8 = 5, /* 256x256x64 block tile, 8 wave64s (2 per SIMD), 2-stage ring */
     TLG_VARIANT_TILE_256_DMA = 6, /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
-    TLG_VARIANT_TILE_128_DMA = 7  /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
+    TLG_VARIANT_TILE_128_DMA = 7, /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
+    TLG_VARIANT_TILE_128_DMA_SPLITK = 8 /* as 7, K split over several workgroups per tile (plan owns a workspace) */
 } tlg_variant;
 
 typedef enum {
@@ -84,8 +87,9 @@ typedef struct {
     int32_t vec_a, vec_b;  /* elements per global load of A / B (8 = 128-bit, 1 = 16-bit) */
     int64_t grid;          /* workgroups per launch                                   */
     int64_t lds_bytes;     /* LDS bytes per workgroup                                 */
-    int32_t k_tiles;       /* trips of the K loop per workgroup                       */
-    int32_t reserved;
+    int32_t k_tiles;       /* trips of the K loop per workgroup (at most)             */
+    int32_t splits;        /* workgroups per output tile along K (1: no split)        */
+    int64_t workspace_bytes; /* device workspace the plan owns (0 unless splits > 1)   */
 } tlg_plan_info;
 
 /*
@@ -100,12 +104,30 @@ typedef struct {
  *   epilogue     : TLG_EPI_NONE or TLG_EPI_RELU.
  * Returns TLG_ERR_NULL if out is NULL, TLG_ERR_INVALID_ARG for a bad dimension,
  * enum or flag, TLG_ERR_UNSUPPORTED for an operand dtype other than F16/BF16,
- * TLG_ERR_NOMEM if the plan cannot be allocated.  No device work happens here.
- * On failure *out is set to NULL.
+ * TLG_ERR_NOMEM if the plan cannot be allocated.  Plans with K split over
+ * several workgroups per tile (tlg_plan_info.splits > 1, chosen for output grids
+ * of fewer than 128 tiles of 128x128 with at least 8 K tiles of 64) allocate a
+ * device workspace here (tlg_plan_info.workspace_bytes: fp32 partial tiles plus
+ * one counter per tile), on the device current at the call, zero its counters
+ * and wait for that to finish (TLG_ERR_HIP if any of it fails); other plans do
+ * no device work.  On failure *out is set to NULL.
  */
 tlg_status tlg_gemm_create(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
                            int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
                            int32_t transpose_B, int32_t clear_accum, int32_t epilogue);
+
+/*
+ * Fill *info with the plan that tlg_gemm_create_variant (variant ==
+ * TLG_VARIANT_AUTO: tlg_gemm_create) would make for these arguments, without
+ * making it: host work only, no device is needed.  Lets a caller learn the
+ * chosen variant, launch grid and workspace size in advance.  Returns the
+ * status create would return for the same arguments, except that it never
+ * returns TLG_ERR_HIP or TLG_ERR_NOMEM; TLG_ERR_NULL for a NULL info.
+ */
+tlg_status tlg_gemm_select(tlg_plan_info *info, int64_t M, int64_t N, int64_t K,
+                           int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
+                           int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
+                           int32_t variant);
 
 /*
  * As tlg_gemm_create, but forces a kernel variant (tlg_variant).  Returns
@@ -124,16 +146,21 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  *   C    : device pointer to the packed M x N output (read when clear_accum == 0).
  * A and B must be aligned to their element size, and to 16 bytes when the plan
  * uses 128-bit loads for them (tlg_plan_info.vec_a / vec_b == 8), except that
- * the direct-load variants (TILE_256_DMA, TILE_128_DMA) take K-contiguous
+ * the direct-load variants (TILE_256_DMA, TILE_128_DMA, TILE_128_DMA_SPLITK) take K-contiguous
  * operands (A with transpose_A == 0, B with transpose_B == 1) at element
  * alignment and any K; C to its element size.  C must not overlap A or B.
  * Returns TLG_ERR_NULL, TLG_ERR_MISALIGNED, TLG_ERR_INVALID_ARG (overlap) or
  * TLG_ERR_HIP (launch failure); TLG_OK once the kernel is queued.  Execution
  * errors surface on the stream, as for any HIP kernel.
+ * Plans without a workspace may run concurrently on several streams.  A plan
+ * with a workspace (splits > 1) must run on the device it was created on
+ * (TLG_ERR_INVALID_ARG otherwise), and its runs must not overlap in time: they
+ * share the workspace, so issue them on one stream or order them by events.
  */
 tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, void *stream);
 
-/* Release a plan.  NULL is accepted (no-op, TLG_OK). */
+/* Release a plan (and its workspace, if any; the caller first makes sure no run of
+ * the plan is still in flight).  NULL is accepted (no-op, TLG_OK). */
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan);
 
 /* Fill *info with the plan's launch facts.  TLG_ERR_NULL for a NULL argument. */

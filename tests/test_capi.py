@@ -57,6 +57,7 @@ def test_create_rejects_bad_arguments():
     assert _create(4, 4, 4, clear=3)[0] == INVALID
     assert _create(4, 4, 4, epi=2)[0] == INVALID
     assert _create(4, 4, 4, variant=9)[0] == INVALID
+    assert _create(100, 100, 777, tA=1, tB=1, variant=8)[0] == UNSUPPORTED
     # forced variants that cannot run the request
     assert _create(16, 64, 777, tB=1, variant=3)[0] == UNSUPPORTED      # skinny needs K % 8 == 0
     assert _create(16, 64, 64, tB=0, variant=3)[0] == UNSUPPORTED       # skinny needs B stored [N,K]
@@ -79,35 +80,72 @@ def test_variant_choice_and_geometry_for_the_workloads():
     import tlg_workloads as W
     C = W.CONFIGS
 
-    def plan(case):
-        return tlg.Gemm(case.M, case.N, case.K, case.ab, case.c, transpose_A=case.transpose_A,
-                        transpose_B=case.transpose_B, epilogue="relu" if case.relu else "none")
+    def info(case, variant="auto"):
+        return tlg.select(case.M, case.N, case.K, case.ab, case.c, transpose_A=case.transpose_A,
+                          transpose_B=case.transpose_B, epilogue="relu" if case.relu else "none",
+                          variant=variant)
 
-    i = plan(C["c1"]).info
-    assert (i.variant, i.block_m, i.grid, i.k_tiles) == (7, 128, 4, 4)
-    i = plan(C["c2"]).info
+    i = info(C["c1"])
+    assert (i.variant, i.block_m, i.grid, i.k_tiles, i.splits) == (7, 128, 4, 4, 1)
+    # 1024^3: 64 tiles of 128x128, 16 K tiles each (too short a K to split)
+    i = info(C["c2"])
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (7, 128, 128, 64, 64, 16)
-    assert (i.stages, i.threads, i.lds_bytes) == (4, 512, 4 * 2 * 128 * 64 * 2)
-    i = plan(C["c3"]).info
+    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (4, 512, 4 * 2 * 128 * 64 * 2, 1, 0)
+    # forced split: 4 ranges of 4 K tiles (256 workgroups)
+    i = info(C["c2"], "tile128dma_sk")
+    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles, i.splits) == (8, 128, 128, 64, 256, 4, 4)
+    assert i.workspace_bytes == 64 * 4 * 128 * 128 * 4 + 256
+    i = info(C["c3"])
     assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (6, 256, 256, 64, 131072, 512)
-    i = plan(C["c4"]).info
-    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles) == (7, 8, 8, 8 * 12, 13)
-    i = plan(C["c5a"]).info
+    i = info(C["c4"])
+    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (7, 8, 8, 8 * 12, 13, 1)
+    # forced split of 1000x1500x777: 8 x 12 = 96 tiles, 13 K tiles -> 2 ranges (7 + 6 K tiles)
+    i = info(C["c4"], "tile128dma_sk")
+    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (8, 8, 8, 8 * 12 * 2, 7, 2)
+    i = info(C["c5a"])
     assert (i.variant, i.grid, i.k_tiles) == (6, 1024, 128)
-    i = plan(C["c5b"]).info
+    i = info(C["c5b"])
     assert (i.variant, i.grid, i.vec_a, i.vec_b) == (3, 256, 8, 8)
-    assert "skinny" in plan(C["c5b"]).describe()
+    # a plan without a workspace needs no device, and describes itself
+    c5b = C["c5b"]
+    assert "skinny" in tlg.Gemm(c5b.M, c5b.N, c5b.K, transpose_B=True).describe()
+
+
+def test_split_k_choice():
+    """Ranges of whole K tiles: ~256 workgroups, at most 8 ranges, >= 2 K tiles per range,
+    no empty range; only for fewer than 128 tiles of 128x128 and at least 48 K tiles."""
+    for M, N, K in [(128, 128, 64 * 64), (256, 384, 8192), (1024, 1024, 1024), (512, 512, 600),
+                    (1000, 1500, 777), (128, 256, 513), (2048, 1024, 4096), (1536, 1280, 2048),
+                    (1024, 1024, 3072), (1000, 1500, 3000), (640, 640, 5000), (100, 3000, 20000)]:
+        i = tlg.select(M, N, K, transpose_B=True)
+        tiles, kt = -(-M // 128) * -(-N // 128), -(-K // 64)
+        if tiles >= 128 or kt < 48:
+            assert i.splits == 1 and i.variant != 8
+            continue
+        s = i.splits
+        per = -(-kt // s)
+        assert i.variant == (8 if s > 1 else 7)
+        assert 1 <= s <= 8 and per >= 2 and (s - 1) * per < kt
+        assert i.k_tiles == per and i.grid == tiles * s
+        assert s == 8 or tiles * s <= 256 or s == 1
+        if s > 1:
+            assert i.workspace_bytes == tiles * s * 128 * 128 * 4 + -(-tiles * 4 // 256) * 256
+    assert tlg.select(128, 128, 4096).splits == 8
+    assert tlg.select(1024, 1024, 1024, variant="tile128dma_sk").splits == 4
+    lib = tlg.load_library()
+    assert lib.tlg_gemm_select(None, 1, 1, 1, 1, 1, 0, 0, 1, 0, 0) == NULL
+    assert lib.tlg_gemm_select(ctypes.byref(tlg.PlanInfo()), -1, 1, 1, 1, 1, 0, 0, 1, 0, 0) == INVALID
 
 
 def test_plan_geometry_matches_the_pages_worked_figures():
     """LDS bytes and K trips of the 128x128x64 fp16 tile against the handbook's exercise answers."""
     rows = [l.split() for l in open(os.path.join(GOLDEN, "page_geometry.txt")) if l.strip() and l[0] != "#"]
-    # the default plan at 1024^3 is the 4-slot direct-load ring, the register-staged
-    # 128x128 variant keeps two stages
-    for variant, stages_wanted in (("auto", 4), ("tile128", 2)):
+    # the unsplit 128x128 direct-load ring has 4 slots, the register-staged 128x128
+    # variant keeps two stages
+    for variant, stages_wanted in (("tile128dma", 4), ("tile128", 2)):
         row = [r for r in rows if int(r[3]) == stages_wanted][0]
         bm, bn, bk, stages, eb, K, per_op, per_stage, total, b_off, trips = map(int, row)
-        i = tlg.Gemm(1024, 1024, K, variant=variant).info
+        i = tlg.select(1024, 1024, K, variant=variant)
         assert (i.block_m, i.block_n, i.block_k, i.stages) == (bm, bn, bk, stages)
         assert i.lds_bytes == total and i.k_tiles == trips
         assert bm * bk * eb == per_op and per_stage == 2 * per_op

@@ -54,10 +54,15 @@ def test_config1_relu_256():
 def test_config2_1024():
     plan = _full_check(W.CONFIGS["c2"])
     assert plan.info.k_tiles == 16          # 1024 / 64, the pages' K trip count
+    plan = _full_check(W.CONFIGS["c2"], variant="tile128dma_sk")
+    assert plan.info.splits == 4 and plan.info.k_tiles == 4   # K split in 4 ranges of 4 K tiles
 
 
 def test_config4_ragged_bf16_bt_f32out():
-    _full_check(W.CONFIGS["c4"], guard=4096)
+    plan = _full_check(W.CONFIGS["c4"], guard=4096)
+    assert plan.info.splits == 1
+    plan = _full_check(W.CONFIGS["c4"], variant="tile128dma_sk", guard=4096)
+    assert plan.info.splits == 2
 
 
 def _sampled_check(case, count):
@@ -92,7 +97,8 @@ def test_config5b_skinny_full():
 
 
 # ---------------------------------------------------------------- exactness
-@pytest.mark.parametrize("variant", ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128", "skinny"])
+@pytest.mark.parametrize("variant", ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk", "tile128",
+                                     "skinny"])
 @pytest.mark.parametrize("ab", ["f16", "bf16"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_small_integers_exact(variant, ab, tA, tB):
@@ -100,7 +106,8 @@ def test_small_integers_exact(variant, ab, tA, tB):
         pytest.skip("the skinny kernel takes A stored [M,K] and B stored [N,K] only")
     # 300 rows: ragged for the 128 tile; the 256 tile needs 128-bit loads, so with A
     # stored [K, M] its M must be a multiple of 8 (304)
-    M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304, "tile128dma": 304}[variant]
+    M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304, "tile128dma": 304,
+         "tile128dma_sk": 304}[variant]
     case = W.GemmCase("smallint", M, 264, 200, ab=ab, c="f32", transpose_A=tA, transpose_B=tB,
                       dist="smallint", seed=77, relu=1)
     _full_check(case, variant=variant, exact=True)
@@ -110,17 +117,17 @@ def test_small_integers_exact(variant, ab, tA, tB):
 RAGGED = [1, 15, 17, 31, 33, 64, 65, 127, 129, 257]
 
 
-@pytest.mark.parametrize("variant", ["tile128", "tile256", "tile256w8", "tile256dma", "tile128dma"])
+@pytest.mark.parametrize("variant", ["tile128", "tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_ragged_sweep(variant, tA, tB):
     rng = np.random.default_rng(1000 + 10 * tA + tB + {"tile128": 0, "tile256": 100, "tile256w8": 200, "tile256dma": 300,
-                                                       "tile128dma": 400}[variant])
+                                                       "tile128dma": 400, "tile128dma_sk": 500}[variant])
     for it in range(6):
         M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
         r8 = lambda x: (x + 7) // 8 * 8
         if variant in ("tile256", "tile256w8"):     # 128-bit register-staged loads: every extent % 8 == 0
             M, N, K = r8(M), r8(N), r8(K)
-        elif variant in ("tile256dma", "tile128dma"):   # only M/N-contiguous rows need % 8 == 0
+        elif variant in ("tile256dma", "tile128dma", "tile128dma_sk"):   # only M/N-contiguous rows need % 8 == 0
             M = r8(M) if tA else M
             N = N if tB else r8(N)
         ab = "f16" if it % 2 == 0 else "bf16"
@@ -130,7 +137,7 @@ def test_ragged_sweep(variant, tA, tB):
         _full_check(case, variant=variant, guard=1024)
 
 
-@pytest.mark.parametrize("variant", ["tile256dma", "tile128dma"])
+@pytest.mark.parametrize("variant", ["tile256dma", "tile128dma", "tile128dma_sk"])
 @pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 1)])
 def test_direct_loads_unaligned_k_and_base(variant, tA, tB):
     """K-contiguous operands at any K and at a base address 2 bytes off 16-byte alignment:
@@ -157,7 +164,8 @@ def test_skinny_rows(M):
 
 def test_accumulate_onto_c():
     for variant, tB in (("tile128", 0), ("tile256", 0), ("tile256w8", 0), ("tile256dma", 0), ("tile256dma", 1),
-                        ("tile128dma", 0), ("tile128dma", 1), ("skinny", 1)):
+                        ("tile128dma", 0), ("tile128dma", 1), ("tile128dma_sk", 0), ("tile128dma_sk", 1),
+                        ("skinny", 1)):
         for c in ("f16", "f32"):
             case = W.GemmCase(f"accum-{variant}-{c}", 16 if variant == "skinny" else 264, 200, 136,
                               c=c, transpose_B=tB, clear_accum=0, relu=1, seed=31)
@@ -189,6 +197,34 @@ def test_deterministic():
     C1, _, _, _ = run_gpu(case, A, B, None)
     C2, _, _, _ = run_gpu(case, A, B, None)
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+def test_split_k_plan_reused():
+    """One split-K plan run on several inputs in a row (its per-tile counters return to
+    zero after every launch), then on the same inputs again: each result within the
+    tolerance, repeats bit-identical.  Range counts 2, 3, 4, 6 and 8, ragged last K tiles
+    (K = 1000: the 16th K tile is 40 wide) and a last range shorter than the others
+    (K = 3100: 49 K tiles in 5 ranges of 9 and one of 4, whose last K tile is 28 wide)."""
+    import tiled_dense_gemm_02_amd as tlg
+    for M, N, K, variant, splits in ((128, 384, 256, "tile128dma_sk", 2), (300, 264, 520, "tile128dma_sk", 3),
+                                     (1024, 1024, 4096, "auto", 4), (1000, 600, 3100, "auto", 6),
+                                     (200, 72, 1000, "tile128dma_sk", 8)):
+        want = tlg.select(M, N, K, transpose_B=True, epilogue="relu", variant=variant)
+        case = W.GemmCase(f"sk-{M}x{N}x{K}", M, N, K, transpose_B=1, relu=1, seed=1234)
+        plan = tlg.Gemm(M, N, K, transpose_B=True, epilogue="relu", variant=variant)
+        assert plan.info.variant == 8 and plan.info.splits == splits
+        assert plan.info.as_dict() == want.as_dict()
+        log(f"[case] split-K reuse {plan.describe()}")
+        outs = []
+        for rep in range(4):
+            A, B, _ = W.make_inputs(case.with_(seed=1234 + rep % 2))
+            C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+            plan.run(A.cuda(), B.cuda(), C)
+            torch.cuda.synchronize()
+            o = oracle_full(case, A, B, None)
+            assert_within_tolerance(out_values(C), o, case, plan.describe())
+            outs.append(C.view(torch.int16).cpu())
+        assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
 
 
 def test_zero_padding_invariant_on_gpu():

@@ -7,13 +7,14 @@ the library is not built, every call raises: there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
 
 import torch
 
-__all__ = ["Gemm", "gemm", "PlanInfo", "TlgError", "lib_path", "load_library", "status_name",
+__all__ = ["Gemm", "gemm", "select", "PlanInfo", "TlgError", "lib_path", "load_library", "status_name",
            "VARIANTS", "F16", "BF16", "F32"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -22,7 +23,7 @@ lib_path = os.path.join(_PKG, "libtlg.so")
 F16, BF16, F32 = 1, 2, 3
 _TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "tile256w8": 5,
-            "tile256dma": 6, "tile128dma": 7}
+            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8}
 EPILOGUES = {"none": 0, "relu": 1}
 
 STATUS = {0: "TLG_OK", -1: "TLG_ERR_INVALID_ARG", -2: "TLG_ERR_UNSUPPORTED", -3: "TLG_ERR_NULL",
@@ -43,10 +44,11 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("block_k", ctypes.c_int32), ("stages", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32), ("grid", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int64), ("k_tiles", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("lds_bytes", ctypes.c_int64), ("k_tiles", ctypes.c_int32), ("splits", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self):
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 _lib = None
@@ -73,6 +75,9 @@ def load_library():
         lib.tlg_gemm_run.restype = i32
         lib.tlg_gemm_destroy.argtypes = [vp]
         lib.tlg_gemm_destroy.restype = i32
+        lib.tlg_gemm_select.argtypes = [ctypes.POINTER(PlanInfo), i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                        i32]
+        lib.tlg_gemm_select.restype = i32
         lib.tlg_gemm_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         lib.tlg_gemm_query.restype = i32
         lib.tlg_gemm_describe.argtypes = [vp]
@@ -93,8 +98,25 @@ def _code(dt) -> int:
     return _TORCH_TO_CODE[dt]
 
 
+def select(M: int, N: int, K: int, ab_dtype=torch.float16, out_dtype=torch.float16, *,
+           transpose_A: bool = False, transpose_B: bool = False, clear_accum: bool = True,
+           epilogue: str = "none", variant: str = "auto") -> PlanInfo:
+    """The plan facts tlg_gemm_create would produce for these arguments (tlg_gemm_select:
+    host only, nothing is allocated)."""
+    lib = load_library()
+    info = PlanInfo()
+    st = lib.tlg_gemm_select(ctypes.byref(info), int(M), int(N), int(K), _code(ab_dtype), _code(out_dtype),
+                             int(bool(transpose_A)), int(bool(transpose_B)), int(bool(clear_accum)),
+                             EPILOGUES[epilogue], VARIANTS[variant])
+    if st != 0:
+        raise TlgError("tlg_gemm_select", st)
+    return info
+
+
 class Gemm:
-    """A plan for C[M,N] = act(A·B) (tlg_gemm_create).  Immutable; reusable on any stream."""
+    """A plan for C[M,N] = act(A·B) (tlg_gemm_create).  Immutable.  A plan without a
+    workspace is reusable on any stream; a split-K plan (info.splits > 1) owns a device
+    workspace on the device current at creation, and its runs must not overlap."""
 
     def __init__(self, M: int, N: int, K: int, ab_dtype=torch.float16, out_dtype=torch.float16, *,
                  transpose_A: bool = False, transpose_B: bool = False, clear_accum: bool = True,
@@ -151,8 +173,9 @@ class Gemm:
         if stream is None:
             stream = torch.cuda.current_stream(C.device)
         s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-        st = self._lib.tlg_gemm_run(self._h, A.data_ptr() or None, B.data_ptr() or None,
-                                    C.data_ptr() or None, ctypes.c_void_p(s))
+        with torch.cuda.device(C.device):
+            st = self._lib.tlg_gemm_run(self._h, A.data_ptr() or None, B.data_ptr() or None,
+                                        C.data_ptr() or None, ctypes.c_void_p(s))
         if st != 0:
             raise TlgError("tlg_gemm_run", st)
         return C
@@ -183,11 +206,13 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, *, tra
         if not clear_accum:
             raise ValueError("clear_accum=False needs C")
         C = torch.empty((M, N), dtype=out_dtype, device=A.device)
-    key = (M, N, K, A.dtype, C.dtype, bool(transpose_A), bool(transpose_B), bool(clear_accum), epilogue,
-           variant)
+    key = (A.device, M, N, K, A.dtype, C.dtype, bool(transpose_A), bool(transpose_B), bool(clear_accum),
+           epilogue, variant)
     plan = _plan_cache.get(key)
     if plan is None:
-        plan = Gemm(M, N, K, A.dtype, C.dtype, transpose_A=transpose_A, transpose_B=transpose_B,
-                    clear_accum=clear_accum, epilogue=epilogue, variant=variant)
+        # a split-K plan's workspace goes to the device current at creation: A's
+        with torch.cuda.device(A.device) if A.device.type == "cuda" else contextlib.nullcontext():
+            plan = Gemm(M, N, K, A.dtype, C.dtype, transpose_A=transpose_A, transpose_B=transpose_B,
+                        clear_accum=clear_accum, epilogue=epilogue, variant=variant)
         _plan_cache[key] = plan
     return plan.run(A, B, C)

@@ -271,7 +271,12 @@ struct LdsOperand {
     }
 };
 
-template <int BM, int BN, int S, int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC>
+// SK: split-K.  Workgroup b handles tile b / splits and K range b % splits; the
+// fp32 partial tiles are summed, in range order, by whichever workgroup of the
+// tile finishes last (a counter per tile elects it), so the result does not
+// depend on the order in which the workgroups finish.
+template <int BM, int BN, int S, int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC,
+          bool SK = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_lds_kernel(GemmParams p)
 {
@@ -301,11 +306,24 @@ gemm_lds_kernel(GemmParams p)
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
+    int tile_id = blockIdx.x, split = 0;
+    if constexpr (SK) {
+        split = blockIdx.x % p.splits;
+        tile_id = blockIdx.x / p.splits;
+    }
     int tm, tn;
-    tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
+    tile_coords(tile_id, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K;
-    const int TP = (K + BK - 1) / BK;                 // K tiles (the last one zero-padded)
+    const int TPALL = (K + BK - 1) / BK;              // K tiles (the last one zero-padded)
+    int kt0 = 0, TP = TPALL;                          // this workgroup's K tiles: kt0 .. kt0+TP-1
+    if constexpr (SK) {
+        const int per = (TPALL + p.splits - 1) / p.splits;
+        kt0 = split * per;
+        TP = min(per, TPALL - kt0);
+    }
+    // Loads stop at the end of the workgroup's K range (elements past it read as zeros).
+    const int KLIM = SK ? min(K, (kt0 + TP) * BK) : K;
 
     OpA opa;
     OpB opb;
@@ -324,7 +342,7 @@ gemm_lds_kernel(GemmParams p)
     };
     auto tile_res = [&](int t) {
         TileRes r;
-        r.k0 = t * BK;
+        r.k0 = (kt0 + t) * BK;
         r.ra = opa.rsrc(r.k0);
         r.rb = opb.rsrc(r.k0);
         r.slot = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t % S) * STAGE) + (uint32_t)wave * 1024u);
@@ -332,21 +350,21 @@ gemm_lds_kernel(GemmParams p)
     };
     auto issue_one = [&](const TileRes& r, int i) {
         if (i < LA)
-            dma16(r.ra, opa.voff(i, r.k0, K), r.slot + (uint32_t)(i * NW * 1024));
+            dma16(r.ra, opa.voff(i, r.k0, KLIM), r.slot + (uint32_t)(i * NW * 1024));
         else
-            dma16(r.rb, opb.voff(i - LA, r.k0, K), r.slot + (uint32_t)OpA::BYTES + (uint32_t)((i - LA) * NW * 1024));
+            dma16(r.rb, opb.voff(i - LA, r.k0, KLIM), r.slot + (uint32_t)OpA::BYTES + (uint32_t)((i - LA) * NW * 1024));
     };
 
     // Last K tile with K % 8 != 0: trim the elements past K that this lane's
     // loads brought into LDS (called after they landed, before the barrier that
     // publishes the tile).  The asm statements keep the compiler from moving LDS
     // accesses across the preceding wait.
-    const bool k_tail = (K & 7) != 0;
+    const bool k_tail = (K & 7) != 0 && kt0 + TP == TPALL;   // this range ends at K
     auto fix_k_tail = [&](int t) {
         asm volatile("" ::: "memory");
         char* region = smem + (t % S) * STAGE + wave * 1024;
-        opa.fix_k_tail(region, t * BK, K, lane);
-        opb.fix_k_tail(region + OpA::BYTES, t * BK, K, lane);
+        opa.fix_k_tail(region, (kt0 + t) * BK, K, lane);
+        opb.fix_k_tail(region + OpA::BYTES, (kt0 + t) * BK, K, lane);
         asm volatile("" ::: "memory");
     };
 
@@ -446,6 +464,65 @@ gemm_lds_kernel(GemmParams p)
     // No direct load may still be writing LDS when the workgroup ends.
     wait_vmcnt<0>();
 
+    if constexpr (SK) {
+        // Publish this range's fp32 partial tile, then take a ticket; the last
+        // workgroup of the tile sums the partials in range order and goes on to the
+        // epilogue, the others are done.  The XCDs have separate L2 caches, so the
+        // partials are written and read with device-scope (sc1) buffer accesses,
+        // which the hardware keeps coherent across XCDs (the same accesses the
+        // compiler emits for agent-scope atomic loads and stores).  Every wave waits
+        // for its partial stores to complete before the barrier that precedes the
+        // ticket, and the partials are read only after the ticket, so no cache
+        // write-back or invalidation is needed.
+        __shared__ unsigned ticket;
+        const __amdgpu_buffer_rsrc_t wsr =
+            make_rsrc(p.ws + (size_t)tile_id * p.splits * (BM * BN), (uint64_t)p.splits * BM * BN * 4u);
+        auto ws_off = [&](int s2, int i, int jj) {
+            const int ml = arow + i * 16 + (lane & 15), nl = bcol + jj * 16 + 4 * (lane >> 4);
+            return (uint32_t)((s2 * (BM * BN) + ml * BN + nl) * 4);
+        };
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][jj]), wsr,
+                                                       ws_off(split, i, jj), 0, kCoherentDevice);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            ticket = __hip_atomic_fetch_add(p.counters + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (ticket != (unsigned)(p.splits - 1)) return;
+        // acc = partial 0 + partial 1 + ... in range order (this workgroup's own
+        // partial is read back from the workspace too, which keeps the code free of
+        // branches).  The loads of up to four ranges are in flight together (ranges
+        // past the last one read zeros: their offsets lie beyond the resource).
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int G = 4;
+        for (int s0 = 0; s0 < p.splits; s0 += G) {
+            u32x4 part[G][FM][FN];
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < FN; ++jj)
+                        part[g][i][jj] = __builtin_amdgcn_raw_buffer_load_b128(
+                            wsr, s0 + g < p.splits ? ws_off(s0 + g, i, jj) : kOOB, 0, kCoherentDevice);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < FN; ++jj) acc[i][jj] += __builtin_bit_cast(f32x4, part[g][i][jj]);
+        }
+        if (threadIdx.x == 0)   // ready for the next launch
+            __hip_atomic_store(p.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     // Epilogue.  acc[i][j][e] is C[m][n + e] with
     //   m = m0 + wm*WTM + i*16 + lane%16,  n = n0 + wn*WTN + j*16 + 4*(lane/16).
     const bool vec_cols = p.c_vec != 0;
@@ -476,25 +553,25 @@ gemm_lds_kernel(GemmParams p)
     }
 }
 
-template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC>
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC, bool SK>
 inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * (SK ? p.splits : 1)));
     const dim3 block(64 * WM * WN);
-    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC>, grid, block,
-                           kargs, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC, SK>, grid,
+                           block, kargs, 0, stream);
 }
 
 // K-contiguous A <=> transpose_A == 0; K-contiguous B <=> transpose_B == 1.
-template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T>
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool SK = false>
 inline hipError_t dispatch_lds_layout(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    if (!tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, true>(p, s);
-    if (!tA && !tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, false>(p, s);
-    if (tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, true>(p, s);
-    return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, false>(p, s);
+    if (!tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, true, SK>(p, s);
+    if (!tA && !tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, false, SK>(p, s);
+    if (tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, true, SK>(p, s);
+    return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, false, SK>(p, s);
 }
 
 // 256 x 256 tiles: 8 waves of 128 x 64, 2-slot ring, barrier after 8 of the last
@@ -511,6 +588,13 @@ template <int T>
 inline hipError_t dispatch_lds128(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
     return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T>(p, tA, tB, s);
+}
+
+// The same 128 x 128 kernel with K split over p.splits workgroups per tile.
+template <int T>
+inline hipError_t dispatch_lds128_sk(const GemmParams& p, int tA, int tB, hipStream_t s)
+{
+    return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T, true>(p, tA, tB, s);
 }
 
 }  // namespace tlg

@@ -7,6 +7,7 @@
 // silently.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -23,8 +24,18 @@ struct tlg_gemm_s {
     int variant;
     int vec_a, vec_b;
     int align_a, align_b;  // byte alignment run() requires of A and B
+    // split-K plans: workspace = [tiles][splits][128*128] fp32 partials, then one
+    // counter per tile (zero between launches); allocated on `device` at create
+    int splits = 1;
+    void* ws = nullptr;
+    size_t ws_partials_bytes = 0, ws_bytes = 0;
+    int device = -1;
     tlg_plan_info info;
     char desc[256];
+    ~tlg_gemm_s()
+    {
+        if (ws) (void)hipFree(ws);
+    }
 };
 
 namespace {
@@ -54,6 +65,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_TILE_256_W8: return "tile256w8";
     case TLG_VARIANT_TILE_256_DMA: return "tile256dma";
     case TLG_VARIANT_TILE_128_DMA: return "tile128dma";
+    case TLG_VARIANT_TILE_128_DMA_SPLITK: return "tile128dma_sk";
     default: return "?";
     }
 }
@@ -70,6 +82,19 @@ int vec_for(int64_t contiguous_len) { return contiguous_len % 8 == 0 ? 8 : 1; }
 
 bool flag_ok(int v) { return v == 0 || v == 1; }
 
+constexpr int64_t kSplitMinKTiles = 48;
+
+// Split-K factor for `tiles` 128x128 output tiles and `ktiles` 64-wide K tiles:
+// about 256 workgroups (one per CU), at most 8 ranges, at least 2 K tiles per
+// range, and no empty last range.
+int choose_splits(int64_t tiles, int64_t ktiles)
+{
+    int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 256 / std::max<int64_t>(tiles, 1)));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, ktiles / 2));
+    while (s > 1 && (s - 1) * ((ktiles + s - 1) / s) >= ktiles) --s;
+    return (int)s;
+}
+
 bool is_tile(int v)
 {
     return v == TLG_VARIANT_TILE_256 || v == TLG_VARIANT_TILE_128 || v == TLG_VARIANT_TILE_256_W8;
@@ -82,18 +107,18 @@ int tile_config(int v)
     return TILE_128;
 }
 
-tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB,
-                       int clear, int epi, int forced)
+// Validation, variant choice and launch geometry: everything a plan holds except
+// its device workspace.  Host only.
+tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB, int clear,
+                      int epi, int forced)
 {
-    if (!out) return TLG_ERR_NULL;
-    *out = nullptr;
     if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
     if (!flag_ok(tA) || !flag_ok(tB) || !flag_ok(clear)) return TLG_ERR_INVALID_ARG;
     if (epi != TLG_EPI_NONE && epi != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
     if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA_SPLITK || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
 
     const int va = vec_for(tA ? M : K);
@@ -111,32 +136,45 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         if (forced == TLG_VARIANT_SKINNY && !skinny_ok) return TLG_ERR_UNSUPPORTED;
         if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
             return TLG_ERR_UNSUPPORTED;
-        if ((forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA) && !dma_ok)
+        if ((forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA ||
+             forced == TLG_VARIANT_TILE_128_DMA_SPLITK) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
         variant = TLG_VARIANT_SKINNY;
     } else if (dma_ok) {
-        // 256x256 tiles once they fill every CU, else 128x128 tiles (4x the workgroups).
-        variant = ceil_div(M, 256) * ceil_div(N, 256) >= 256 ? TLG_VARIANT_TILE_256_DMA : TLG_VARIANT_TILE_128_DMA;
+        // 256x256 tiles once they fill every CU, else 128x128 tiles (4x the workgroups);
+        // fewer than 128 of those with a long K: split K as well.  The exchange of
+        // partial tiles costs ~5-10 us per launch (measured on MI355X), which a
+        // split repays only from about 48 K tiles (K >= 3072) on.
+        const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), kt = ceil_div(K, 64);
+        if (ceil_div(M, 256) * ceil_div(N, 256) >= 256)
+            variant = TLG_VARIANT_TILE_256_DMA;
+        else if (t128 < 128 && kt >= kSplitMinKTiles && choose_splits(t128, kt) >= 2)
+            variant = TLG_VARIANT_TILE_128_DMA_SPLITK;
+        else
+            variant = TLG_VARIANT_TILE_128_DMA;
     } else {
         variant = TLG_VARIANT_TILE_128;
     }
 
     // Launch-grid limits: the tile kernels use a 1-D grid of tile ids (int), the
     // skinny kernel a 2-D grid with row blocks in y.
-    if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA) {
-        const int64_t b = (variant == TLG_VARIANT_TILE_128 || variant == TLG_VARIANT_TILE_128_DMA) ? 128 : 256;
-        if (ceil_div(M, b) * ceil_div(N, b) > INT32_MAX) return TLG_ERR_INVALID_ARG;
+    int splits = 1;
+    if (variant == TLG_VARIANT_TILE_128_DMA_SPLITK) splits = choose_splits(ceil_div(M, 128) * ceil_div(N, 128), ceil_div(K, 64));
+    if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
+        variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
+        const int64_t b = (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_256_W8 ||
+                           variant == TLG_VARIANT_TILE_256_DMA) ? 256 : 128;
+        if (ceil_div(M, b) * ceil_div(N, b) * splits > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
         if (ceil_div(M, kSkinnyRows) > 65535 || ceil_div(N, kSkinnyNB) > INT32_MAX) return TLG_ERR_INVALID_ARG;
     }
 
-    tlg_gemm_s* p = new (std::nothrow) tlg_gemm_s();
-    if (!p) return TLG_ERR_NOMEM;
     p->M = M; p->N = N; p->K = K;
     p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
     p->variant = variant;
-    const bool dma = variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA;
+    const bool dma = variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
+                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK;
     p->vec_a = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : va;
     p->vec_b = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : vb;
     if (dma) {
@@ -166,13 +204,19 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         in.grid = ceil_div(M, kLdsBM) * ceil_div(N, kLdsBN);
         in.lds_bytes = (int64_t)kLdsStages * (kLdsBM + kLdsBN) * kLdsBK * 2;
         in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
-    } else if (variant == TLG_VARIANT_TILE_128_DMA) {
+    } else if (variant == TLG_VARIANT_TILE_128_DMA || variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
+        const int64_t tiles = ceil_div(M, kLds128BM) * ceil_div(N, kLds128BN);
         in.block_m = kLds128BM; in.block_n = kLds128BN; in.block_k = kLdsBK;
         in.stages = kLds128Stages;
         in.threads = kLdsThreads;
-        in.grid = ceil_div(M, kLds128BM) * ceil_div(N, kLds128BN);
+        in.grid = tiles * splits;
         in.lds_bytes = (int64_t)kLds128Stages * (kLds128BM + kLds128BN) * kLdsBK * 2;
-        in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
+        in.k_tiles = (int32_t)ceil_div(ceil_div(K, kLdsBK), splits);
+        if (variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
+            p->splits = splits;
+            p->ws_partials_bytes = (size_t)tiles * splits * kLds128BM * kLds128BN * sizeof(float);
+            p->ws_bytes = p->ws_partials_bytes + (size_t)((tiles * sizeof(unsigned) + 255) / 256 * 256);
+        }
     } else if (variant == TLG_VARIANT_SKINNY) {
         in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
         in.stages = kSkinnyStages;
@@ -181,12 +225,43 @@ tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab,
         in.lds_bytes = (int64_t)kSkinnyStages * (kSkinnyNB + kSkinnyRows) * kSkinnyKST * 2;
         in.k_tiles = (int32_t)ceil_div(K, kSkinnyKST);
     }
+    in.splits = p->splits;
+    in.workspace_bytes = (int64_t)p->ws_bytes;
     std::snprintf(p->desc, sizeof(p->desc),
                   "%s M=%lld N=%lld K=%lld ab=%s c=%s tA=%d tB=%d clear=%d relu=%d block=%dx%dx%d "
-                  "stages=%d threads=%d grid=%lld lds=%lld vec=%d/%d",
+                  "stages=%d threads=%d grid=%lld lds=%lld vec=%d/%d splits=%d",
                   variant_name(variant), (long long)M, (long long)N, (long long)K, dt_name(ab), dt_name(c), tA,
                   tB, clear, p->relu, in.block_m, in.block_n, in.block_k, in.stages, in.threads,
-                  (long long)in.grid, (long long)in.lds_bytes, in.vec_a, in.vec_b);
+                  (long long)in.grid, (long long)in.lds_bytes, in.vec_a, in.vec_b, in.splits);
+    return TLG_OK;
+}
+
+tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB,
+                       int clear, int epi, int forced)
+{
+    if (!out) return TLG_ERR_NULL;
+    *out = nullptr;
+    tlg_gemm_s* p = new (std::nothrow) tlg_gemm_s();
+    if (!p) return TLG_ERR_NOMEM;
+    const tlg_status st = plan_build(p, M, N, K, ab, c, tA, tB, clear, epi, forced);
+    if (st != TLG_OK) {
+        delete p;
+        return st;
+    }
+    if (p->ws_bytes) {
+        // Split-K workspace on the current device; the per-tile counters start at
+        // zero (the kernel returns each one to zero after use).
+        if (hipGetDevice(&p->device) != hipSuccess || hipMalloc(&p->ws, p->ws_bytes) != hipSuccess) {
+            p->ws = nullptr;
+            delete p;
+            return TLG_ERR_HIP;
+        }
+        if (hipMemset((char*)p->ws + p->ws_partials_bytes, 0, p->ws_bytes - p->ws_partials_bytes) != hipSuccess ||
+            hipStreamSynchronize(nullptr) != hipSuccess) {
+            delete p;
+            return TLG_ERR_HIP;
+        }
+    }
     *out = p;
     return TLG_OK;
 }
@@ -216,6 +291,18 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t* out, int64_t M, int64_t N, int64_
                        variant);
 }
 
+tlg_status tlg_gemm_select(tlg_plan_info* info, int64_t M, int64_t N, int64_t K, int32_t ab_dtype,
+                           int32_t c_dtype, int32_t transpose_A, int32_t transpose_B, int32_t clear_accum,
+                           int32_t epilogue, int32_t variant)
+{
+    if (!info) return TLG_ERR_NULL;
+    tlg_gemm_s p;
+    const tlg_status st =
+        plan_build(&p, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue, variant);
+    if (st == TLG_OK) *info = p.info;
+    return st;
+}
+
 tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, void* stream)
 {
     if (!plan) return TLG_ERR_NULL;
@@ -235,6 +322,12 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
     const uint64_t c_bytes = (uint64_t)p.M * (uint64_t)p.N * (uint64_t)cb;
     if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, b, b_bytes))
         return TLG_ERR_INVALID_ARG;
+
+    if (p.ws) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return TLG_ERR_HIP;
+        if (dev != p.device) return TLG_ERR_INVALID_ARG;   // the workspace lives on the plan's device
+    }
 
     GemmParams gp{};
     gp.A = A; gp.B = B; gp.C = C;
@@ -259,6 +352,14 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
         err = p.ab == TLG_F16 ? launch_lds128_f16(gp, p.tA, p.tB, (hipStream_t)stream)
                               : launch_lds128_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
+    } else if (p.variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
+        gp.tiles_m = (int)ceil_div(p.M, kLds128BM);
+        gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
+        gp.splits = p.splits;
+        gp.ws = (float*)p.ws;
+        gp.counters = (unsigned*)((char*)p.ws + p.ws_partials_bytes);
+        err = p.ab == TLG_F16 ? launch_lds128sk_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                              : launch_lds128sk_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else {
         const int cfg = tile_config(p.variant);
         const TileShape ts = tile_shape(cfg);

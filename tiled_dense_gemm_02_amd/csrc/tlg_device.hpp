@@ -29,6 +29,9 @@ constexpr uint32_t kOOB = 0x80000000u;
 constexpr uint32_t kMaxRecords = 0x7fffffffu;
 // Word 3 of a gfx9 buffer descriptor: DATA_FORMAT = 32-bit, everything else 0.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy operand of the buffer builtins: sc1, device scope (coherent
+// across the XCDs' separate L2 caches).
+constexpr int kCoherentDevice = 16;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes_left)
 {

@@ -21,6 +21,12 @@ struct GemmParams {
     int c_vec;        // 1: N % 4 == 0 and C aligned to 4 elements (vector stores allowed)
     int tiles_m;      // output tiles along M (tile kernels) / row blocks (skinny)
     int tiles_n;      // output tiles along N
+    // split-K plans only: K is cut into `splits` ranges of whole K tiles, one
+    // workgroup per (tile, range); fp32 partial tiles go to ws ([tile][split][BM*BN])
+    // and counters[tile] (zero between launches) elects the workgroup that sums them.
+    int splits;
+    float* ws;
+    unsigned* counters;
 };
 
 // Block-tile configurations of the tiled kernel.
@@ -87,5 +93,7 @@ hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B,
 hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds128sk_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds128sk_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 
 }  // namespace tlg
