@@ -15,7 +15,9 @@ rotated so that the inputs of consecutive launches are not the same buffers
 
 Timing: W untimed launches, then exactly K launches between a barrier +
 device synchronisation on both sides, bracketed by HIP events recorded on the
-stream the kernels run on.  Rank 0 prints one JSON line.
+stream the kernels run on.  Rank 0 prints one JSON line.  The secondary
+workloads warm up for at least 100 ms of launches besides (their kernels are
+short, and the clock settles only after tens of milliseconds of load).
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ KERNEL_SOURCES = {
     3: ["gemm_skinny.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     6: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     7: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
+    8: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
 }
 
 
@@ -78,8 +81,12 @@ def parse():
     return ap.parse_args()
 
 
-def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None):
-    """Time `steps` launches of `case`.  Returns a dict with the timing and the plan."""
+def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=0.0):
+    """Time `steps` launches of `case` after `warmup` untimed ones (and, with
+    min_warm_ms > 0, after as many more as make up that much GPU time: the clock
+    and power management settle only after tens of milliseconds of load, which a
+    fixed count of a short kernel does not reach).  Returns a dict with the timing
+    and the plan."""
     import torch
     import tiled_dense_gemm_02_amd as tlg
     import tlg_workloads as W
@@ -106,6 +113,18 @@ def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None):
     for i in range(warmup):
         status |= plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh)
     torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for i in range(20):
+            status |= plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        per = max(w0.elapsed_time(w1) / 20, 1e-3)
+        for i in range(int(math.ceil(max(0.0, min_warm_ms - 20 * per) / per))):
+            status |= plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh)
+        torch.cuda.synchronize()
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
     start = torch.cuda.Event(enable_timing=True)
@@ -210,7 +229,7 @@ def main():
             if name == args.workload:
                 continue
             c2 = W.CONFIGS[name]
-            rr = measure(c2, max(10, args.steps // 2), 40, log=log)
+            rr = measure(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
             t = rr["ms"] * 1e-3
             entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
                      "GB/s": c2.algorithmic_bytes / t / 1e9, "plan": rr["plan"].describe()}
