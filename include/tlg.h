@@ -159,6 +159,43 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  */
 tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, void *stream);
 
+/* One timed candidate of tlg_gemm_tune. */
+typedef struct {
+    int32_t variant;   /* tlg_variant */
+    int32_t splits;    /* K ranges per output tile (split-K variant), else 1 */
+    float ms;          /* average time of one run, milliseconds */
+} tlg_tune_result;
+
+/*
+ * Autotune (the pages' autotuner: overview page, "autotuning" section): make a
+ * plan for the same request as tlg_gemm_create, choosing the kernel variant,
+ * and for the split-K variant the number of K ranges, by timing every
+ * candidate that can serve the request on the caller's buffers.  Candidates:
+ * every variant of tlg_variant but EMPTY, and the split-K variant with 2..8
+ * ranges when the output has fewer than 256 tiles of 128 x 128.  A candidate
+ * that refuses the request (TLG_ERR_UNSUPPORTED) or the buffers' alignment
+ * (TLG_ERR_MISALIGNED) is skipped.
+ *   A, B, C, stream : as for tlg_gemm_run.  C is overwritten, and with
+ *                     clear_accum == 0 its prior contents are lost (the runs
+ *                     accumulate into it).
+ *   iters           : timed runs per candidate, 1..1000, after one untimed run.
+ *   results         : receives up to max_results entries (may be NULL when
+ *                     max_results == 0), one per candidate timed, in the order
+ *                     timed; *n_results (may be NULL) gets the number written.
+ * The choice is cached per (current device, M, N, K, dtypes, flags, epilogue)
+ * for the life of the process: a later call with the same key times nothing
+ * (*n_results = 0) and returns a new plan of the cached choice.  The choice
+ * depends on timings and so may differ between processes.  Synchronises the
+ * stream.  Returns the errors of tlg_gemm_create and tlg_gemm_run,
+ * TLG_ERR_INVALID_ARG for iters or max_results out of range, TLG_ERR_HIP if
+ * timing fails.  On failure *out is set to NULL.
+ */
+tlg_status tlg_gemm_tune(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
+                         int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
+                         int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
+                         const void *A, const void *B, void *C, void *stream, int32_t iters,
+                         tlg_tune_result *results, int32_t max_results, int32_t *n_results);
+
 /* Release a plan (and its workspace, if any; the caller first makes sure no run of
  * the plan is still in flight).  NULL is accepted (no-op, TLG_OK). */
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan);

@@ -191,3 +191,29 @@ def test_python_binding_checks_shapes_and_devices():
               torch.zeros(8, 8, dtype=torch.float16))       # host tensors are refused
     with pytest.raises(tlg.TlgError):
         tlg.Gemm(-1, 8, 8)
+
+
+def test_tune_validates_before_touching_a_device():
+    lib = tlg.load_library()
+    h = ctypes.c_void_p()
+    res = (tlg.TuneResult * 4)()
+    n = ctypes.c_int32(-1)
+    args = (64, 64, 64, 1, 1, 0, 0, 1, 0)
+    assert lib.tlg_gemm_tune(None, *args, 4096, 8192, 16384, None, 5, res, 4, ctypes.byref(n)) == NULL
+    assert lib.tlg_gemm_tune(ctypes.byref(h), *args, 4096, 8192, 16384, None, 0, res, 4, ctypes.byref(n)) == INVALID
+    assert lib.tlg_gemm_tune(ctypes.byref(h), *args, 4096, 8192, 16384, None, 1001, res, 4, None) == INVALID
+    assert lib.tlg_gemm_tune(ctypes.byref(h), *args, 4096, 8192, 16384, None, 5, None, 4, None) == NULL
+    assert lib.tlg_gemm_tune(ctypes.byref(h), -1, 64, 64, 1, 1, 0, 0, 1, 0, 4096, 8192, 16384, None, 5, res, 4,
+                             ctypes.byref(n)) == INVALID
+    assert lib.tlg_gemm_tune(ctypes.byref(h), 64, 64, 64, 3, 1, 0, 0, 1, 0, 4096, 8192, 16384, None, 5, res, 4,
+                             None) == UNSUPPORTED
+    assert lib.tlg_gemm_tune(ctypes.byref(h), *args, None, 8192, 16384, None, 5, res, 4, ctypes.byref(n)) == NULL
+    assert lib.tlg_gemm_tune(ctypes.byref(h), *args, 4096, 8192, None, None, 5, res, 4, ctypes.byref(n)) == NULL
+    assert not h.value and n.value == 0
+    # an empty output needs no timing (and no device)
+    assert lib.tlg_gemm_tune(ctypes.byref(h), 0, 64, 64, 1, 1, 0, 0, 1, 0, None, None, None, None, 5, res, 4,
+                             ctypes.byref(n)) == OK
+    assert h.value and n.value == 0
+    info = tlg.PlanInfo()
+    assert lib.tlg_gemm_query(h, ctypes.byref(info)) == OK and info.variant == 4
+    assert lib.tlg_gemm_destroy(h) == OK

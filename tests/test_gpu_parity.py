@@ -227,6 +227,43 @@ def test_split_k_plan_reused():
         assert torch.equal(outs[0], outs[2]) and torch.equal(outs[1], outs[3])
 
 
+@pytest.mark.parametrize("shape", [("c2", None), ("c4", None), ("longk", (1024, 1024, 8192))])
+def test_autotuned_plan(shape):
+    """tlg_gemm_tune: every candidate timed once, the fastest kept (its entry is the
+    minimum of the report), its result within the tolerance, the choice cached."""
+    import tiled_dense_gemm_02_amd as tlg
+    name, mnk = shape
+    case = W.CONFIGS[name] if mnk is None else W.CONFIGS["c2"].with_(name=name, M=mnk[0], N=mnk[1], K=mnk[2])
+    A, B, _ = W.make_inputs(case)
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    C = torch.empty((case.M, case.N), dtype=dt[case.c], device="cuda")
+    Ad, Bd = A.cuda(), B.cuda()
+    kw = dict(transpose_A=bool(case.transpose_A), transpose_B=bool(case.transpose_B),
+              epilogue="relu" if case.relu else "none")
+    plan, report = tlg.tune(Ad, Bd, C, iters=3, **kw)
+    log(f"[case] tune {case.name}: chose {plan.describe()}")
+    for v, sp, ms in report:
+        log(f"    {v:14s} splits {sp}: {ms * 1e3:8.1f} us")
+    assert len(report) >= 3
+    best = min(report, key=lambda r: r[2])
+    assert (tlg.VARIANTS[best[0]], best[1]) == (plan.info.variant, plan.info.splits)
+    if case.M * case.N <= 1 << 21:
+        o = oracle_full(case, A, B, None)
+        C.fill_(0)
+        plan.run(Ad, Bd, C)
+        torch.cuda.synchronize()
+        assert_within_tolerance(out_values(C), o, case, plan.describe())
+    else:
+        ms_, ns_ = W.sample_points(case.M, case.N, 2048)
+        o = oracle_points(case, A, B, None, ms_, ns_)
+        C.fill_(0)
+        plan.run(Ad, Bd, C)
+        torch.cuda.synchronize()
+        assert_within_tolerance(out_values(C)[ms_, ns_], o, case, plan.describe())
+    plan2, report2 = tlg.tune(Ad, Bd, C, iters=3, **kw)
+    assert report2 == [] and plan2.info.as_dict() == plan.info.as_dict()
+
+
 def test_zero_padding_invariant_on_gpu():
     """The ragged-K workload equals the same GEMM with K zero-padded to 832 = 13 * 64."""
     case = W.CONFIGS["c4"]

@@ -14,8 +14,8 @@ import threading
 
 import torch
 
-__all__ = ["Gemm", "gemm", "select", "PlanInfo", "TlgError", "lib_path", "load_library", "status_name",
-           "VARIANTS", "F16", "BF16", "F32"]
+__all__ = ["Gemm", "gemm", "select", "tune", "PlanInfo", "TuneResult", "TlgError", "lib_path", "load_library",
+           "status_name", "VARIANTS", "F16", "BF16", "F32"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtlg.so")
@@ -51,6 +51,10 @@ class PlanInfo(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class TuneResult(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("splits", ctypes.c_int32), ("ms", ctypes.c_float)]
+
+
 _lib = None
 _lib_lock = threading.Lock()
 
@@ -78,6 +82,9 @@ def load_library():
         lib.tlg_gemm_select.argtypes = [ctypes.POINTER(PlanInfo), i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                         i32]
         lib.tlg_gemm_select.restype = i32
+        lib.tlg_gemm_tune.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp,
+                                      vp, i32, ctypes.POINTER(TuneResult), i32, ctypes.POINTER(i32)]
+        lib.tlg_gemm_tune.restype = i32
         lib.tlg_gemm_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         lib.tlg_gemm_query.restype = i32
         lib.tlg_gemm_describe.argtypes = [vp]
@@ -120,13 +127,17 @@ class Gemm:
 
     def __init__(self, M: int, N: int, K: int, ab_dtype=torch.float16, out_dtype=torch.float16, *,
                  transpose_A: bool = False, transpose_B: bool = False, clear_accum: bool = True,
-                 epilogue: str = "none", variant: str = "auto"):
+                 epilogue: str = "none", variant: str = "auto", _handle=None):
         lib = load_library()
         self.M, self.N, self.K = int(M), int(N), int(K)
         self.ab_code, self.c_code = _code(ab_dtype), _code(out_dtype)
         self.transpose_A, self.transpose_B = bool(transpose_A), bool(transpose_B)
         self.clear_accum = bool(clear_accum)
         self.epilogue = epilogue
+        self._lib = lib
+        if _handle is not None:          # a plan made by tlg_gemm_tune
+            self._h = _handle
+            return
         self._h = ctypes.c_void_p()
         args = (self.M, self.N, self.K, self.ab_code, self.c_code, int(self.transpose_A),
                 int(self.transpose_B), int(self.clear_accum), EPILOGUES[epilogue])
@@ -190,6 +201,42 @@ class Gemm:
         if h:
             self._lib.tlg_gemm_destroy(h)
             self._h = None
+
+
+def tune(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, transpose_A: bool = False,
+         transpose_B: bool = False, clear_accum: bool = True, epilogue: str = "none", iters: int = 10,
+         stream=None):
+    """Autotuned plan for C = act(A·B) on these device tensors (tlg_gemm_tune): every
+    candidate kernel is timed on them (C is overwritten) and the fastest kept; the
+    choice is cached per device and problem.  Returns (Gemm, [(variant name, splits,
+    ms), ...]) with one entry per candidate timed (empty when the cache answered)."""
+    lib = load_library()
+    M = A.shape[1] if transpose_A else A.shape[0]
+    K = A.shape[0] if transpose_A else A.shape[1]
+    N = B.shape[0] if transpose_B else B.shape[1]
+    probe = Gemm.__new__(Gemm)
+    probe.M, probe.N, probe.K = M, N, K
+    probe.ab_code, probe.c_code = _code(A.dtype), _code(C.dtype)
+    probe.transpose_A, probe.transpose_B = bool(transpose_A), bool(transpose_B)
+    probe._h = None
+    probe._check(A, B, C)
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    res = (TuneResult * 32)()
+    n = ctypes.c_int32(0)
+    h = ctypes.c_void_p()
+    with torch.cuda.device(C.device):
+        st = lib.tlg_gemm_tune(ctypes.byref(h), M, N, K, _code(A.dtype), _code(C.dtype), int(bool(transpose_A)),
+                               int(bool(transpose_B)), int(bool(clear_accum)), EPILOGUES[epilogue],
+                               A.data_ptr() or None, B.data_ptr() or None, C.data_ptr() or None,
+                               ctypes.c_void_p(s), int(iters), res, 32, ctypes.byref(n))
+    if st != 0:
+        raise TlgError("tlg_gemm_tune", st)
+    names = {v: k for k, v in VARIANTS.items()}
+    plan = Gemm(M, N, K, A.dtype, C.dtype, transpose_A=transpose_A, transpose_B=transpose_B,
+                clear_accum=clear_accum, epilogue=epilogue, _handle=h)
+    return plan, [(names.get(r.variant, str(r.variant)), r.splits, r.ms) for r in res[:n.value]]
 
 
 _plan_cache: dict = {}

@@ -11,7 +11,11 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <map>
+#include <mutex>
 #include <new>
+#include <tuple>
+#include <vector>
 
 #include "../../include/tlg.h"
 #include "tlg_internal.h"
@@ -83,6 +87,7 @@ int vec_for(int64_t contiguous_len) { return contiguous_len % 8 == 0 ? 8 : 1; }
 bool flag_ok(int v) { return v == 0 || v == 1; }
 
 constexpr int64_t kSplitMinKTiles = 48;
+constexpr int kMaxSplits = 8;
 
 // Split-K factor for `tiles` 128x128 output tiles and `ktiles` 64-wide K tiles:
 // about 256 workgroups (one per CU), at most 8 ranges, at least 2 K tiles per
@@ -110,7 +115,7 @@ int tile_config(int v)
 // Validation, variant choice and launch geometry: everything a plan holds except
 // its device workspace.  Host only.
 tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB, int clear,
-                      int epi, int forced)
+                      int epi, int forced, int forced_splits = 0)
 {
     if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
     if (!flag_ok(tA) || !flag_ok(tB) || !flag_ok(clear)) return TLG_ERR_INVALID_ARG;
@@ -160,7 +165,17 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     // Launch-grid limits: the tile kernels use a 1-D grid of tile ids (int), the
     // skinny kernel a 2-D grid with row blocks in y.
     int splits = 1;
-    if (variant == TLG_VARIANT_TILE_128_DMA_SPLITK) splits = choose_splits(ceil_div(M, 128) * ceil_div(N, 128), ceil_div(K, 64));
+    if (variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
+        const int64_t kt = ceil_div(K, 64);
+        if (forced_splits > 0) {
+            // a split count asked for by the tuner: whole K tiles per range, none empty
+            if (forced_splits > kMaxSplits || (forced_splits - 1) * ceil_div(kt, forced_splits) >= kt)
+                return TLG_ERR_UNSUPPORTED;
+            splits = forced_splits;
+        } else {
+            splits = choose_splits(ceil_div(M, 128) * ceil_div(N, 128), kt);
+        }
+    }
     if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
         variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
         const int64_t b = (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_256_W8 ||
@@ -237,13 +252,13 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
 }
 
 tlg_status plan_create(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int ab, int c, int tA, int tB,
-                       int clear, int epi, int forced)
+                       int clear, int epi, int forced, int forced_splits = 0)
 {
     if (!out) return TLG_ERR_NULL;
     *out = nullptr;
     tlg_gemm_s* p = new (std::nothrow) tlg_gemm_s();
     if (!p) return TLG_ERR_NOMEM;
-    const tlg_status st = plan_build(p, M, N, K, ab, c, tA, tB, clear, epi, forced);
+    const tlg_status st = plan_build(p, M, N, K, ab, c, tA, tB, clear, epi, forced, forced_splits);
     if (st != TLG_OK) {
         delete p;
         return st;
@@ -400,5 +415,140 @@ const char* tlg_status_string(int32_t status)
 }
 
 const char* tlg_version(void) { return "tlg 0.1.0 (gfx950)"; }
+
+// Autotuning, after the pages' autotuner (overview page, "autotuning" section):
+// a search space of kernel configurations pruned by what each can serve, every
+// candidate run on the same real inputs, warmed up, timed over repeated runs,
+// and the best configuration kept in a cache keyed by device and problem.
+namespace {
+
+struct TuneKey {
+    int dev;
+    int64_t M, N, K;
+    int ab, c, tA, tB, clear, epi;
+    bool operator<(const TuneKey& o) const
+    {
+        return std::tie(dev, M, N, K, ab, c, tA, tB, clear, epi) <
+               std::tie(o.dev, o.M, o.N, o.K, o.ab, o.c, o.tA, o.tB, o.clear, o.epi);
+    }
+};
+
+std::mutex g_tune_mu;
+std::map<TuneKey, std::pair<int, int>> g_tune_cache;   // -> (variant, forced splits)
+
+struct TuneCandidate {
+    int variant, splits;   // splits: 0 = the plan's own choice
+};
+
+// The search space for a request: every kernel family, and for output grids that
+// leave CUs idle (fewer than 256 tiles of 128 x 128) the split-K kernel with each
+// split count from 2 to kMaxSplits.  Candidates that cannot serve the request are
+// dropped when their plan is refused.
+std::vector<TuneCandidate> tune_space(int64_t M, int64_t N)
+{
+    std::vector<TuneCandidate> c = {{TLG_VARIANT_TILE_256_DMA, 0}, {TLG_VARIANT_TILE_128_DMA, 0},
+                                    {TLG_VARIANT_SKINNY, 0},       {TLG_VARIANT_TILE_256_W8, 0},
+                                    {TLG_VARIANT_TILE_256, 0},     {TLG_VARIANT_TILE_128, 0}};
+    if (ceil_div(M, 128) * ceil_div(N, 128) < 256)
+        for (int s = 2; s <= kMaxSplits; ++s) c.push_back({TLG_VARIANT_TILE_128_DMA_SPLITK, s});
+    return c;
+}
+
+}  // namespace
+
+tlg_status tlg_gemm_tune(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                         int32_t transpose_A, int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
+                         const void* A, const void* B, void* C, void* stream, int32_t iters,
+                         tlg_tune_result* results, int32_t max_results, int32_t* n_results)
+{
+    if (!out) return TLG_ERR_NULL;
+    *out = nullptr;
+    if (n_results) *n_results = 0;
+    if (iters < 1 || iters > 1000 || max_results < 0) return TLG_ERR_INVALID_ARG;
+    if (max_results > 0 && !results) return TLG_ERR_NULL;
+    // The request itself must be valid (the automatic plan's checks).
+    tlg_gemm_s probe;
+    tlg_status st = plan_build(&probe, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                               TLG_VARIANT_AUTO);
+    if (st != TLG_OK) return st;
+    if (probe.variant == TLG_VARIANT_EMPTY)
+        return plan_create(out, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                           TLG_VARIANT_AUTO);
+    if (!C || (K > 0 && (!A || !B))) return TLG_ERR_NULL;
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERR_HIP;
+    const TuneKey key{dev, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue};
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        auto it = g_tune_cache.find(key);
+        if (it != g_tune_cache.end())
+            return plan_create(out, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                               it->second.first, it->second.second);
+    }
+
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return TLG_ERR_HIP;
+    }
+    tlg_gemm_t best = nullptr;
+    TuneCandidate best_c{0, 0};
+    float best_ms = 0.f;
+    int32_t count = 0;
+    st = TLG_OK;
+    for (const TuneCandidate& cand : tune_space(M, N)) {
+        tlg_gemm_t pl = nullptr;
+        const tlg_status cs = plan_create(&pl, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum,
+                                          epilogue, cand.variant, cand.splits);
+        if (cs == TLG_ERR_UNSUPPORTED) continue;
+        if (cs != TLG_OK) {
+            st = cs;
+            break;
+        }
+        // one untimed run (also checks the buffers for this plan), then `iters` timed
+        st = tlg_gemm_run(pl, A, B, C, stream);
+        if (st == TLG_ERR_MISALIGNED) {   // this candidate needs an alignment the buffers lack
+            tlg_gemm_destroy(pl);
+            st = TLG_OK;
+            continue;
+        }
+        if (st == TLG_OK && hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) st = TLG_ERR_HIP;
+        for (int i = 0; i < iters && st == TLG_OK; ++i) st = tlg_gemm_run(pl, A, B, C, stream);
+        float ms = 0.f;
+        if (st == TLG_OK && (hipEventRecord(e1, (hipStream_t)stream) != hipSuccess ||
+                             hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            st = TLG_ERR_HIP;
+        if (st != TLG_OK) {
+            tlg_gemm_destroy(pl);
+            break;
+        }
+        ms /= (float)iters;
+        if (count < max_results) results[count] = tlg_tune_result{pl->variant, pl->splits, ms};
+        ++count;
+        if (!best || ms < best_ms) {
+            tlg_gemm_destroy(best);
+            best = pl;
+            best_ms = ms;
+            best_c = TuneCandidate{cand.variant, cand.splits};
+        } else {
+            tlg_gemm_destroy(pl);
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (n_results) *n_results = std::min(count, max_results);
+    if (st != TLG_OK) {
+        tlg_gemm_destroy(best);
+        return st;
+    }
+    if (!best) return TLG_ERR_UNSUPPORTED;
+    {
+        std::lock_guard<std::mutex> lock(g_tune_mu);
+        g_tune_cache[key] = {best_c.variant, best_c.splits};
+    }
+    *out = best;
+    return TLG_OK;
+}
 
 }  // extern "C"
