@@ -39,6 +39,14 @@ class Oracle:
         lib.oracle_decode.restype = i32
         lib.oracle_encode.argtypes = [i32, vp, i64, vp]
         lib.oracle_encode.restype = i32
+        lib.oracle_mxgemm_rows.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                           i64, i64, vp, i32]
+        lib.oracle_mxgemm_rows.restype = i32
+        lib.oracle_mxgemm_points.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp,
+                                             i64, vp, vp, vp]
+        lib.oracle_mxgemm_points.restype = i32
+        lib.oracle_mx_decode.argtypes = [i32, vp, i64, vp]
+        lib.oracle_mx_decode.restype = i32
         self.lib = lib
         self.path = lib_path
 
@@ -71,6 +79,44 @@ class Oracle:
             raise ValueError(f"oracle_gemm_points failed with {rc}")
         return out
 
+    def mxgemm(self, M, N, K, A, SA, B, SB, *, fmt_a="e4m3", fmt_b="e4m3", c="f16", clear_accum=1, relu=0,
+               C_in_bits=None, rows=None, nthreads=None) -> np.ndarray:
+        """Block-scaled GEMM oracle o(m, n) in float64 (A uint8 [M,K], SA uint8 [M,K/32],
+        B uint8 [N,K], SB uint8 [N,K/32]) for the rows ``rows=(m0, m1)`` (default: all)."""
+        A, SA, B, SB = _u8(A), _u8(SA), _u8(B), _u8(SB)
+        C = _cin(C_in_bits, c)
+        m0, m1 = (0, M) if rows is None else rows
+        out = np.empty((m1 - m0, N), dtype=np.float64)
+        nt = nthreads if nthreads is not None else min(os.cpu_count() or 1, 16)
+        rc = self.lib.oracle_mxgemm_rows(M, N, K, MX_CODES[fmt_a], MX_CODES[fmt_b], _code(c), int(clear_accum),
+                                         int(relu), _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(C), m0, m1,
+                                         out.ctypes.data, int(nt))
+        if rc != 0:
+            raise ValueError(f"oracle_mxgemm_rows failed with {rc}")
+        return out
+
+    def mxgemm_points(self, M, N, K, A, SA, B, SB, ms, ns, *, fmt_a="e4m3", fmt_b="e4m3", c="f16",
+                      clear_accum=1, relu=0, C_in_bits=None) -> np.ndarray:
+        A, SA, B, SB = _u8(A), _u8(SA), _u8(B), _u8(SB)
+        C = _cin(C_in_bits, c)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_mxgemm_points(M, N, K, MX_CODES[fmt_a], MX_CODES[fmt_b], _code(c),
+                                           int(clear_accum), int(relu), _ptr(A), _ptr(SA), _ptr(B), _ptr(SB),
+                                           _ptr(C), ms.shape[0], ms.ctypes.data, ns.ctypes.data,
+                                           out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_mxgemm_points failed with {rc}")
+        return out
+
+    def mx_decode(self, bytes_, fmt) -> np.ndarray:
+        b = np.ascontiguousarray(bytes_).reshape(-1).astype(np.uint8)
+        out = np.empty(b.shape[0], dtype=np.float64)
+        if self.lib.oracle_mx_decode(MX_CODES[fmt], b.ctypes.data, b.shape[0], out.ctypes.data) != 0:
+            raise ValueError("oracle_mx_decode failed")
+        return out
+
     def decode(self, bits, dtype) -> np.ndarray:
         b = np.ascontiguousarray(bits).reshape(-1).astype(np.uint32)
         out = np.empty(b.shape[0], dtype=np.float64)
@@ -91,6 +137,18 @@ class Oracle:
     def rne_out(self, x, dtype) -> np.ndarray:
         """Oracle value rounded to the output dtype and decoded back to float64."""
         return self.decode(self.encode(x, dtype), dtype)
+
+
+MX_CODES = {"e4m3": 10, "e5m2": 11, "e8m0": 12}
+
+
+def _u8(x):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(x)
+    if a.dtype != np.uint8:
+        raise TypeError(f"block-scaled operands and scales are uint8, got {a.dtype}")
+    return a.reshape(-1)
 
 
 def _code(d):
@@ -140,6 +198,14 @@ def gemm_points(*args, **kw):
 
 def decode(bits, dtype):
     return default().decode(bits, dtype)
+
+
+def mxgemm(*args, **kw):
+    return default().mxgemm(*args, **kw)
+
+
+def mxgemm_points(*args, **kw):
+    return default().mxgemm_points(*args, **kw)
 
 
 def encode(x, dtype):

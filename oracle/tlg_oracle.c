@@ -274,3 +274,160 @@ int oracle_encode(int dtype, const double *x, int64_t n, uint32_t *bits)
     for (int64_t i = 0; i < n; ++i) bits[i] = enc(dtype, x[i]);
     return 0;
 }
+
+/* ===========================================================================
+ * Block-scaled ("MX") GEMM: the codegen chapter's block-scaled MMA (sections
+ * 3.4 and 4.6.3): low-precision elements in which every 32 consecutive
+ * elements along K share one power-of-two scale factor (E8M0), fp32
+ * accumulation.  Element formats, from their definitions:
+ *   E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits; exponent field 0 is
+ *         subnormal (frac * 2^-9); S.1111.111 is NaN; there is no infinity
+ *         (largest finite 1.75 * 2^8 = 448).
+ *   E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits, IEEE-style:
+ *         subnormal at field 0, Inf / NaN at field 31.
+ *   E8M0 (scale): an 8-bit biased exponent, value 2^(e - 127); 255 is NaN.
+ * Value computed (A stored [M, K], B stored [N, K], both K-contiguous, as the
+ * pages' "1d1d" block-scaled example has it):
+ *   a(m,k) = elem(A[m*K + k]) * 2^(SA[m*(K/32) + k/32] - 127)
+ *   b(k,n) = elem(B[n*K + k]) * 2^(SB[n*(K/32) + k/32] - 127)
+ *   s(m,n) = (clear_accum ? 0 : C_in(m,n)) + sum_k a(m,k) * b(k,n)   (double)
+ *   o(m,n) = relu ? max(s, +0) : s
+ * K must be a multiple of 32 (whole scale blocks).  NaN inputs: parity unpinned.
+ * ======================================================================== */
+enum { ORACLE_E4M3 = 10, ORACLE_E5M2 = 11, ORACLE_E8M0 = 12 };
+
+static double dec_e4m3(uint32_t b)
+{
+    const uint32_t frac = b & 7u, e = (b >> 3) & 15u;
+    const int neg = (b >> 7) & 1u;
+    double v;
+    if (e == 15u && frac == 7u) return NAN;
+    if (e == 0) v = ldexp((double)frac, 1 - 7 - 3);
+    else v = ldexp((double)(8u + frac), (int)e - 7 - 3);
+    return neg ? -v : v;
+}
+
+static double dec_e5m2(uint32_t b) { return dec_ieee(b & 0xffu, 2, 5); }
+
+static double dec_e8m0(uint32_t b)
+{
+    b &= 0xffu;
+    return b == 255u ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+static double dec_mx(int fmt, uint32_t b)
+{
+    switch (fmt) {
+    case ORACLE_E4M3: return dec_e4m3(b);
+    case ORACLE_E5M2: return dec_e5m2(b);
+    default: return dec_e8m0(b);
+    }
+}
+
+static int valid_elem_fmt(int f) { return f == ORACLE_E4M3 || f == ORACLE_E5M2; }
+
+struct mxjob {
+    int64_t M, N, K, m0;
+    int cd, clear, relu, fa;
+    const uint8_t *A, *SA;
+    const double *bcol;   /* N x K decoded and scaled b: bcol[n*K + k] = b(k, n) */
+    const void *C_in;
+    double *out;
+    int64_t r_begin, r_end;
+};
+
+static void *run_mx_rows(void *arg)
+{
+    struct mxjob *j = (struct mxjob *)arg;
+    const int64_t KB = j->K / 32;
+    double *arow = (double *)malloc(sizeof(double) * (size_t)(j->K > 0 ? j->K : 1));
+    if (!arow) return (void *)1;
+    for (int64_t m = j->r_begin; m < j->r_end; ++m) {
+        for (int64_t k = 0; k < j->K; ++k)
+            arow[k] = dec_mx(j->fa, j->A[m * j->K + k]) * dec_e8m0(j->SA[m * KB + k / 32]);
+        for (int64_t n = 0; n < j->N; ++n) {
+            const double prior = j->clear ? 0.0 : dec(j->cd, c_bits(j->C_in, j->cd, m * j->N + n));
+            const double *bc = j->bcol + n * j->K;
+            double s = prior;
+            for (int64_t kk = 0; kk < j->K; ++kk)
+                s += arow[kk] * bc[kk];
+            if (j->relu && !(s > 0.0)) s = 0.0;
+            j->out[(m - j->m0) * j->N + n] = s;
+        }
+    }
+    free(arow);
+    return NULL;
+}
+
+/* Output rows [m0, m1) of the block-scaled GEMM.  Returns 0 on success, -1 on
+ * bad arguments, -2 on allocation failure. */
+int oracle_mxgemm_rows(int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, int c_dtype, int clear_accum,
+                       int relu, const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                       const void *C_in, int64_t m0, int64_t m1, double *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || m0 < 0 || m1 < m0 || m1 > M) return -1;
+    if (!valid_elem_fmt(fmt_a) || !valid_elem_fmt(fmt_b) || !valid_dtype(c_dtype)) return -1;
+    if (!clear_accum && !C_in && M * N > 0) return -1;
+    if (m1 == m0 || N == 0) return 0;
+    if (K > 0 && (!A || !SA || !B || !SB)) return -1;
+    if (nthreads < 1) nthreads = 1;
+    const int64_t KB = K / 32;
+    double *bcol = (double *)malloc(sizeof(double) * (size_t)(N * (K > 0 ? K : 1)));
+    if (!bcol) return -2;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            bcol[n * K + k] = dec_mx(fmt_b, B[n * K + k]) * dec_e8m0(SB[n * KB + k / 32]);
+    int64_t rows = m1 - m0;
+    if (nthreads > rows) nthreads = (int)rows;
+    struct mxjob *jobs = (struct mxjob *)calloc((size_t)nthreads, sizeof(struct mxjob));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(bcol); free(jobs); free(th); return -2; }
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        struct mxjob *j = &jobs[t];
+        j->M = M; j->N = N; j->K = K; j->m0 = m0;
+        j->cd = c_dtype; j->clear = clear_accum; j->relu = relu; j->fa = fmt_a;
+        j->A = A; j->SA = SA; j->bcol = bcol; j->C_in = C_in; j->out = out;
+        j->r_begin = m0 + rows * t / nthreads;
+        j->r_end = m0 + rows * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[t], NULL, run_mx_rows, &jobs[t]) != 0) { rc = -2; th[t] = 0; }
+    if (run_mx_rows(&jobs[0]) != NULL) rc = -2;
+    for (int t = 1; t < nthreads; ++t) {
+        void *ret = NULL;
+        if (th[t]) { pthread_join(th[t], &ret); if (ret) rc = -2; }
+        else run_mx_rows(&jobs[t]);
+    }
+    free(bcol); free(jobs); free(th);
+    return rc;
+}
+
+/* The same definition at selected output coordinates (pm[i], pn[i]). */
+int oracle_mxgemm_points(int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, int c_dtype, int clear_accum,
+                         int relu, const uint8_t *A, const uint8_t *SA, const uint8_t *B, const uint8_t *SB,
+                         const void *C_in, int64_t npts, const int64_t *pm, const int64_t *pn, double *out)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || npts < 0) return -1;
+    if (!valid_elem_fmt(fmt_a) || !valid_elem_fmt(fmt_b) || !valid_dtype(c_dtype)) return -1;
+    const int64_t KB = K / 32;
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t m = pm[i], n = pn[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) return -1;
+        double s = clear_accum ? 0.0 : dec(c_dtype, c_bits(C_in, c_dtype, m * N + n));
+        for (int64_t k = 0; k < K; ++k)
+            s += (dec_mx(fmt_a, A[m * K + k]) * dec_e8m0(SA[m * KB + k / 32])) *
+                 (dec_mx(fmt_b, B[n * K + k]) * dec_e8m0(SB[n * KB + k / 32]));
+        if (relu) s = (s > 0.0) ? s : 0.0;
+        out[i] = s;
+    }
+    return 0;
+}
+
+/* Decode of E4M3 / E5M2 / E8M0 bytes (for the comparisons and the pins). */
+int oracle_mx_decode(int fmt, const uint8_t *bytes, int64_t n, double *out)
+{
+    if ((!valid_elem_fmt(fmt) && fmt != ORACLE_E8M0) || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = dec_mx(fmt, bytes[i]);
+    return 0;
+}

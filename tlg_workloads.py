@@ -137,3 +137,107 @@ def sample_points(M: int, N: int, count: int, seed: int = 7):
     ms += list(rng.integers(0, M, extra))
     ns += list(rng.integers(0, N, extra))
     return np.asarray(ms, dtype=np.int64), np.asarray(ns, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Block-scaled ("MX") operands: FP8 elements (E4M3 or E5M2) in which every 32
+# consecutive elements along K share one E8M0 power-of-two scale.  Both A and B
+# are stored K-contiguous (A [M, K], B [N, K]); the scales are [M, K/32] and
+# [N, K/32] bytes.
+#
+# Recipe (the pages give the format, not a generator; this is the reading used):
+#   * the same seeded CPU generator, drawing A's values, then B's, then the
+#     prior C when needed, as float32 ("normal": A ~ N(0,1)/sqrt(K), B ~ N(0,1),
+#     so C is O(1); "uniform": U[-1, 1) for both);
+#   * per block of 32 values, the shared exponent X = floor(log2(max |v|)) minus
+#     the element format's largest exponent (8 for E4M3, 15 for E5M2), the usual
+#     way of converting to a block-scaled format; the scale byte is X + 127;
+#   * elements v / 2^X, clamped to the format's largest finite value, cast to
+#     FP8 with torch's round-to-nearest-even conversion;
+#   * "smallint": elements are integers drawn from [lo, hi] (exact in both FP8
+#     formats) and scale bytes are drawn from [125, 129], so every product is an
+#     exact multiple of 2^-4 and the fp32 sums are exact.
+# ---------------------------------------------------------------------------
+FP8_DTYPES = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+FP8_EMAX = {"e4m3": 8, "e5m2": 15}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+
+
+@dataclass(frozen=True)
+class MxCase:
+    name: str
+    M: int
+    N: int
+    K: int
+    fmt: str = "e4m3"        # element format of A and B
+    c: str = "f16"
+    relu: int = 0
+    clear_accum: int = 1
+    dist: str = "normal"     # "normal" | "uniform" | "smallint"
+    seed: int = 0
+    lo: int = -4
+    hi: int = 4
+    note: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """One read of A, B and their scales, one write of C (plus a read when accumulating)."""
+        sc = 4 if self.c == "f32" else 2
+        c_reads = 0 if self.clear_accum else sc * self.M * self.N
+        return (self.M + self.N) * self.K + (self.M + self.N) * (self.K // 32) + sc * self.M * self.N + c_reads
+
+    def with_(self, **kw) -> "MxCase":
+        return replace(self, **kw)
+
+
+MX_CONFIGS = {
+    "mx1": MxCase("mx1", 256, 256, 256, relu=1, seed=1101,
+                  note="C=ReLU(A·B) 256^3 MXFP8 (E4M3, E8M0 scales per 32 of K), fp16 out"),
+    "mx2": MxCase("mx2", 1000, 1500, 768, fmt="e5m2", c="f32", dist="uniform", seed=1102,
+                  note="ragged 1000x1500x768 MXFP8 (E5M2), fp32 out"),
+    "mx3": MxCase("mx3", 8192, 8192, 8192, seed=1103,
+                  note="8192^3 MXFP8 (E4M3, E8M0 scales per 32 of K), fp16 out"),
+}
+
+
+def _mx_quantize(v: torch.Tensor, fmt: str, g: torch.Generator, case: MxCase):
+    rows, K = v.shape
+    if case.dist == "smallint":
+        elems = torch.randint(case.lo, case.hi + 1, (rows, K), generator=g).to(torch.float32)
+        scales = torch.randint(125, 130, (rows, K // 32), generator=g).to(torch.uint8)
+    else:
+        blocks = v.reshape(rows, K // 32, 32)
+        amax = blocks.abs().amax(dim=2).clamp_min(2.0 ** -100)
+        X = torch.floor(torch.log2(amax)) - FP8_EMAX[fmt]
+        X = X.clamp(-127, 127)
+        scales = (X + 127).to(torch.uint8)
+        elems = (blocks / torch.exp2(X).unsqueeze(2)).clamp(-FP8_MAX[fmt], FP8_MAX[fmt]).reshape(rows, K)
+    q = elems.to(FP8_DTYPES[fmt]).view(torch.uint8).contiguous()
+    return q, scales.contiguous()
+
+
+def make_mx_inputs(case: MxCase, with_c: bool | None = None):
+    """CPU uint8 tensors (A [M,K], SA [M,K/32], B [N,K], SB [N,K/32]) and the prior C
+    (or None when clear_accum)."""
+    if case.K % 32:
+        raise ValueError("block-scaled operands need K % 32 == 0")
+    g = torch.Generator().manual_seed(case.seed)
+    if case.dist == "uniform":
+        va = torch.rand((case.M, case.K), generator=g) * 2.0 - 1.0
+        vb = torch.rand((case.N, case.K), generator=g) * 2.0 - 1.0
+    elif case.dist in ("normal", "smallint"):
+        va = torch.randn((case.M, case.K), generator=g) / math.sqrt(max(case.K, 1))
+        vb = torch.randn((case.N, case.K), generator=g)
+    else:
+        raise ValueError(f"unknown distribution {case.dist!r}")
+    A, SA = _mx_quantize(va, case.fmt, g, case)
+    B, SB = _mx_quantize(vb, case.fmt, g, case)
+    need_c = (not case.clear_accum) if with_c is None else with_c
+    C = None
+    if need_c:
+        C = (torch.rand((case.M, case.N), generator=g) * 2.0 - 1.0).to(DTYPES[case.c]).contiguous()
+    return A, SA, B, SB, C
