@@ -51,7 +51,8 @@ extern "C" {
 
 typedef struct tlg_gemm_s *tlg_gemm_t;
 
-typedef enum { TLG_F16 = 1, TLG_BF16 = 2, TLG_F32 = 3 } tlg_dtype;
+/* TLG_E4M3 / TLG_E5M2: FP8 operands of the block-scaled GEMM (tlg_gemm_run_mx). */
+typedef enum { TLG_F16 = 1, TLG_BF16 = 2, TLG_F32 = 3, TLG_E4M3 = 4, TLG_E5M2 = 5 } tlg_dtype;
 
 typedef enum { TLG_EPI_NONE = 0, TLG_EPI_RELU = 1 } tlg_epilogue;
 
@@ -65,7 +66,8 @@ typedef enum {
     TLG_VARIANT_TILE_256_W8 = 5, /* 256x256x64 block tile, 8 wave64s (2 per SIMD), 2-stage ring */
     TLG_VARIANT_TILE_256_DMA = 6, /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
     TLG_VARIANT_TILE_128_DMA = 7, /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
-    TLG_VARIANT_TILE_128_DMA_SPLITK = 8 /* as 7, K split over several workgroups per tile (plan owns a workspace) */
+    TLG_VARIANT_TILE_128_DMA_SPLITK = 8, /* as 7, K split over several workgroups per tile (plan owns a workspace) */
+    TLG_VARIANT_MX_256 = 9     /* block-scaled FP8: 256x256x128, 8 wave64s, scaled MFMA 16x16x128 */
 } tlg_variant;
 
 typedef enum {
@@ -96,14 +98,16 @@ typedef struct {
  * Create a plan for C[M,N] = act(A·B).
  *   M, N, K      : 0 <= M, N <= 2^24, 0 <= K <= 2^22.  M or N == 0 is a no-op plan;
  *                  K == 0 gives C = act(clear_accum ? 0 : C) (the empty sum).
- *   ab_dtype     : TLG_F16 or TLG_BF16 (A and B).
+ *   ab_dtype     : TLG_F16 or TLG_BF16 (A and B); TLG_E4M3 / TLG_E5M2 for the
+ *                  block-scaled GEMM (see tlg_gemm_run_mx).
  *   c_dtype      : TLG_F16, TLG_BF16 or TLG_F32.
  *   transpose_A  : 0 -> A stored [M,K];  1 -> A stored [K,M].
  *   transpose_B  : 0 -> B stored [K,N];  1 -> B stored [N,K].
  *   clear_accum  : 1 -> start from zero; 0 -> add onto C's prior contents.
  *   epilogue     : TLG_EPI_NONE or TLG_EPI_RELU.
  * Returns TLG_ERR_NULL if out is NULL, TLG_ERR_INVALID_ARG for a bad dimension,
- * enum or flag, TLG_ERR_UNSUPPORTED for an operand dtype other than F16/BF16,
+ * enum or flag, TLG_ERR_UNSUPPORTED for an operand dtype other than F16/BF16 (or a
+ * block-scaled request other than the one tlg_gemm_run_mx describes),
  * TLG_ERR_NOMEM if the plan cannot be allocated.  Plans with K split over
  * several workgroups per tile (tlg_plan_info.splits > 1, chosen for output grids
  * of fewer than 128 tiles of 128x128 with at least 8 K tiles of 64) allocate a
@@ -158,6 +162,34 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  * share the workspace, so issue them on one stream or order them by events.
  */
 tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, void *stream);
+
+/*
+ * Block-scaled ("MX") GEMM: the block-scaled MMA of the codegen chapter
+ * (sections 3.4 and 4.6.3): FP8 elements in which every 32 consecutive
+ * elements along K share one E8M0 scale factor, fp32 accumulation.  A plan is
+ * made by tlg_gemm_create with ab_dtype TLG_E4M3 or TLG_E5M2 (both operands
+ * in that format), transpose_A = 0 and transpose_B = 1, and K a multiple of
+ * 128; any other combination is refused with TLG_ERR_UNSUPPORTED (a scaled
+ * operand is never run without its scales).  Value computed:
+ *   acc(m,n) = (clear_accum ? 0 : (float)C[m*N + n])
+ *              + sum_k (A[m*K + k] * 2^(SA[m*(K/32) + k/32] - 127))
+ *                      * (B[n*K + k] * 2^(SB[n*(K/32) + k/32] - 127))
+ *   C[m*N + n] = convert_rne(epilogue == RELU ? max(acc, +0) : acc)
+ * where A[.] and B[.] are decoded as E4M3 (1 sign, 4 exponent bits with bias 7,
+ * 3 fraction bits, no infinity) or E5M2 (IEEE-style, 5/2 bits, bias 15).
+ *   A  : device pointer, M x K bytes, row-major (16-byte aligned).
+ *   SA : device pointer, M x K/32 E8M0 bytes (4-byte aligned).
+ *   B  : device pointer, N x K bytes, row-major (16-byte aligned).
+ *   SB : device pointer, N x K/32 E8M0 bytes (4-byte aligned).
+ *   C  : as for tlg_gemm_run.
+ * Returns TLG_ERR_INVALID_ARG for a plan that is not block-scaled (or C
+ * overlapping an input), TLG_ERR_NULL, TLG_ERR_MISALIGNED, TLG_ERR_HIP; TLG_OK
+ * once the kernel is queued.  tlg_gemm_run refuses block-scaled plans with
+ * TLG_ERR_INVALID_ARG, and tlg_gemm_tune refuses block-scaled requests with
+ * TLG_ERR_UNSUPPORTED.  NaN scales or elements: unspecified.
+ */
+tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void *A, const void *SA, const void *B,
+                           const void *SB, void *C, void *stream);
 
 /* One timed candidate of tlg_gemm_tune. */
 typedef struct {

@@ -56,7 +56,8 @@ def test_create_rejects_bad_arguments():
     assert _create(4, 4, 4, tA=2)[0] == INVALID
     assert _create(4, 4, 4, clear=3)[0] == INVALID
     assert _create(4, 4, 4, epi=2)[0] == INVALID
-    assert _create(4, 4, 4, variant=9)[0] == INVALID
+    assert _create(4, 4, 4, variant=10)[0] == INVALID
+    assert _create(4, 4, 4, variant=9)[0] == UNSUPPORTED                # the block-scaled kernel needs FP8
     assert _create(100, 100, 777, tA=1, tB=1, variant=8)[0] == UNSUPPORTED
     # forced variants that cannot run the request
     assert _create(16, 64, 777, tB=1, variant=3)[0] == UNSUPPORTED      # skinny needs K % 8 == 0
@@ -217,3 +218,44 @@ def test_tune_validates_before_touching_a_device():
     info = tlg.PlanInfo()
     assert lib.tlg_gemm_query(h, ctypes.byref(info)) == OK and info.variant == 4
     assert lib.tlg_gemm_destroy(h) == OK
+
+
+def test_block_scaled_plans():
+    """FP8 block-scaled requests: only A [M,K], B [N,K] with whole 128-wide K tiles; the
+    plan runs through tlg_gemm_run_mx only, and run-time checks precede any launch."""
+    lib = tlg.load_library()
+    E4M3, E5M2 = 4, 5
+    i = tlg.select(8192, 8192, 8192, "e4m3", "f16", transpose_B=True)
+    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles, i.threads) == (9, 256, 256, 128, 1024, 64, 512)
+    assert i.lds_bytes == 2 * (2 * 256 * 128 + 2 * 256 * 4)
+    i = tlg.select(1000, 1500, 768, "e5m2", "f32", transpose_B=True)
+    assert (i.variant, i.grid, i.k_tiles) == (9, 4 * 6, 6)
+    assert tlg.select(0, 16, 128, "e4m3", transpose_B=True).variant == 4
+    for kw, want in ((dict(transpose_B=False), UNSUPPORTED), (dict(transpose_A=True, transpose_B=True), UNSUPPORTED)):
+        with pytest.raises(tlg.TlgError) as e:
+            tlg.select(256, 256, 256, "e4m3", **kw)
+        assert e.value.status == want
+    assert _create(256, 256, 96, ab=E4M3, tB=1)[0] == UNSUPPORTED            # K % 128 != 0
+    assert _create(256, 256, 256, ab=E5M2, tB=1, variant=6)[0] == UNSUPPORTED  # 16-bit kernel, FP8 data
+    st, h = _create(256, 256, 256, ab=E4M3, tB=1)
+    assert st == OK
+    try:
+        # the plain run refuses a block-scaled plan; the scaled run checks its pointers
+        assert lib.tlg_gemm_run(h, 4096, 8192, 1 << 20, None) == INVALID
+        run = lib.tlg_gemm_run_mx
+        assert run(h, 4096, 8192, 12288, 16384, None, None) == NULL
+        assert run(h, 4096, None, 12288, 16384, 1 << 20, None) == NULL
+        assert run(h, 4096 + 8, 8192, 12288, 16384, 1 << 20, None) == MISALIGNED   # A 16-byte aligned
+        assert run(h, 4096, 8192 + 2, 12288, 16384, 1 << 20, None) == MISALIGNED   # SA 4-byte aligned
+        assert run(h, 4096, 8192, 12288, 16384, (1 << 20) + 1, None) == MISALIGNED  # C element-aligned
+        assert run(h, 1 << 20, 8192, 12288, 16384, (1 << 20) + 4096, None) == INVALID  # C overlaps A
+        assert run(None, 1, 1, 1, 1, 1, None) == NULL
+    finally:
+        lib.tlg_gemm_destroy(h)
+    st, h16 = _create(64, 64, 64)
+    assert lib.tlg_gemm_run_mx(h16, 4096, 8192, 12288, 16384, 1 << 20, None) == INVALID
+    lib.tlg_gemm_destroy(h16)
+    # no tuning for the block-scaled GEMM (one kernel serves it)
+    hh = ctypes.c_void_p()
+    assert lib.tlg_gemm_tune(ctypes.byref(hh), 256, 256, 256, E4M3, 1, 0, 1, 1, 0, 4096, 8192, 16384, None, 3,
+                             None, 0, None) == UNSUPPORTED

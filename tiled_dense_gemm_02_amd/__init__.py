@@ -14,16 +14,17 @@ import threading
 
 import torch
 
-__all__ = ["Gemm", "gemm", "select", "tune", "PlanInfo", "TuneResult", "TlgError", "lib_path", "load_library",
-           "status_name", "VARIANTS", "F16", "BF16", "F32"]
+__all__ = ["Gemm", "gemm", "gemm_mx", "select", "tune", "PlanInfo", "TuneResult", "TlgError", "lib_path", "load_library",
+           "status_name", "VARIANTS", "F16", "BF16", "F32", "E4M3", "E5M2"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtlg.so")
 
-F16, BF16, F32 = 1, 2, 3
-_TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+F16, BF16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
+_TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
+                  torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
 VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "tile256w8": 5,
-            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8}
+            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8, "mx256": 9}
 EPILOGUES = {"none": 0, "relu": 1}
 
 STATUS = {0: "TLG_OK", -1: "TLG_ERR_INVALID_ARG", -2: "TLG_ERR_UNSUPPORTED", -3: "TLG_ERR_NULL",
@@ -77,6 +78,8 @@ def load_library():
         lib.tlg_gemm_create_variant.restype = i32
         lib.tlg_gemm_run.argtypes = [vp, vp, vp, vp, vp]
         lib.tlg_gemm_run.restype = i32
+        lib.tlg_gemm_run_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+        lib.tlg_gemm_run_mx.restype = i32
         lib.tlg_gemm_destroy.argtypes = [vp]
         lib.tlg_gemm_destroy.restype = i32
         lib.tlg_gemm_select.argtypes = [ctypes.POINTER(PlanInfo), i64, i64, i64, i32, i32, i32, i32, i32, i32,
@@ -101,7 +104,7 @@ def _code(dt) -> int:
     if isinstance(dt, int):
         return dt
     if isinstance(dt, str):
-        return {"f16": F16, "bf16": BF16, "f32": F32}[dt]
+        return {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2}[dt]
     return _TORCH_TO_CODE[dt]
 
 
@@ -191,6 +194,41 @@ class Gemm:
             raise TlgError("tlg_gemm_run", st)
         return C
 
+    def run_mx(self, A: torch.Tensor, SA: torch.Tensor, B: torch.Tensor, SB: torch.Tensor, C: torch.Tensor,
+               stream=None) -> torch.Tensor:
+        """Enqueue the block-scaled GEMM (tlg_gemm_run_mx).  A [M,K] and B [N,K] hold FP8 bytes
+        (uint8 or the matching float8 dtype), SA [M,K/32] and SB [N,K/32] E8M0 bytes."""
+        M, N, K = self.M, self.N, self.K
+        for name, t, shape in (("A", A, (M, K)), ("SA", SA, (M, K // 32)), ("B", B, (N, K)),
+                               ("SB", SB, (N, K // 32)), ("C", C, (M, N))):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be a device tensor, got {t.device}")
+            if tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+            if t.numel() and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if name != "C" and t.element_size() != 1:
+                raise ValueError(f"{name} must hold one byte per element, got {t.dtype}")
+        if _TORCH_TO_CODE.get(C.dtype) != self.c_code:
+            raise ValueError(f"C has dtype {C.dtype}, plan expects code {self.c_code}")
+        if stream is None:
+            stream = torch.cuda.current_stream(C.device)
+        s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        with torch.cuda.device(C.device):
+            st = self._lib.tlg_gemm_run_mx(self._h, A.data_ptr() or None, SA.data_ptr() or None,
+                                           B.data_ptr() or None, SB.data_ptr() or None, C.data_ptr() or None,
+                                           ctypes.c_void_p(s))
+        if st != 0:
+            raise TlgError("tlg_gemm_run_mx", st)
+        return C
+
+    def run_mx_ptrs(self, a, sa, b, sb, c, stream_handle: int = 0) -> int:
+        """Raw-pointer form of run_mx; returns the status."""
+        return self._lib.tlg_gemm_run_mx(self._h, a or None, sa or None, b or None, sb or None, c or None,
+                                         ctypes.c_void_p(stream_handle))
+
     def run_ptrs(self, a_ptr: int, b_ptr: int, c_ptr: int, stream_handle: int = 0) -> int:
         """Raw-pointer form of run (no checks beyond the library's own); returns the status."""
         return self._lib.tlg_gemm_run(self._h, a_ptr or None, b_ptr or None, c_ptr or None,
@@ -237,6 +275,25 @@ def tune(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, transpose_A: bool
     plan = Gemm(M, N, K, A.dtype, C.dtype, transpose_A=transpose_A, transpose_B=transpose_B,
                 clear_accum=clear_accum, epilogue=epilogue, _handle=h)
     return plan, [(names.get(r.variant, str(r.variant)), r.splits, r.ms) for r in res[:n.value]]
+
+
+def gemm_mx(A: torch.Tensor, SA: torch.Tensor, B: torch.Tensor, SB: torch.Tensor, C: torch.Tensor | None = None,
+            *, fmt: str = "e4m3", clear_accum: bool = True, epilogue: str = "none",
+            out_dtype=torch.float16) -> torch.Tensor:
+    """Block-scaled FP8 GEMM C = act(A·Bᵀ) with E8M0 scales per 32 of K (A [M,K], B [N,K])."""
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        if not clear_accum:
+            raise ValueError("clear_accum=False needs C")
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    key = ("mx", A.device, M, N, K, fmt, C.dtype, bool(clear_accum), epilogue)
+    plan = _plan_cache.get(key)
+    if plan is None:
+        plan = Gemm(M, N, K, fmt, C.dtype, transpose_A=False, transpose_B=True, clear_accum=clear_accum,
+                    epilogue=epilogue)
+        _plan_cache[key] = plan
+    return plan.run_mx(A, SA, B, SB, C)
 
 
 _plan_cache: dict = {}

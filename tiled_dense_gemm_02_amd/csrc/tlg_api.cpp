@@ -47,7 +47,9 @@ namespace {
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 22;
 
-int elem_bytes(int dt) { return dt == TLG_F32 ? 4 : 2; }
+int elem_bytes(int dt) { return dt == TLG_F32 ? 4 : (dt == TLG_E4M3 || dt == TLG_E5M2) ? 1 : 2; }
+
+bool is_mx(int dt) { return dt == TLG_E4M3 || dt == TLG_E5M2; }
 
 const char* dt_name(int dt)
 {
@@ -55,6 +57,8 @@ const char* dt_name(int dt)
     case TLG_F16: return "f16";
     case TLG_BF16: return "bf16";
     case TLG_F32: return "f32";
+    case TLG_E4M3: return "e4m3";
+    case TLG_E5M2: return "e5m2";
     default: return "?";
     }
 }
@@ -70,6 +74,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_TILE_256_DMA: return "tile256dma";
     case TLG_VARIANT_TILE_128_DMA: return "tile128dma";
     case TLG_VARIANT_TILE_128_DMA_SPLITK: return "tile128dma_sk";
+    case TLG_VARIANT_MX_256: return "mx256";
     default: return "?";
     }
 }
@@ -120,11 +125,46 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
     if (!flag_ok(tA) || !flag_ok(tB) || !flag_ok(clear)) return TLG_ERR_INVALID_ARG;
     if (epi != TLG_EPI_NONE && epi != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
-    if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32) return TLG_ERR_INVALID_ARG;
+    if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32 && ab != TLG_E4M3 && ab != TLG_E5M2)
+        return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA_SPLITK || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_MX_256 || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
+    if (is_mx(ab)) {
+        // Block-scaled FP8: A stored [M, K], B stored [N, K], whole 128-wide K
+        // tiles; anything else is refused rather than run without its scales.
+        if (tA || !tB || K % 128 != 0) return TLG_ERR_UNSUPPORTED;
+        if (forced != TLG_VARIANT_AUTO && forced != TLG_VARIANT_MX_256) return TLG_ERR_UNSUPPORTED;
+        const int variant = (M == 0 || N == 0) ? TLG_VARIANT_EMPTY : TLG_VARIANT_MX_256;
+        if (ceil_div(M, 256) * ceil_div(N, 256) > INT32_MAX) return TLG_ERR_INVALID_ARG;
+        p->M = M; p->N = N; p->K = K;
+        p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
+        p->variant = variant;
+        p->vec_a = p->vec_b = 16;
+        p->align_a = p->align_b = 16;
+        tlg_plan_info& in = p->info;
+        in = tlg_plan_info{};
+        in.variant = variant;
+        in.vec_a = in.vec_b = 16;
+        if (variant == TLG_VARIANT_MX_256) {
+            in.block_m = 256; in.block_n = 256; in.block_k = 128;
+            in.stages = 2;
+            in.threads = 512;
+            in.grid = ceil_div(M, 256) * ceil_div(N, 256);
+            in.lds_bytes = 2 * (2 * 256 * 128 + 2 * 256 * 4);
+            in.k_tiles = (int32_t)(K / 128);
+        }
+        in.splits = 1;
+        std::snprintf(p->desc, sizeof(p->desc),
+                      "%s M=%lld N=%lld K=%lld ab=%s c=%s tA=%d tB=%d clear=%d relu=%d block=%dx%dx%d "
+                      "stages=%d threads=%d grid=%lld lds=%lld scale_block=32",
+                      variant_name(variant), (long long)M, (long long)N, (long long)K, dt_name(ab), dt_name(c), tA,
+                      tB, clear, p->relu, in.block_m, in.block_n, in.block_k, in.stages, in.threads,
+                      (long long)in.grid, (long long)in.lds_bytes);
+        return TLG_OK;
+    }
+    if (forced == TLG_VARIANT_MX_256) return TLG_ERR_UNSUPPORTED;
 
     const int va = vec_for(tA ? M : K);
     const int vb = vec_for(tB ? K : N);
@@ -322,6 +362,7 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
 {
     if (!plan) return TLG_ERR_NULL;
     const tlg_gemm_s& p = *plan;
+    if (is_mx(p.ab)) return TLG_ERR_INVALID_ARG;   // needs its scales: tlg_gemm_run_mx
     if (p.variant == TLG_VARIANT_EMPTY) return TLG_OK;
     if (!C) return TLG_ERR_NULL;
     if (p.K > 0 && (!A || !B)) return TLG_ERR_NULL;
@@ -382,6 +423,39 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_n = (int)ceil_div(p.N, ts.bn);
         err = launch_tile(cfg, gp, p.ab, p.tA, p.tB, p.vec_a, p.vec_b, (hipStream_t)stream);
     }
+    return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
+tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const void* B, const void* SB, void* C,
+                           void* stream)
+{
+    if (!plan) return TLG_ERR_NULL;
+    const tlg_gemm_s& p = *plan;
+    if (!is_mx(p.ab)) return TLG_ERR_INVALID_ARG;
+    if (p.variant == TLG_VARIANT_EMPTY) return TLG_OK;
+    if (!C) return TLG_ERR_NULL;
+    if (p.K > 0 && (!A || !B || !SA || !SB)) return TLG_ERR_NULL;
+    const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C, sa = (uintptr_t)SA, sb = (uintptr_t)SB;
+    const int cb = elem_bytes(p.c);
+    if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
+    if (p.K > 0 && ((a % 16) || (b % 16) || (sa % 4) || (sb % 4))) return TLG_ERR_MISALIGNED;
+    const uint64_t a_bytes = p.K > 0 ? (uint64_t)p.M * (uint64_t)p.K : 0;
+    const uint64_t b_bytes = p.K > 0 ? (uint64_t)p.N * (uint64_t)p.K : 0;
+    const uint64_t sa_bytes = a_bytes / 32, sb_bytes = b_bytes / 32;
+    const uint64_t c_bytes = (uint64_t)p.M * (uint64_t)p.N * (uint64_t)cb;
+    if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, b, b_bytes) ||
+        ranges_overlap(c, c_bytes, sa, sa_bytes) || ranges_overlap(c, c_bytes, sb, sb_bytes))
+        return TLG_ERR_INVALID_ARG;
+    MxParams mp{};
+    mp.A = A; mp.SA = SA; mp.B = B; mp.SB = SB; mp.C = C;
+    mp.M = (int)p.M; mp.N = (int)p.N; mp.K = (int)p.K;
+    mp.relu = p.relu;
+    mp.clear_accum = p.clear;
+    mp.c_dtype = p.c;
+    mp.c_vec = (p.N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    mp.tiles_m = (int)ceil_div(p.M, 256);
+    mp.tiles_n = (int)ceil_div(p.N, 256);
+    const hipError_t err = launch_mx(mp, p.ab == TLG_E4M3 ? 0 : 1, (hipStream_t)stream);
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }
 
@@ -471,6 +545,7 @@ tlg_status tlg_gemm_tune(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int32
     tlg_status st = plan_build(&probe, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
                                TLG_VARIANT_AUTO);
     if (st != TLG_OK) return st;
+    if (is_mx(ab_dtype)) return TLG_ERR_UNSUPPORTED;   // one kernel serves block-scaled GEMM: nothing to tune
     if (probe.variant == TLG_VARIANT_EMPTY)
         return plan_create(out, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
                            TLG_VARIANT_AUTO);

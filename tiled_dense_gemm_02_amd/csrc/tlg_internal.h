@@ -96,4 +96,18 @@ hipError_t launch_lds128_bf16(const GemmParams& p, int transpose_A, int transpos
 hipError_t launch_lds128sk_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128sk_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 
+// Block-scaled FP8 GEMM (gemm_mx.hip).  A [M,K], B [N,K] FP8 bytes; SA [M,K/32],
+// SB [N,K/32] E8M0 bytes; K % 128 == 0.
+struct MxParams {
+    const void* A;
+    const void* SA;
+    const void* B;
+    const void* SB;
+    void* C;
+    int M, N, K;
+    int relu, clear_accum, c_dtype, c_vec;
+    int tiles_m, tiles_n;
+};
+hipError_t launch_mx(const MxParams& p, int fmt, hipStream_t stream);   // fmt: 0 = E4M3, 1 = E5M2
+
 }  // namespace tlg
