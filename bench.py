@@ -1,15 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the tiled GEMM C = act(A·B) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5a|c3|c2|c5b|c1|c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5a|c3|c2|c5b|c1|c4|mx1|mx2|mx3]
                     [--no-cpu-baseline] [--no-secondary] [--copy-calibration]
 
 A step is one launch of the whole hot path (global->LDS tile copies, the
 pipelined MFMA K loop and the fused epilogue) over one batch of seeded synthetic
 inputs already resident in HBM.  The headline workload is the 8192^3 fp16 GEMM
 (fp32 accumulate, fp16 out); the 4096^3 ReLU GEMM, the memory-bound skinny
-16x16384x8192 case and the small 1024^3, 1000x1500x777 bf16 and 256^3 cases are
-reported alongside in "secondary".  Operand sets are
+16x16384x8192 case, the small 1024^3, 1000x1500x777 bf16 and 256^3 cases and the
+8192^3 block-scaled MXFP8 GEMM are reported alongside in "secondary".  Operand sets are
 rotated so that the inputs of consecutive launches are not the same buffers
 (keeps the ~256 MB Infinity Cache from serving repeat reads).
 
@@ -33,7 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s (fp16, fp32 acc) and % of MFMA peak; skinny: HBM GB/s %"
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}     # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6,     # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+               "e4m3": 5033.2, "e5m2": 5033.2}    # FP8 (block-scaled): twice that
 PEAK_HBM_GBS = 8000.0
 # Sources of each kernel family, keyed by the plan's variant number (tlg.h).
 KERNEL_SOURCES = {
@@ -44,6 +45,7 @@ KERNEL_SOURCES = {
     6: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     7: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     8: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
+    9: ["gemm_mx.hpp", "gemm_mx.hip", "gemm_lds.hpp", "tlg_device.hpp"],
 }
 
 
@@ -73,7 +75,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     # ~40 ms of launches: the clock settles only after tens of ms of MFMA load
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c5a")
+    ap.add_argument("--workload", default="c5a", help="c1..c5b, or a block-scaled workload mx1..mx3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -143,6 +145,61 @@ def measure(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=0.0
     return {"ms": ms, "wall_s": wall, "plan": plan, "C": C, "A": A, "B": B, "nsets": nsets}
 
 
+def measure_mx(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=0.0):
+    """measure() for a block-scaled FP8 workload (tlg_gemm_run_mx)."""
+    import torch
+    import tiled_dense_gemm_02_amd as tlg
+    import tlg_workloads as W
+
+    dev = torch.device("cuda:0")
+    A, SA, B, SB, _ = W.make_mx_inputs(case)
+    plan = tlg.Gemm(case.M, case.N, case.K, case.fmt, plan_out_dtype(case), transpose_B=True,
+                    epilogue="relu" if case.relu else "none")
+    nsets = max(1, min(8, math.ceil(rotate_bytes / max(A.numel() + B.numel(), 1))))
+    sets = [(A.to(dev), SA.to(dev), B.to(dev), SB.to(dev)) for _ in range(nsets)]
+    C = torch.empty((case.M, case.N), dtype=plan_out_dtype(case), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    plan.run_mx(*sets[0][:2], *sets[0][2:], C, stream)
+    ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
+    c_ptr, sh = C.data_ptr(), stream.cuda_stream
+    status = 0
+
+    def launch(i):
+        a, sa, b, sb = ptrs[i % nsets]
+        return plan.run_mx_ptrs(a, sa, b, sb, c_ptr, sh)
+
+    for i in range(warmup):
+        status |= launch(i)
+    torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for i in range(20):
+            status |= launch(i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        per = max(w0.elapsed_time(w1) / 20, 1e-3)
+        for i in range(int(math.ceil(max(0.0, min_warm_ms - 20 * per) / per))):
+            status |= launch(i)
+        torch.cuda.synchronize()
+    if log:
+        log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        status |= launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError(f"tlg_gemm_run_mx failed during the timed launches (status {status})")
+    return {"ms": start.elapsed_time(end) / steps, "wall_s": time.perf_counter() - t0, "plan": plan, "C": C,
+            "nsets": nsets}
+
+
 def plan_out_dtype(case):
     import torch
     return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.c]
@@ -173,6 +230,28 @@ def cpu_baseline(case, C_gpu, rows):
             "seconds": dt, "sample_matches_gpu": ok}
 
 
+def cpu_baseline_mx(case, C_gpu, rows):
+    """cpu_baseline() for a block-scaled FP8 workload (the MX oracle)."""
+    import numpy as np
+    import tlg_workloads as W
+    from oracle import build_oracle, oracle as O
+    if not os.path.exists(O.LIB_PATH):
+        build_oracle.build()
+    A, SA, B, SB, _ = W.make_mx_inputs(case)
+    nthreads = min(os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    o = O.mxgemm(case.M, case.N, case.K, A.numpy(), SA.numpy(), B.numpy(), SB.numpy(), fmt_a=case.fmt,
+                 fmt_b=case.fmt, c=case.c, relu=case.relu, rows=(0, rows), nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * case.N * case.K
+    gpu = C_gpu[:rows].float().cpu().numpy().astype(np.float64)
+    ok = bool((np.abs(gpu - o) <= O.tolerance(o, case.K, case.c)).all())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"first {rows} of {case.M} output rows of {case.name} "
+                      f"({flops / 1e9:.1f} GFLOP, fp64 triple loop, {dt:.1f} s)",
+            "seconds": dt, "sample_matches_gpu": ok}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -193,11 +272,13 @@ def main():
         log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
         del x, y
 
-    case = W.CONFIGS[args.workload]
-    r = measure(case, args.steps, args.warmup, log=log)
+    is_mx = args.workload in W.MX_CONFIGS
+    case = W.MX_CONFIGS[args.workload] if is_mx else W.CONFIGS[args.workload]
+    r = (measure_mx if is_mx else measure)(case, args.steps, args.warmup, log=log)
     plan = r["plan"]
     info = plan.info
     kind = "skinny" if info.variant == 3 else "tile"   # HBM-bound vs MFMA-bound kernel
+    ab = case.fmt if is_mx else case.ab
     ms = r["ms"]
     tflops = case.flops / (ms * 1e-3) / 1e12
     gbs = case.algorithmic_bytes / (ms * 1e-3) / 1e9
@@ -206,8 +287,8 @@ def main():
                 "frac": gbs / PEAK_HBM_GBS}
         value, unit = gbs, "GB/s"
     else:
-        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[case.ab], "unit": "TFLOP/s",
-                "frac": tflops / PEAK_TFLOPS[case.ab]}
+        roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[ab], "unit": "TFLOP/s",
+                "frac": tflops / PEAK_TFLOPS[ab]}
         value, unit = tflops, "TFLOP/s"
     roof["traffic"] = stored_traffic(args.workload, info.variant)
     roof["kernel"] = plan.describe().split()[0]
@@ -216,24 +297,25 @@ def main():
 
     out = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": case.ab, "data": "synthetic (seeded, see tlg_workloads.py)",
+           "vs_baseline": None, "dtype": ab, "data": "synthetic (seeded, see tlg_workloads.py)",
            "config": {"workload": f"{case.name}: {case.note}", "M": case.M, "N": case.N, "K": case.K,
-                      "ab_dtype": case.ab, "c_dtype": case.c, "transpose_A": case.transpose_A,
-                      "transpose_B": case.transpose_B, "epilogue": "relu" if case.relu else "none",
+                      "ab_dtype": ab, "c_dtype": case.c, "transpose_A": 0 if is_mx else case.transpose_A,
+                      "transpose_B": 1 if is_mx else case.transpose_B, "epilogue": "relu" if case.relu else "none",
                       "plan": plan.describe(), "operand_sets_rotated": r["nsets"]},
            "roofline": roof}
 
     if not args.no_secondary:
         sec = []
-        for name in ("c3", "c5b", "c2", "c4", "c1"):
+        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3"):
             if name == args.workload:
                 continue
-            c2 = W.CONFIGS[name]
-            rr = measure(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
+            sec_mx = name in W.MX_CONFIGS
+            c2 = W.MX_CONFIGS[name] if sec_mx else W.CONFIGS[name]
+            rr = (measure_mx if sec_mx else measure)(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
             t = rr["ms"] * 1e-3
             entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
                      "GB/s": c2.algorithmic_bytes / t / 1e9, "plan": rr["plan"].describe()}
-            entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.ab]
+            entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.fmt if sec_mx else c2.ab]
             entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS
             sec.append(entry)
             del rr
@@ -241,8 +323,9 @@ def main():
 
     if not args.no_cpu_baseline:
         # a bounded sample (~10 s of the oracle on 16 host threads)
-        rows = {"c5a": 4096, "c3": 4096, "c2": 1024, "c1": 256, "c4": 1000, "c5b": 16}[args.workload]
-        cb = cpu_baseline(case, r["C"], rows)
+        rows = {"c5a": 4096, "c3": 4096, "c2": 1024, "c1": 256, "c4": 1000, "c5b": 16, "mx1": 256, "mx2": 1000,
+                "mx3": 2048}[args.workload]
+        cb = (cpu_baseline_mx if is_mx else cpu_baseline)(case, r["C"], rows)
         out["cpu_baseline"] = cb
         if unit == "GB/s":
             cb["value_gbs"] = None
