@@ -47,6 +47,11 @@ class Oracle:
         lib.oracle_mxgemm_points.restype = i32
         lib.oracle_mx_decode.argtypes = [i32, vp, i64, vp]
         lib.oracle_mx_decode.restype = i32
+        f64 = ctypes.c_double
+        lib.oracle_attn_rows.argtypes = [i64, i64, i64, i64, i32, i32, f64, vp, vp, vp, i64, i64, vp, i32]
+        lib.oracle_attn_rows.restype = i32
+        lib.oracle_attn_points.argtypes = [i64, i64, i64, i64, i32, i32, f64, vp, vp, vp, i64, vp, vp, vp, vp]
+        lib.oracle_attn_points.restype = i32
         self.lib = lib
         self.path = lib_path
 
@@ -108,6 +113,35 @@ class Oracle:
                                            out.ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle_mxgemm_points failed with {rc}")
+        return out
+
+    def attn(self, B, S, H, D, Q_bits, K_bits, V_bits, *, dtype="f16", causal=1, scale=None, rows=None,
+             nthreads=None) -> np.ndarray:
+        """Attention forward o(b, i, h, :) in float64, operands [B, S, H, D] as uint16 bits, for the
+        query positions ``rows=(i0, i1)`` (default: all); the result is [B, i1-i0, H, D]."""
+        Q, K, V = _u16(Q_bits), _u16(K_bits), _u16(V_bits)
+        i0, i1 = (0, S) if rows is None else rows
+        out = np.empty((B, i1 - i0, H, D), dtype=np.float64)
+        sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        nt = nthreads if nthreads is not None else min(os.cpu_count() or 1, 16)
+        rc = self.lib.oracle_attn_rows(B, S, H, D, _code(dtype), int(causal), sc, _ptr(Q), _ptr(K), _ptr(V),
+                                       i0, i1, out.ctypes.data, int(nt))
+        if rc != 0:
+            raise ValueError(f"oracle_attn_rows failed with {rc}")
+        return out
+
+    def attn_points(self, B, S, H, D, Q_bits, K_bits, V_bits, pb, pi, ph, *, dtype="f16", causal=1,
+                    scale=None) -> np.ndarray:
+        """Output rows o(pb[n], pi[n], ph[n], :) as an [n, D] float64 array."""
+        Q, K, V = _u16(Q_bits), _u16(K_bits), _u16(V_bits)
+        pb, pi, ph = (np.ascontiguousarray(x, dtype=np.int64) for x in (pb, pi, ph))
+        out = np.empty((pb.shape[0], D), dtype=np.float64)
+        sc = 1.0 / np.sqrt(D) if scale is None else float(scale)
+        rc = self.lib.oracle_attn_points(B, S, H, D, _code(dtype), int(causal), sc, _ptr(Q), _ptr(K), _ptr(V),
+                                         pb.shape[0], pb.ctypes.data, pi.ctypes.data, ph.ctypes.data,
+                                         out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_attn_points failed with {rc}")
         return out
 
     def mx_decode(self, bytes_, fmt) -> np.ndarray:
@@ -206,6 +240,27 @@ def mxgemm(*args, **kw):
 
 def mxgemm_points(*args, **kw):
     return default().mxgemm_points(*args, **kw)
+
+
+def attn(*args, **kw):
+    return default().attn(*args, **kw)
+
+
+def attn_points(*args, **kw):
+    return default().attn_points(*args, **kw)
+
+
+def attn_tolerance(o: np.ndarray, vmax: float, dtype="f16") -> np.ndarray:
+    """Per-element bound for the attention forward:
+    |gpu - o| <= 2u (|o| + max|V|) + 1e-5, u the unit roundoff of the operand type
+    (2^-11 for fp16, 2^-8 for bf16).  The probabilities are rounded to the operand
+    type before the second product (relative error <= u each, so <= u max|V| on
+    the weighted sum of V rows), the normaliser may use unrounded or rounded
+    probabilities (<= u |o|) and the output is rounded once (<= u |o|); the fp32
+    scores, exponentials and sums add far less than 1e-5 for the workloads'
+    magnitudes."""
+    u = 2.0 ** -8 if _code(dtype) == BF16 else 2.0 ** -11
+    return 2.0 * u * (np.abs(o) + vmax) + 1e-5
 
 
 def encode(x, dtype):

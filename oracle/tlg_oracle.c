@@ -1,5 +1,7 @@
 /*
  * CPU oracle for the tiled dense GEMM  C = act(A·B)  — TEST INFRASTRUCTURE ONLY.
+ * Further sections below hold the block-scaled (MX) GEMM and the attention
+ * forward pass, each with its own statement of what it computes.
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
  * load this library.  It shares no code, header, table or helper with the HIP
@@ -429,5 +431,135 @@ int oracle_mx_decode(int fmt, const uint8_t *bytes, int64_t n, double *out)
 {
     if ((!valid_elem_fmt(fmt) && fmt != ORACLE_E8M0) || n < 0) return -1;
     for (int64_t i = 0; i < n; ++i) out[i] = dec_mx(fmt, bytes[i]);
+    return 0;
+}
+
+/* ===========================================================================
+ * Attention forward (the FlashAttention tile program of the handbook page
+ * "TileLang: a tile language one level below Triton", section "FlashAttention:
+ * online softmax as tile code").  The tile program walks the keys in blocks
+ * and keeps a running row maximum and row sum; that online rescaling reaches
+ * the ordinary softmax exactly (up to rounding), so the oracle is the plain
+ * definition, in double:
+ *
+ *   element (b, t, h, d) of Q, K, V and O sits at ((b*S + t)*H + h)*D + d
+ *   keys allowed for query i:  j in [0, S), and j <= i when causal
+ *   s_j   = scale * sum_d q(b,i,h,d) * k(b,j,h,d)
+ *   w_j   = exp(s_j - max_j s_j)
+ *   o(d)  = sum_j w_j * v(b,j,h,d) / sum_j w_j
+ *
+ * The page folds log2(e) into its scale and uses exp2; exp2(x*log2 e) is
+ * exp(x), so the oracle uses exp with the plain scale (the page sets
+ * scale = 1/sqrt(dim); here it is an input).  The causal rule is the page's:
+ * a query at position i sees the keys at positions j <= i.  Subtracting the
+ * row maximum changes nothing mathematically and keeps exp finite.
+ * ======================================================================== */
+struct attnjob {
+    int64_t S, H, D, i0, i1;
+    int dt, causal;
+    double scale;
+    const uint16_t *Q, *K, *V;
+    double *out;            /* [B, i1-i0, H, D] */
+    int64_t w_begin, w_end; /* work items: (b, i, h) flattened over [B, i1-i0, H] */
+};
+
+static void attn_row(const struct attnjob *j, int64_t b, int64_t i, int64_t h, double *s, double *o)
+{
+    const int64_t S = j->S, H = j->H, D = j->D;
+    const int64_t nkeys = j->causal ? i + 1 : S;
+    const uint16_t *q = j->Q + ((b * S + i) * H + h) * D;
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < nkeys; ++t) {
+        const uint16_t *k = j->K + ((b * S + t) * H + h) * D;
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += dec(j->dt, q[d]) * dec(j->dt, k[d]);
+        s[t] = j->scale * dot;
+        if (s[t] > mx) mx = s[t];
+    }
+    double denom = 0.0;
+    for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t t = 0; t < nkeys; ++t) {
+        const double w = exp(s[t] - mx);
+        const uint16_t *v = j->V + ((b * S + t) * H + h) * D;
+        denom += w;
+        for (int64_t d = 0; d < D; ++d) o[d] += w * dec(j->dt, v[d]);
+    }
+    for (int64_t d = 0; d < D; ++d) o[d] /= denom;
+}
+
+static void *run_attn(void *arg)
+{
+    struct attnjob *j = (struct attnjob *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(j->S > 0 ? j->S : 1));
+    if (!s) return (void *)1;
+    const int64_t rows = j->i1 - j->i0;
+    for (int64_t w = j->w_begin; w < j->w_end; ++w) {
+        const int64_t h = w % j->H, r = (w / j->H) % rows, b = w / (j->H * rows);
+        attn_row(j, b, j->i0 + r, h, s, j->out + ((b * rows + r) * j->H + h) * j->D);
+    }
+    free(s);
+    return NULL;
+}
+
+static int attn_args_ok(int64_t B, int64_t S, int64_t H, int64_t D, int dtype, double scale)
+{
+    return B >= 0 && S >= 0 && H >= 0 && D > 0 && (dtype == ORACLE_F16 || dtype == ORACLE_BF16) && isfinite(scale);
+}
+
+/* Query positions [i0, i1) of every batch and head.  Returns 0 on success, -1 on
+ * bad arguments, -2 on allocation failure. */
+int oracle_attn_rows(int64_t B, int64_t S, int64_t H, int64_t D, int dtype, int causal, double scale,
+                     const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t i0, int64_t i1,
+                     double *out, int nthreads)
+{
+    if (!attn_args_ok(B, S, H, D, dtype, scale) || i0 < 0 || i1 < i0 || i1 > S) return -1;
+    const int64_t items = B * (i1 - i0) * H;
+    if (items == 0) return 0;
+    if (!Q || !K || !V || !out) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > items) nthreads = (int)items;
+    struct attnjob *jobs = (struct attnjob *)calloc((size_t)nthreads, sizeof(struct attnjob));
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        struct attnjob *j = &jobs[t];
+        j->S = S; j->H = H; j->D = D; j->i0 = i0; j->i1 = i1;
+        j->dt = dtype; j->causal = causal != 0; j->scale = scale;
+        j->Q = Q; j->K = K; j->V = V; j->out = out;
+        j->w_begin = items * t / nthreads;
+        j->w_end = items * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t)
+        if (pthread_create(&th[t], NULL, run_attn, &jobs[t]) != 0) { rc = -2; th[t] = 0; }
+    if (run_attn(&jobs[0]) != NULL) rc = -2;
+    for (int t = 1; t < nthreads; ++t) {
+        void *ret = NULL;
+        if (th[t]) { pthread_join(th[t], &ret); if (ret) rc = -2; }
+        else if (run_attn(&jobs[t]) != NULL) rc = -2;
+    }
+    free(jobs); free(th);
+    return rc;
+}
+
+/* The same definition for the output rows (pb[n], pi[n], ph[n]); out is [npts, D]. */
+int oracle_attn_points(int64_t B, int64_t S, int64_t H, int64_t D, int dtype, int causal, double scale,
+                       const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t npts,
+                       const int64_t *pb, const int64_t *pi, const int64_t *ph, double *out)
+{
+    if (!attn_args_ok(B, S, H, D, dtype, scale) || npts < 0) return -1;
+    if (npts == 0) return 0;
+    if (!Q || !K || !V || !out || !pb || !pi || !ph) return -1;
+    struct attnjob j;
+    memset(&j, 0, sizeof j);
+    j.S = S; j.H = H; j.D = D; j.dt = dtype; j.causal = causal != 0; j.scale = scale;
+    j.Q = Q; j.K = K; j.V = V;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (!s) return -2;
+    for (int64_t n = 0; n < npts; ++n) {
+        if (pb[n] < 0 || pb[n] >= B || pi[n] < 0 || pi[n] >= S || ph[n] < 0 || ph[n] >= H) { free(s); return -1; }
+        attn_row(&j, pb[n], pi[n], ph[n], s, out + n * D);
+    }
+    free(s);
     return 0;
 }

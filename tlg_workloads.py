@@ -241,3 +241,94 @@ def make_mx_inputs(case: MxCase, with_c: bool | None = None):
     if need_c:
         C = (torch.rand((case.M, case.N), generator=g) * 2.0 - 1.0).to(DTYPES[case.c]).contiguous()
     return A, SA, B, SB, C
+
+
+# ---------------------------------------------------------------------------
+# Attention forward (the FlashAttention tile program of the handbook page,
+# section "FlashAttention: online softmax as tile code"): Q, K, V and O are
+# [batch, seq, heads, dim] tensors of fp16 (or bf16), as on that page.
+#
+# Recipe (the page gives shapes, not values; this is the reading used):
+#   * the same seeded CPU generator, drawing Q, then K, then V as float32;
+#   * "normal": i.i.d. N(0, 1) entries, so with the page's scale 1/sqrt(dim)
+#     the scores are O(1) and the softmax is neither flat nor one-hot;
+#   * "uniform_keys": K all zeros (every allowed key gets the same weight, so
+#     the output is the mean of the allowed V rows), Q and V N(0, 1);
+#   * then a round-to-nearest-even cast to the operand dtype on the CPU; the
+#     rounded bits are the inputs of both sides.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class AttnCase:
+    name: str
+    B: int
+    S: int
+    H: int
+    D: int
+    causal: int = 1
+    dtype: str = "f16"
+    dist: str = "normal"     # "normal" | "uniform_keys"
+    scale: float | None = None   # None: 1/sqrt(D), the page's choice
+    seed: int = 0
+    note: str = field(default="", compare=False)
+
+    @property
+    def softmax_scale(self) -> float:
+        return 1.0 / math.sqrt(self.D) if self.scale is None else float(self.scale)
+
+    @property
+    def shape(self):
+        return (self.B, self.S, self.H, self.D)
+
+    @property
+    def flops(self) -> int:
+        """Two products of 2*D flops per allowed (query, key) pair."""
+        pairs = self.S * (self.S + 1) // 2 if self.causal else self.S * self.S
+        return 4 * self.D * pairs * self.B * self.H
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """One read of Q, K and V and one write of O."""
+        return 4 * self.B * self.S * self.H * self.D * 2
+
+    def with_(self, **kw) -> "AttnCase":
+        return replace(self, **kw)
+
+
+ATTN_CONFIGS = {
+    "fa1": AttnCase("fa1", 1, 1024, 8, 64, causal=1, seed=1201,
+                    note="causal attention, batch 1, seq 1024, 8 heads, dim 64 (the page's instance), fp16"),
+    "fa2": AttnCase("fa2", 2, 777, 3, 128, causal=0, seed=1202,
+                    note="non-causal attention, ragged seq 777, dim 128, fp16"),
+    "fa3": AttnCase("fa3", 4, 4096, 32, 128, causal=1, seed=1203,
+                    note="causal attention, batch 4, seq 4096, 32 heads, dim 128, fp16"),
+    "fa4": AttnCase("fa4", 4, 4096, 32, 64, causal=1, seed=1204,
+                    note="causal attention, batch 4, seq 4096, 32 heads, dim 64, fp16"),
+}
+
+
+def make_attn_inputs(case: AttnCase):
+    """CPU tensors Q, K, V of shape [B, S, H, D] in the case's dtype."""
+    g = torch.Generator().manual_seed(case.seed)
+    q = torch.randn(case.shape, generator=g)
+    k = torch.randn(case.shape, generator=g)
+    v = torch.randn(case.shape, generator=g)
+    if case.dist == "uniform_keys":
+        k = torch.zeros(case.shape)
+    elif case.dist != "normal":
+        raise ValueError(f"unknown distribution {case.dist!r}")
+    dt = DTYPES[case.dtype]
+    return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+def sample_attn_rows(case: AttnCase, count: int, seed: int = 11):
+    """Output rows (b, i, h) for sampled checks: the first and last query of the first and
+    last (batch, head), plus random rows."""
+    rng = np.random.default_rng(seed)
+    pb = [0, 0, case.B - 1, case.B - 1]
+    pi = [0, case.S - 1, 0, case.S - 1]
+    ph = [0, 0, case.H - 1, case.H - 1]
+    extra = max(count - 4, 0)
+    pb += list(rng.integers(0, case.B, extra))
+    pi += list(rng.integers(0, case.S, extra))
+    ph += list(rng.integers(0, case.H, extra))
+    return tuple(np.asarray(x, dtype=np.int64) for x in (pb, pi, ph))
