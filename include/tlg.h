@@ -228,6 +228,40 @@ tlg_status tlg_gemm_tune(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
                          const void *A, const void *B, void *C, void *stream, int32_t iters,
                          tlg_tune_result *results, int32_t max_results, int32_t *n_results);
 
+/*
+ * Attention forward with online softmax: the FlashAttention tile program of the
+ * handbook page "TileLang: a tile language one level below Triton", section
+ * "FlashAttention: online softmax as tile code".
+ *
+ * Value computed, for every batch b, head h and query position i (0 <= i < seq):
+ *   keys allowed:  j in [0, seq), and j <= i when causal != 0 (the page's rule)
+ *   s_j  = softmax_scale * sum_d Q[b,i,h,d] * K[b,j,h,d]          (fp32)
+ *   O[b,i,h,:] = convert_rne( sum_j p_j V[b,j,h,:] / sum_j p_j ),
+ *   p_j  = exp(s_j - max_j s_j), rounded to the operand type before the second
+ *          product (the page rounds its probability tile to fp16), fp32 sums.
+ * The page's scale is 1/sqrt(dim); the caller passes it (any finite value).
+ *
+ * Layout: Q, K, V and O are dense [batch, seq, heads, dim] tensors; element
+ * (b, t, h, d) sits at ((b*seq + t)*heads + h)*dim + d.  All four share dtype
+ * (TLG_F16 or TLG_BF16) and must be 16-byte aligned.  dim must be 64 or 128.
+ * seq * heads * dim * 2 must stay below 2^31 bytes (per-batch offsets are 32-bit).
+ * O must not overlap Q, K or V (Q, K and V may overlap each other).
+ *
+ * Ownership: the caller owns all four tensors (device memory) and keeps them
+ * alive until the queued work has finished.  The call allocates nothing, does
+ * not synchronise and enqueues at most one kernel on `stream`; calls with
+ * disjoint outputs may overlap.  batch, seq or heads == 0 enqueues nothing.
+ *
+ * Errors: TLG_ERR_INVALID_ARG (negative sizes, dim <= 0, causal not 0/1,
+ * non-finite scale, unknown dtype, O overlapping an input), TLG_ERR_UNSUPPORTED
+ * (dim other than 64/128, FP32 or FP8 operands, sizes past the limits above),
+ * TLG_ERR_NULL (a null tensor with non-empty sizes), TLG_ERR_MISALIGNED,
+ * TLG_ERR_HIP (launch failure).  Nothing is enqueued on error.
+ */
+tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, int64_t batch, int64_t seq,
+                        int64_t heads, int64_t dim, int32_t dtype, int32_t causal, float softmax_scale,
+                        void *stream);
+
 /* Release a plan (and its workspace, if any; the caller first makes sure no run of
  * the plan is still in flight).  NULL is accepted (no-op, TLG_OK). */
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan);

@@ -1,0 +1,127 @@
+"""GPU parity of the attention forward (tlg_attn_fwd) against the CPU attention oracle on
+the same seeded fp16/bf16 bits.  Tolerance per element (derived in the oracle):
+|gpu - o| <= 2u (|o| + max|V|) + 1e-5, u = 2^-11 (fp16) or 2^-8 (bf16)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import tlg_workloads as W
+from oracle import oracle as O
+from parity import log, out_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _run(case: W.AttnCase, q, k, v, guard: int = 0):
+    """Run through the binding; with guard > 0 (elements), O sits inside a larger buffer whose
+    guard bands must come back untouched."""
+    import tiled_dense_gemm_02_amd as tlg
+    dev = _device()
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    n = q.numel()
+    if guard:
+        buf = torch.empty(guard + n + guard, dtype=q.dtype, device=dev)
+        buf.view(torch.int16).fill_(0x5A5A)
+        O_ = buf[guard:guard + n].view(q.shape)
+    else:
+        buf, O_ = None, torch.empty_like(qd)
+    tlg.attention(qd, kd, vd, O_, causal=bool(case.causal), scale=case.scale)
+    torch.cuda.synchronize()
+    if guard:
+        g = buf.view(torch.int16)
+        assert bool((g[:guard] == 0x5A5A).all()) and bool((g[guard + n:] == 0x5A5A).all()), "guard band written"
+    return O_
+
+
+def _check(case: W.AttnCase, gpu: np.ndarray, o: np.ndarray, vmax: float):
+    tol = O.attn_tolerance(o, vmax, case.dtype)
+    err = np.abs(gpu - o)
+    bad = ~(err <= tol)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{case.name}: {int(bad.sum())} of {bad.size} outside tolerance; first {idx.tolist()} "
+                             f"gpu={gpu[bad][:5]} oracle={o[bad][:5]}")
+    return float(err.max()) if err.size else 0.0
+
+
+def _full(case: W.AttnCase, guard: int = 0):
+    log(f"[case] {case.name} B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} {case.dtype}")
+    q, k, v = W.make_attn_inputs(case)
+    out = _run(case, q, k, v, guard)
+    o = O.attn(case.B, case.S, case.H, case.D, W.bits16(q), W.bits16(k), W.bits16(v), dtype=case.dtype,
+               causal=case.causal, scale=case.softmax_scale)
+    err = _check(case, out_values(out), o, float(v.float().abs().max()))
+    log(f"    max|err| = {err:.3e}")
+
+
+def test_fa1_page_instance_full():
+    _full(W.ATTN_CONFIGS["fa1"])
+
+
+def test_fa2_ragged_noncausal_full():
+    _full(W.ATTN_CONFIGS["fa2"], guard=4096)
+
+
+@pytest.mark.parametrize("name", ["fa3", "fa4"])
+def test_full_size_sampled(name):
+    case = W.ATTN_CONFIGS[name]
+    log(f"[case] {name} sampled")
+    q, k, v = W.make_attn_inputs(case)
+    out = out_values(_run(case, q, k, v))
+    pb, pi, ph = W.sample_attn_rows(case, 384)
+    o = O.attn_points(case.B, case.S, case.H, case.D, W.bits16(q), W.bits16(k), W.bits16(v), pb, pi, ph,
+                      dtype=case.dtype, causal=case.causal, scale=case.softmax_scale)
+    err = _check(case, out[pb, pi, ph], o, float(v.float().abs().max()))
+    assert np.isfinite(out).all()
+    log(f"    max|err| = {err:.3e}")
+
+
+SWEEP = [(1, 1, 1, 64, 1), (1, 2, 3, 128, 0), (2, 63, 2, 64, 1), (1, 64, 2, 128, 1), (1, 65, 1, 64, 0),
+         (2, 127, 1, 128, 1), (1, 128, 2, 64, 1), (1, 129, 2, 128, 0), (3, 200, 2, 64, 1), (1, 300, 3, 128, 1),
+         (1, 257, 1, 64, 0), (1, 513, 1, 128, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", SWEEP, ids=lambda s: "x".join(map(str, s)))
+def test_shape_sweep(shape, dtype):
+    B, S, H, D, causal = shape
+    seed = 1300 + B * 7 + S * 3 + H + D + causal
+    _full(W.AttnCase(f"sweep-{B}x{S}x{H}x{D}-c{causal}-{dtype}", B, S, H, D, causal=causal, dtype=dtype, seed=seed),
+          guard=2048)
+
+
+def test_explicit_scale_and_flat_keys():
+    """K = 0 gives the prefix mean of V (causal) whatever the scale; a large explicit
+    scale on random keys makes the softmax nearly one-hot."""
+    _full(W.AttnCase("flat-keys", 2, 333, 2, 64, causal=1, dist="uniform_keys", scale=5.0, seed=1401))
+    _full(W.AttnCase("sharp", 1, 300, 2, 128, causal=0, scale=1.0, seed=1402))
+    _full(W.AttnCase("sharp-bf16", 1, 300, 2, 64, causal=1, scale=0.9, dtype="bf16", seed=1403))
+
+
+def test_deterministic():
+    case = W.ATTN_CONFIGS["fa1"].with_(name="attn-determinism", B=2, S=640)
+    q, k, v = W.make_attn_inputs(case)
+    a = _run(case, q, k, v)
+    b = _run(case, q, k, v)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_error_paths_enqueue_nothing():
+    import tiled_dense_gemm_02_amd as tlg
+    dev = _device()
+    x = torch.zeros((1, 64, 2, 64), dtype=torch.float16, device=dev)
+    o = torch.full_like(x, 3.0)
+    p, po = x.data_ptr(), o.data_ptr()
+    assert tlg.attention_ptrs(p + 8, p, p, po, 1, 32, 2, 64, torch.float16, 1, 0.125) == -4     # misaligned
+    assert tlg.attention_ptrs(p, p, p, p, 1, 64, 2, 64, torch.float16, 1, 0.125) == -1          # O overlaps Q
+    assert tlg.attention_ptrs(p, p, p, po, 1, 64, 2, 96, torch.float16, 1, 0.125) == -2         # dim 96
+    torch.cuda.synchronize()
+    assert bool((o == 3.0).all())

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import contextlib
 import ctypes
+import math
 import os
 import threading
 
@@ -88,6 +89,8 @@ def load_library():
         lib.tlg_gemm_tune.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp,
                                       vp, i32, ctypes.POINTER(TuneResult), i32, ctypes.POINTER(i32)]
         lib.tlg_gemm_tune.restype = i32
+        lib.tlg_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_float, vp]
+        lib.tlg_attn_fwd.restype = i32
         lib.tlg_gemm_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         lib.tlg_gemm_query.restype = i32
         lib.tlg_gemm_describe.argtypes = [vp]
@@ -320,3 +323,45 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, *, tra
                         clear_accum=clear_accum, epilogue=epilogue, variant=variant)
         _plan_cache[key] = plan
     return plan.run(A, B, C)
+
+
+def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor | None = None, *,
+              causal: bool = True, scale: float | None = None, stream=None) -> torch.Tensor:
+    """Attention forward with online softmax (tlg_attn_fwd) on [batch, seq, heads, dim]
+    device tensors of fp16 or bf16 (dim 64 or 128).  scale defaults to 1/sqrt(dim).
+    Returns O (allocated when not given)."""
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor, got {t.device}")
+        if t.dim() != 4 or tuple(t.shape) != tuple(Q.shape):
+            raise ValueError(f"{name} must be [batch, seq, heads, dim] like Q, got {tuple(t.shape)}")
+        if t.dtype != Q.dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, Q has {Q.dtype}")
+        if t.numel() and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if O is None:
+        O = torch.empty_like(Q)
+    if tuple(O.shape) != tuple(Q.shape) or O.dtype != Q.dtype or (O.numel() and not O.is_contiguous()):
+        raise ValueError("O must be a contiguous tensor of Q's shape and dtype")
+    B, S, H, D = Q.shape
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lib = load_library()
+    with torch.cuda.device(Q.device):
+        st = lib.tlg_attn_fwd(Q.data_ptr() or None, K.data_ptr() or None, V.data_ptr() or None,
+                              O.data_ptr() or None, B, S, H, D, _code(Q.dtype), int(bool(causal)), sc,
+                              ctypes.c_void_p(s))
+    if st != 0:
+        raise TlgError("tlg_attn_fwd", st)
+    return O
+
+
+def attention_ptrs(q: int, k: int, v: int, o: int, batch: int, seq: int, heads: int, dim: int, dtype, causal: int,
+                   scale: float, stream_handle: int = 0) -> int:
+    """Raw-pointer form of attention (no checks beyond the library's own); returns the status."""
+    return load_library().tlg_attn_fwd(q or None, k or None, v or None, o or None, batch, seq, heads, dim,
+                                       _code(dtype), int(causal), float(scale), ctypes.c_void_p(stream_handle))

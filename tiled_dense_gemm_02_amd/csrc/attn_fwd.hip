@@ -1,0 +1,24 @@
+// Instances of the attention-forward kernel: dim 64 / 128, fp16 / bf16, causal or not.
+#include "attn_fwd.hpp"
+
+namespace tlg {
+
+template <int D, int T>
+static hipError_t launch_attn_t(const AttnParams& p, int causal, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(p.nqb * p.H * p.B)), block(256);
+    if (causal)
+        hipLaunchKernelGGL((attn_fwd_kernel<D, T, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_kernel<D, T, false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnParams& p, int dim, int dtype, int causal, hipStream_t stream)
+{
+    if (dim == 64)
+        return dtype == DT_F16 ? launch_attn_t<64, DT_F16>(p, causal, stream) : launch_attn_t<64, DT_BF16>(p, causal, stream);
+    return dtype == DT_F16 ? launch_attn_t<128, DT_F16>(p, causal, stream) : launch_attn_t<128, DT_BF16>(p, causal, stream);
+}
+
+}  // namespace tlg

@@ -1,0 +1,274 @@
+// Attention forward with online softmax (FlashAttention), on the same building
+// blocks as the GEMM kernels: the tile program of the handbook page "TileLang: a
+// tile language one level below Triton", section "FlashAttention: online softmax
+// as tile code".  One workgroup owns a block of queries of one (batch, head),
+// walks the keys in blocks, and per block
+//   scores = Q K^T (fp32), scaled by scale * log2(e), masked;
+//   m_new  = max(m_old, row max of the block);   alpha = exp2(m_old - m_new);
+//   P      = exp2(scores - m_new), rounded to the operand type;
+//   l      = l * alpha + row sum of P;   O = O * alpha + P V;
+// and finally O / l is rounded to the operand type and stored.  The causal rule
+// is the page's: the query at position i sees the keys at positions j <= i; key
+// blocks wholly to the right of a query block are never visited.
+//
+// Tensors Q, K, V and O are [batch, seq, heads, dim], dim 64 or 128, fp16 or
+// bf16, 16-byte aligned; element (b, t, h, d) sits at ((b*S + t)*H + h)*D + d.
+//
+// gfx950 mapping.
+//   - Workgroup: 4 waves, 128 queries (32 per wave: two 16-row MFMA tiles).  Q
+//     fragments are loaded once into registers.  Key blocks of 64 keys (K and V
+//     tiles) stream through a two-slot LDS ring filled by global->LDS direct
+//     loads; the loads of block j+1 are in flight while block j is computed.
+//   - Both products run on v_mfma_f32_16x16x32 with the key-side operand first,
+//     so the score tile lands as S[q][key] with lane l holding query l%16 and
+//     keys 4(l/16)..+3 of each 16-key tile.  That is already the A-operand
+//     layout of the P V product once the keys of two adjacent 16-key tiles are
+//     taken as one 32-wide K step in the order {4g..4g+3, 16+4g..16+4g+3}
+//     (g = l/16); the V fragment is read in the same key order, so P never
+//     leaves the registers.  Row statistics need a reduction over the four lanes
+//     that share a query (lanes l, l^16, l^32, l^48) only for the maximum; the
+//     row sum is kept per lane and reduced once at the end.
+//   - LDS layouts (row = one key, 2*dim bytes, 16-byte chunks):
+//       K: chunk c of row r at c ^ ((r / RPB) % CH)  -- a fragment read (16 rows
+//          of one chunk per 16 lanes) touches every bank once;
+//       V: chunk c of row r at c ^ 2((r / RPB) % (CH/2)) -- the transposing
+//          reads (ds_read_b64_tr_b16: 16 consecutive rows, 32 bytes each) spread
+//          over all banks; the XOR is even, so the two chunks a read needs stay
+//          adjacent;
+//     with CH = dim/8 chunks per row and RPB = rows per 256 bytes.
+//   - Grid: (query blocks) x heads x batch workgroups.  The query blocks of one
+//     (batch, head) go to one XCD (its L2 then holds that head's K and V), the
+//     causal ones heaviest first.
+#pragma once
+
+#include "gemm_lds.hpp"
+
+namespace tlg {
+
+template <int D>
+struct AttnLds {
+    static constexpr int RB = 2 * D;                    // bytes per key row
+    static constexpr int CH = D / 8;                    // 16-byte chunks per row
+    static constexpr int RPB = RB >= 256 ? 1 : 256 / RB;
+    static constexpr int RPK = 1024 / RB;               // rows per 1 KiB direct-load block
+    __device__ static int swz_k(int r) { return (r / RPB) % CH; }
+    __device__ static int swz_v(int r) { return 2 * ((r / RPB) % (CH / 2)); }
+};
+
+__device__ inline float wave_max4(float x)
+{
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ inline float wave_sum4(float x)
+{
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+template <int T>
+__device__ inline float round_op(float x, uint32_t& bits)
+{
+    if constexpr (T == DT_F16) {
+        const _Float16 h = (_Float16)x;
+        bits = __builtin_bit_cast(uint16_t, h);
+        return (float)h;
+    } else {
+        const __bf16 h = (__bf16)x;
+        bits = __builtin_bit_cast(uint16_t, h);
+        return (float)h;
+    }
+}
+
+template <int D, int T, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
+{
+    constexpr int BM = 128, BN = 64, NW = 4, WROWS = 32;
+    using Lay = AttnLds<D>;
+    constexpr int RB = Lay::RB, CH = Lay::CH, RPK = Lay::RPK;
+    constexpr int TILE = BN * RB;                 // bytes of one K (or V) tile
+    constexpr int SLOT = 2 * TILE;
+    constexpr int LK = TILE / (NW * 1024);        // direct loads per lane per tile
+    constexpr int KS = D / 32;                    // MFMA K steps of the score product
+    constexpr int DT = D / 16;                    // 16-wide output column tiles
+    static_assert(TILE % (NW * 1024) == 0 && LK >= 1, "tile must split into 1 KiB blocks per wave");
+    static_assert(2 * SLOT <= 64 * 1024, "two slots per workgroup, two workgroups per CU");
+
+    __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+
+    // Work item: (batch, head, query block).
+    const int total = p.nqb * p.H * p.B;
+    int id = blockIdx.x;
+    if (total % kXcds == 0) id = (id % kXcds) * (total / kXcds) + id / kXcds;
+    const int bh = id / p.nqb;
+    const int qi = id - bh * p.nqb;
+    const int qb = CAUSAL ? p.nqb - 1 - qi : qi;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int S = p.S;
+    const int q0 = qb * BM;
+    const uint32_t stride = (uint32_t)p.H * (uint32_t)RB;            // bytes between consecutive positions
+    const uint64_t head_off = ((uint64_t)b * (uint64_t)S * (uint64_t)p.H + (uint64_t)h) * (uint64_t)RB;
+    const uint64_t head_bytes = (uint64_t)(S - 1) * stride + RB;    // up to the end of position S-1
+
+    const int q_last = min(q0 + BM, S) - 1;
+    const int nkb = CAUSAL ? q_last / BN + 1 : (S + BN - 1) / BN;
+
+    // Q fragments of this wave's 32 rows (rows past S read as zeros).
+    u32x4 qf[2][KS];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.Q + head_off, head_bytes);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int q = q0 + wave * WROWS + rt * 16 + r16;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint32_t off = q < S ? (uint32_t)q * stride + (uint32_t)(ks * 4 + g) * 16u : kOOB;
+                qf[rt][ks] = buf_load16(rq, off);
+            }
+        }
+    }
+
+    // Direct loads: load i of this lane fills row r0 + 4 i RPK of a tile, chunk
+    // position lane % CH; the swizzle of that row is the same for every i.
+    const int r0 = wave * RPK + lane / CH;
+    const int ck = (lane % CH) ^ Lay::swz_k(r0);
+    const int cv = (lane % CH) ^ Lay::swz_v(r0);
+    const i32x4 rk = rsrc_words((const char*)p.K + head_off, head_bytes);
+    const i32x4 rv = rsrc_words((const char*)p.V + head_off, head_bytes);
+    const uint32_t lds0 = lds_addr_of(smem);
+    auto issue = [&](int kb) {
+        const uint32_t slot = lds0 + (uint32_t)((kb & 1) * SLOT) + (uint32_t)wave * 1024u;
+#pragma unroll
+        for (int i = 0; i < LK; ++i) {
+            const int key = kb * BN + r0 + i * NW * RPK;
+            const uint32_t base = (uint32_t)key * stride;
+            dma16(rk, key < S ? base + (uint32_t)ck * 16u : kOOB,
+                  __builtin_amdgcn_readfirstlane(slot + (uint32_t)(i * NW * 1024)));
+            dma16(rv, key < S ? base + (uint32_t)cv * 16u : kOOB,
+                  __builtin_amdgcn_readfirstlane(slot + (uint32_t)(TILE + i * NW * 1024)));
+        }
+    };
+
+    f32x4 oacc[2][DT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+
+    const int wq0 = q0 + wave * WROWS;          // first query row of this wave
+    issue(0);
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        if (kb + 1 < nkb) issue(kb + 1);
+        const int kb0 = kb * BN;
+        // Under the causal rule a wave whose rows all precede the block sees none of it.
+        const bool active = !CAUSAL || kb0 <= wq0 + WROWS - 1;
+        if (active) {
+            const char* kt_base = smem + (kb & 1) * SLOT;
+            const char* vt_base = kt_base + TILE;
+
+            f32x4 sacc[2][4];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) sacc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt) {
+                    const int row = kt * 16 + r16;
+                    const int c = ks * 4 + g;
+                    const u32x4 kf = *(const u32x4*)(kt_base + row * RB + ((c ^ Lay::swz_k(row)) << 4));
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) sacc[rt][kt] = mfma16x16x32<T>(kf, qf[rt][ks], sacc[rt][kt]);
+                }
+            }
+
+            const bool need_mask = (kb0 + BN > S) || (CAUSAL && kb0 + BN - 1 > wq0);
+            u32x4 pf[2][2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const int q = wq0 + rt * 16 + r16;
+                float x[16];
+                float mloc = -INFINITY;
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float v = sacc[rt][kt][e] * p.scale_log2;
+                        if (need_mask) {
+                            const int key = kb0 + kt * 16 + 4 * g + e;
+                            if (key >= S || (CAUSAL && key > q)) v = -INFINITY;
+                        }
+                        x[kt * 4 + e] = v;
+                        mloc = fmaxf(mloc, v);
+                    }
+                mloc = wave_max4(mloc);
+                const float m_new = fmaxf(m_run[rt], mloc);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+                m_run[rt] = m_new;
+                float lsum = 0.f;
+                uint32_t bits[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) lsum += round_op<T>(__builtin_amdgcn_exp2f(x[t] - m_use), bits[t]);
+                l_run[rt] = l_run[rt] * alpha + lsum;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) oacc[rt][dt][e] *= alpha;
+                // K step kk of the P V product: keys {4g..4g+3} of tile 2kk, then of tile 2kk+1.
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    pf[rt][kk] = u32x4{bits[8 * kk + 0] | (bits[8 * kk + 1] << 16), bits[8 * kk + 2] | (bits[8 * kk + 3] << 16),
+                                       bits[8 * kk + 4] | (bits[8 * kk + 5] << 16), bits[8 * kk + 6] | (bits[8 * kk + 7] << 16)};
+            }
+
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int s = r16;
+                const int chunk = 2 * dt + ((s & 3) >> 1);
+                const int half = (s & 1) * 8;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int klo = kk * 32 + 4 * g + (s >> 2), khi = klo + 16;
+                    const u32x2 lo = lds_read_tr16(vt_base + klo * RB + ((chunk ^ Lay::swz_v(klo)) << 4) + half);
+                    const u32x2 hi = lds_read_tr16(vt_base + khi * RB + ((chunk ^ Lay::swz_v(khi)) << 4) + half);
+                    const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) oacc[rt][dt] = mfma16x16x32<T>(vf, pf[rt][kk], oacc[rt][dt]);
+                }
+            }
+        }
+        // The next block has landed (this lane's loads) and every wave is done
+        // with this slot (the barrier), so the slot can be refilled.
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+
+    // Epilogue: O / l, rounded to the operand type; lane holds four consecutive dims.
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int q = wq0 + rt * 16 + r16;
+        const float inv = 1.0f / wave_sum4(l_run[rt]);
+        if (q >= S) continue;
+        char* orow = (char*)p.O + head_off + (uint64_t)q * stride;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            uint32_t hb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) round_op<T>(oacc[rt][dt][e] * inv, hb[e]);
+            *(u32x2*)(orow + (dt * 16 + 4 * g) * 2) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        }
+    }
+}
+
+}  // namespace tlg

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -456,6 +457,37 @@ tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const
     mp.tiles_m = (int)ceil_div(p.M, 256);
     mp.tiles_n = (int)ceil_div(p.N, 256);
     const hipError_t err = launch_mx(mp, p.ab == TLG_E4M3 ? 0 : 1, (hipStream_t)stream);
+    return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
+tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t seq,
+                        int64_t heads, int64_t dim, int32_t dtype, int32_t causal, float softmax_scale, void* stream)
+{
+    if (batch < 0 || seq < 0 || heads < 0 || dim <= 0) return TLG_ERR_INVALID_ARG;
+    if (!flag_ok(causal) || !std::isfinite(softmax_scale)) return TLG_ERR_INVALID_ARG;
+    if (dtype != TLG_F16 && dtype != TLG_BF16) {
+        if (dtype == TLG_F32 || dtype == TLG_E4M3 || dtype == TLG_E5M2) return TLG_ERR_UNSUPPORTED;
+        return TLG_ERR_INVALID_ARG;
+    }
+    if (dim != 64 && dim != 128) return TLG_ERR_UNSUPPORTED;
+    if (batch == 0 || seq == 0 || heads == 0) return TLG_OK;
+    constexpr int64_t kBlockQ = 128;
+    const uint64_t per_batch = (uint64_t)seq * (uint64_t)heads * (uint64_t)dim * 2u;
+    if (per_batch >= (uint64_t(1) << 31)) return TLG_ERR_UNSUPPORTED;
+    const int64_t nqb = ceil_div(seq, kBlockQ);
+    if (batch > INT32_MAX || nqb * heads > INT32_MAX || nqb * heads * batch > INT32_MAX) return TLG_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !O) return TLG_ERR_NULL;
+    const uintptr_t q = (uintptr_t)Q, k = (uintptr_t)K, v = (uintptr_t)V, o = (uintptr_t)O;
+    if ((q | k | v | o) % 16) return TLG_ERR_MISALIGNED;
+    const uint64_t bytes = per_batch * (uint64_t)batch;
+    if (ranges_overlap(o, bytes, q, bytes) || ranges_overlap(o, bytes, k, bytes) || ranges_overlap(o, bytes, v, bytes))
+        return TLG_ERR_INVALID_ARG;
+    AttnParams ap{};
+    ap.Q = Q; ap.K = K; ap.V = V; ap.O = O;
+    ap.B = (int)batch; ap.S = (int)seq; ap.H = (int)heads;
+    ap.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);   // log2(e)
+    ap.nqb = (int)nqb;
+    const hipError_t err = launch_attn(ap, (int)dim, dtype == TLG_F16 ? DT_F16 : DT_BF16, causal, (hipStream_t)stream);
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }
 

@@ -110,4 +110,17 @@ struct MxParams {
 };
 hipError_t launch_mx(const MxParams& p, int fmt, hipStream_t stream);   // fmt: 0 = E4M3, 1 = E5M2
 
+// Attention forward (attn_fwd.hip).  Q, K, V, O are [B, S, H, dim] (dim 64 or 128),
+// fp16 or bf16, 16-byte aligned; S >= 1; S * H * dim * 2 < 2^31.
+struct AttnParams {
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* O;
+    int B, S, H;
+    float scale_log2;   // softmax scale * log2(e)
+    int nqb;            // query blocks of 128 per (batch, head)
+};
+hipError_t launch_attn(const AttnParams& p, int dim, int dtype, int causal, hipStream_t stream);
+
 }  // namespace tlg
