@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import tiled_dense_gemm_02_amd as tlg
 
@@ -259,3 +260,27 @@ def test_block_scaled_plans():
     hh = ctypes.c_void_p()
     assert lib.tlg_gemm_tune(ctypes.byref(hh), 256, 256, 256, E4M3, 1, 0, 1, 1, 0, 4096, 8192, 16384, None, 3,
                              None, 0, None) == UNSUPPORTED
+
+
+def test_attention_validation_happens_before_any_launch():
+    """tlg_attn_fwd rejects bad requests with distinct statuses before touching a device
+    (these pointers are never dereferenced)."""
+    lib = tlg.load_library()
+    f = lib.tlg_attn_fwd
+    p = 1 << 20                                         # 16-byte aligned fake address
+    ok = (p, p + (1 << 24), p + (2 << 24), p + (3 << 24))
+    assert f(*ok, -1, 64, 2, 64, 1, 1, 0.125, None) == -1        # negative batch
+    assert f(*ok, 1, 64, 2, 0, 1, 1, 0.125, None) == -1          # dim 0
+    assert f(*ok, 1, 64, 2, 64, 1, 2, 0.125, None) == -1         # causal flag
+    assert f(*ok, 1, 64, 2, 64, 1, 1, float("nan"), None) == -1  # scale
+    assert f(*ok, 1, 64, 2, 64, 9, 1, 0.125, None) == -1         # unknown dtype
+    assert f(*ok, 1, 64, 2, 64, 3, 1, 0.125, None) == -2         # fp32 operands
+    assert f(*ok, 1, 64, 2, 64, 4, 1, 0.125, None) == -2         # FP8 operands
+    assert f(*ok, 1, 64, 2, 96, 1, 1, 0.125, None) == -2         # dim 96
+    assert f(*ok, 1, 1 << 22, 64, 128, 1, 1, 0.125, None) == -2  # 2^31 bytes per batch
+    assert f(None, None, None, None, 0, 64, 2, 64, 1, 1, 0.125, None) == 0   # empty: nothing to do
+    assert f(None, p, p, p, 1, 64, 2, 64, 1, 1, 0.125, None) == -3
+    assert f(p + 8, ok[1], ok[2], ok[3], 1, 64, 2, 64, 1, 1, 0.125, None) == -4
+    assert f(p, ok[1], ok[2], p + 4096, 1, 64, 2, 64, 1, 1, 0.125, None) == -1   # O overlaps Q
+    with pytest.raises(ValueError):
+        tlg.attention(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
