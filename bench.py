@@ -46,7 +46,9 @@ KERNEL_SOURCES = {
     7: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     8: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     9: ["gemm_mx.hpp", "gemm_mx.hip", "gemm_lds.hpp", "tlg_device.hpp"],
+    "attn": ["attn_fwd.hpp", "attn_fwd.hip", "gemm_lds.hpp", "tlg_device.hpp"],
 }
+ATTN_VARIANT = "attn"
 
 
 def kernel_hash(variant: int) -> str:
@@ -75,7 +77,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     # ~40 ms of launches: the clock settles only after tens of ms of MFMA load
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c5a", help="c1..c5b, or a block-scaled workload mx1..mx3")
+    ap.add_argument("--workload", default="c5a", help="c1..c5b, a block-scaled workload mx1..mx3, "
+                    "or an attention workload fa1..fa4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -200,6 +203,61 @@ def measure_mx(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=
             "nsets": nsets}
 
 
+def measure_attn(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=0.0):
+    """measure() for an attention-forward workload (tlg_attn_fwd)."""
+    import torch
+    import tiled_dense_gemm_02_amd as tlg
+    import tlg_workloads as W
+
+    dev = torch.device("cuda:0")
+    q, k, v = W.make_attn_inputs(case)
+    nsets = max(1, min(8, math.ceil(rotate_bytes / max(3 * q.numel() * 2, 1))))
+    sets = [tuple(x.to(dev) for x in (q, k, v)) for _ in range(nsets)]
+    O = torch.empty_like(sets[0][0])
+    stream = torch.cuda.current_stream(dev)
+    tlg.attention(*sets[0], O, causal=bool(case.causal), scale=case.scale, stream=stream)
+    ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
+    o_ptr, sh = O.data_ptr(), stream.cuda_stream
+    sc = case.softmax_scale
+    status = 0
+
+    def launch(i):
+        qp, kp, vp = ptrs[i % nsets]
+        return tlg.attention_ptrs(qp, kp, vp, o_ptr, case.B, case.S, case.H, case.D, q.dtype, case.causal, sc, sh)
+
+    for i in range(warmup):
+        status |= launch(i)
+    torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for i in range(20):
+            status |= launch(i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        per = max(w0.elapsed_time(w1) / 20, 1e-3)
+        for i in range(int(math.ceil(max(0.0, min_warm_ms - 20 * per) / per))):
+            status |= launch(i)
+        torch.cuda.synchronize()
+    if log:
+        log(f"[bench] {case.name}: attention B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} "
+            f"sets={nsets}")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        status |= launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError(f"tlg_attn_fwd failed during the timed launches (status {status})")
+    return {"ms": start.elapsed_time(end) / steps, "wall_s": time.perf_counter() - t0, "C": O, "nsets": nsets,
+            "describe": f"attn_fwd block=128x64 threads=256 dim={case.D} causal={case.causal} dtype={case.dtype}"}
+
+
 def plan_out_dtype(case):
     import torch
     return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.c]
@@ -252,6 +310,54 @@ def cpu_baseline_mx(case, C_gpu, rows):
             "seconds": dt, "sample_matches_gpu": ok}
 
 
+def cpu_baseline_attn(case, O_gpu, positions):
+    """cpu_baseline() for an attention workload: the attention oracle on the last
+    `positions` query positions of every (batch, head)."""
+    import numpy as np
+    import tlg_workloads as W
+    from oracle import build_oracle, oracle as O
+    if not os.path.exists(O.LIB_PATH):
+        build_oracle.build()
+    q, k, v = W.make_attn_inputs(case)
+    nthreads = min(os.cpu_count() or 1, 16)
+    i0 = case.S - positions
+    t0 = time.perf_counter()
+    o = O.attn(case.B, case.S, case.H, case.D, W.bits16(q), W.bits16(k), W.bits16(v), dtype=case.dtype,
+               causal=case.causal, scale=case.softmax_scale, rows=(i0, case.S), nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    keys = sum(i + 1 for i in range(i0, case.S)) if case.causal else positions * case.S
+    flops = 4.0 * case.D * keys * case.B * case.H
+    gpu = O_gpu[:, i0:].float().cpu().numpy().astype(np.float64)
+    ok = bool((np.abs(gpu - o) <= O.attn_tolerance(o, float(v.float().abs().max()), case.dtype)).all())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"last {positions} of {case.S} query positions of every batch and head of {case.name} "
+                      f"({flops / 1e9:.1f} GFLOP, fp64 loops, {dt:.1f} s)",
+            "seconds": dt, "sample_matches_gpu": ok}
+
+
+def bench_attn(args, case, log):
+    """The JSON line of an attention-forward workload (MFMA-bound: both products run on
+    the matrix cores; the algorithmic work is 4 * dim FLOPs per allowed query-key pair)."""
+    r = measure_attn(case, args.steps, args.warmup, log=log, min_warm_ms=100.0)
+    ms = r["ms"]
+    tflops = case.flops / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": tflops, "peak": PEAK_TFLOPS[case.dtype], "unit": "TFLOP/s",
+            "frac": tflops / PEAK_TFLOPS[case.dtype], "traffic": stored_traffic(args.workload, ATTN_VARIANT),
+            "kernel": "attn_fwd", "per_launch": {"flops": case.flops, "algorithmic_bytes": case.algorithmic_bytes,
+                                                 "avg_kernel_ms": ms}}
+    out = {"metric": "attention forward TFLOP/s (fp16, fp32 accumulate) and % of MFMA peak", "value": tflops,
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.dtype,
+           "data": "synthetic (seeded, see tlg_workloads.py)",
+           "config": {"workload": f"{case.name}: {case.note}", "batch": case.B, "seq": case.S, "heads": case.H,
+                      "dim": case.D, "causal": case.causal, "plan": r["describe"], "operand_sets_rotated": r["nsets"]},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        positions = {"fa1": 1024, "fa2": 777, "fa3": 32, "fa4": 64}[case.name]
+        out["cpu_baseline"] = cpu_baseline_attn(case, r["C"], positions)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -272,6 +378,9 @@ def main():
         log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
         del x, y
 
+    if args.workload in W.ATTN_CONFIGS:
+        print(json.dumps(bench_attn(args, W.ATTN_CONFIGS[args.workload], log)), flush=True)
+        return
     is_mx = args.workload in W.MX_CONFIGS
     case = W.MX_CONFIGS[args.workload] if is_mx else W.CONFIGS[args.workload]
     r = (measure_mx if is_mx else measure)(case, args.steps, args.warmup, log=log)
@@ -306,16 +415,18 @@ def main():
 
     if not args.no_secondary:
         sec = []
-        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3"):
+        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3", "fa3"):
             if name == args.workload:
                 continue
-            sec_mx = name in W.MX_CONFIGS
-            c2 = W.MX_CONFIGS[name] if sec_mx else W.CONFIGS[name]
-            rr = (measure_mx if sec_mx else measure)(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
+            sec_mx, sec_attn = name in W.MX_CONFIGS, name in W.ATTN_CONFIGS
+            c2 = W.MX_CONFIGS[name] if sec_mx else W.ATTN_CONFIGS[name] if sec_attn else W.CONFIGS[name]
+            fn = measure_mx if sec_mx else measure_attn if sec_attn else measure
+            rr = fn(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
             t = rr["ms"] * 1e-3
             entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
-                     "GB/s": c2.algorithmic_bytes / t / 1e9, "plan": rr["plan"].describe()}
-            entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.fmt if sec_mx else c2.ab]
+                     "GB/s": c2.algorithmic_bytes / t / 1e9,
+                     "plan": rr["describe"] if sec_attn else rr["plan"].describe()}
+            entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.fmt if sec_mx else c2.dtype if sec_attn else c2.ab]
             entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS
             sec.append(entry)
             del rr
