@@ -106,6 +106,14 @@ def test_explicit_scale_and_flat_keys():
     _full(W.AttnCase("sharp-bf16", 1, 300, 2, 64, causal=1, scale=0.9, dtype="bf16", seed=1403))
 
 
+@pytest.mark.parametrize("scale", [-0.3, -2.0, 0.0])
+def test_negative_and_zero_scale(scale):
+    """A negative scale turns the row maximum of the scaled scores into the scale times the
+    row minimum of the raw scores; a zero scale gives every allowed key the same weight."""
+    _full(W.AttnCase(f"scale{scale}", 1, 333, 2, 128, causal=1, scale=scale, seed=1410))
+    _full(W.AttnCase(f"scale{scale}-d64-full", 2, 200, 1, 64, causal=0, scale=scale, dtype="bf16", seed=1411))
+
+
 def test_deterministic():
     case = W.ATTN_CONFIGS["fa1"].with_(name="attn-determinism", B=2, S=640)
     q, k, v = W.make_attn_inputs(case)

@@ -61,10 +61,26 @@ __device__ inline float wave_max4(float x)
     return fmaxf(x, __shfl_xor(x, 32));
 }
 
-__device__ inline float wave_sum4(float x)
+__device__ inline float wave_min4(float x)
 {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    x = fminf(x, __shfl_xor(x, 16));
+    return fminf(x, __shfl_xor(x, 32));
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even in the operand type, packed (one
+// v_cvt_pk_{f16,bf16}_f32 on gfx950).
+template <int T>
+__device__ inline uint32_t pack_op(float a, float b)
+{
+    const f32x2 v = {a, b};
+    if constexpr (T == DT_F16)
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <int T>
@@ -81,7 +97,9 @@ __device__ inline float round_op(float x, uint32_t& bits)
     }
 }
 
-template <int D, int T, bool CAUSAL>
+// NEG: the softmax scale is negative (the row maximum of the scaled scores is
+// then the scale times the row minimum of the raw scores).
+template <int D, int T, bool CAUSAL, bool NEG>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 {
     constexpr int BM = 128, BN = 64, NW = 4, WROWS = 32;
@@ -154,12 +172,20 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
     };
 
     f32x4 oacc[2][DT];
+    f32x4 lacc[2];                       // row sums of P (all four entries equal)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 2; ++rt) {
+        lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    // All-ones operand: P times it gives the row sums of the rounded P on the
+    // matrix cores, exactly as the page sums its fp16 probability tile.
+    const uint32_t one2 = T == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
+    const u32x4 ones = u32x4{one2, one2, one2, one2};
+    const float c = p.scale_log2;
+    constexpr float SENT = NEG ? INFINITY : -INFINITY;   // masked raw score, ignored by the row extreme
 
     const int wq0 = q0 + wave * WROWS;          // first query row of this wave
     issue(0);
@@ -194,43 +220,65 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 
             const bool need_mask = (kb0 + BN > S) || (CAUSAL && kb0 + BN - 1 > wq0);
             u32x4 pf[2][2];
+            float alpha[2];
+            bool rescale = false;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 const int q = wq0 + rt * 16 + r16;
-                float x[16];
-                float mloc = -INFINITY;
+                // Score t of this lane is key kb0 + 4g + 16(t/4) + t%4; it is masked
+                // when that key lies past the row's last allowed key.
+                const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - (kb0 + 4 * g);
+                float sv[16];
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float v = sacc[rt][kt][e] * p.scale_log2;
-                        if (need_mask) {
-                            const int key = kb0 + kt * 16 + 4 * g + e;
-                            if (key >= S || (CAUSAL && key > q)) v = -INFINITY;
-                        }
-                        x[kt * 4 + e] = v;
-                        mloc = fmaxf(mloc, v);
-                    }
-                mloc = wave_max4(mloc);
-                const float m_new = fmaxf(m_run[rt], mloc);
+                    for (int e = 0; e < 4; ++e) sv[kt * 4 + e] = sacc[rt][kt][e];
+                if (need_mask) {          // uniform: only the diagonal and the last key block
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) sv[t] = (t >> 2) * 16 + (t & 3) > lim ? SENT : sv[t];
+                }
+                // Row maximum of the scaled scores, from the raw scores: the scale
+                // is applied once per row, and once per score inside the FMA below.
+                float mloc = sv[0];
+#pragma unroll
+                for (int t = 1; t < 16; ++t) mloc = NEG ? fminf(mloc, sv[t]) : fmaxf(mloc, sv[t]);
+                mloc = NEG ? wave_min4(mloc) : wave_max4(mloc);
+                const float mblk = mloc == SENT ? -INFINITY : mloc * c;
+                const float m_new = fmaxf(m_run[rt], mblk);
                 const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+                alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
+                rescale = rescale || alpha[rt] != 1.0f;
                 m_run[rt] = m_new;
-                float lsum = 0.f;
-                uint32_t bits[16];
+                float pv[16];
 #pragma unroll
-                for (int t = 0; t < 16; ++t) lsum += round_op<T>(__builtin_amdgcn_exp2f(x[t] - m_use), bits[t]);
-                l_run[rt] = l_run[rt] * alpha + lsum;
+                for (int t = 0; t < 16; ++t) pv[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t], c, -m_use));
+                if (need_mask) {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) oacc[rt][dt][e] *= alpha;
+                    for (int t = 0; t < 16; ++t) pv[t] = (t >> 2) * 16 + (t & 3) > lim ? 0.f : pv[t];
+                }
                 // K step kk of the P V product: keys {4g..4g+3} of tile 2kk, then of tile 2kk+1.
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    pf[rt][kk] = u32x4{bits[8 * kk + 0] | (bits[8 * kk + 1] << 16), bits[8 * kk + 2] | (bits[8 * kk + 3] << 16),
-                                       bits[8 * kk + 4] | (bits[8 * kk + 5] << 16), bits[8 * kk + 6] | (bits[8 * kk + 7] << 16)};
+                    pf[rt][kk] = u32x4{pack_op<T>(pv[8 * kk + 0], pv[8 * kk + 1]), pack_op<T>(pv[8 * kk + 2], pv[8 * kk + 3]),
+                                       pack_op<T>(pv[8 * kk + 4], pv[8 * kk + 5]), pack_op<T>(pv[8 * kk + 6], pv[8 * kk + 7])};
             }
+            // O and the row sums are rescaled only when some row's maximum moved
+            // (alpha is exactly 1 otherwise).
+            if (__any(rescale)) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lacc[rt][e] *= alpha[rt];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) oacc[rt][dt][e] *= alpha[rt];
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) lacc[rt] = mfma16x16x32<T>(ones, pf[rt][kk], lacc[rt]);
 
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
@@ -258,7 +306,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int q = wq0 + rt * 16 + r16;
-        const float inv = 1.0f / wave_sum4(l_run[rt]);
+        const float inv = 1.0f / lacc[rt][0];
         if (q >= S) continue;
         char* orow = (char*)p.O + head_off + (uint64_t)q * stride;
 #pragma unroll
