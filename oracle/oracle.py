@@ -48,6 +48,12 @@ class Oracle:
         lib.oracle_mx_decode.argtypes = [i32, vp, i64, vp]
         lib.oracle_mx_decode.restype = i32
         f64 = ctypes.c_double
+        lib.oracle_w4_dequant.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp]
+        lib.oracle_w4_dequant.restype = i32
+        lib.oracle_w4gemm_rows.argtypes = [i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, i64, i64, vp]
+        lib.oracle_w4gemm_rows.restype = i32
+        lib.oracle_w4gemm_points.argtypes = [i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, i64, vp, vp, vp]
+        lib.oracle_w4gemm_points.restype = i32
         lib.oracle_attn_rows.argtypes = [i64, i64, i64, i64, i32, i32, f64, vp, vp, vp, i64, i64, vp, i32]
         lib.oracle_attn_rows.restype = i32
         lib.oracle_attn_points.argtypes = [i64, i64, i64, i64, i32, i32, f64, vp, vp, vp, i64, vp, vp, vp, vp]
@@ -142,6 +148,37 @@ class Oracle:
                                          out.ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle_attn_points failed with {rc}")
+        return out
+
+    def w4_dequant(self, N, K, G, Wq, S_bits, Z, *, dtype="f16") -> np.ndarray:
+        """Dequantized 4-bit weights w(n, k) as an [N, K] float64 array."""
+        Wq, Z, S = _u8(Wq), _u8(Z), _u16(S_bits)
+        out = np.empty((N, K), dtype=np.float64)
+        rc = self.lib.oracle_w4_dequant(N, K, G, _code(dtype), _ptr(Wq), _ptr(S), _ptr(Z), out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_w4_dequant failed with {rc}")
+        return out
+
+    def w4gemm(self, M, N, K, G, A_bits, Wq, S_bits, Z, *, dtype="f16", relu=0, rows=None) -> np.ndarray:
+        """Dequant GEMM o(m, n) = act(sum_k a(m,k) w(n,k)) in float64 for rows=(m0, m1) (default all)."""
+        A, Wq, Z, S = _u16(A_bits), _u8(Wq), _u8(Z), _u16(S_bits)
+        m0, m1 = (0, M) if rows is None else rows
+        out = np.empty((m1 - m0, N), dtype=np.float64)
+        rc = self.lib.oracle_w4gemm_rows(M, N, K, G, _code(dtype), int(relu), _ptr(A), _ptr(Wq), _ptr(S), _ptr(Z),
+                                         m0, m1, out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_w4gemm_rows failed with {rc}")
+        return out
+
+    def w4gemm_points(self, M, N, K, G, A_bits, Wq, S_bits, Z, ms, ns, *, dtype="f16", relu=0) -> np.ndarray:
+        A, Wq, Z, S = _u16(A_bits), _u8(Wq), _u8(Z), _u16(S_bits)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_w4gemm_points(M, N, K, G, _code(dtype), int(relu), _ptr(A), _ptr(Wq), _ptr(S), _ptr(Z),
+                                           ms.shape[0], ms.ctypes.data, ns.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_w4gemm_points failed with {rc}")
         return out
 
     def mx_decode(self, bytes_, fmt) -> np.ndarray:
@@ -248,6 +285,18 @@ def attn(*args, **kw):
 
 def attn_points(*args, **kw):
     return default().attn_points(*args, **kw)
+
+
+def w4_dequant(*args, **kw):
+    return default().w4_dequant(*args, **kw)
+
+
+def w4gemm(*args, **kw):
+    return default().w4gemm(*args, **kw)
+
+
+def w4gemm_points(*args, **kw):
+    return default().w4gemm_points(*args, **kw)
 
 
 def attn_tolerance(o: np.ndarray, vmax: float, dtype="f16") -> np.ndarray:

@@ -1,7 +1,8 @@
 /*
  * CPU oracle for the tiled dense GEMM  C = act(A·B)  — TEST INFRASTRUCTURE ONLY.
- * Further sections below hold the block-scaled (MX) GEMM and the attention
- * forward pass, each with its own statement of what it computes.
+ * Further sections below hold the block-scaled (MX) GEMM, the attention
+ * forward pass and the 4-bit dequant GEMM, each with its own statement of
+ * what it computes.
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
  * load this library.  It shares no code, header, table or helper with the HIP
@@ -561,5 +562,102 @@ int oracle_attn_points(int64_t B, int64_t S, int64_t H, int64_t D, int dtype, in
         attn_row(&j, pb[n], pi[n], ph[n], s, out + n * D);
     }
     free(s);
+    return 0;
+}
+
+/* ===========================================================================
+ * Dequant GEMM (the pages' table of representative operators, "dequant GEMM":
+ * load packed weights, apply scale and zero point, convert, then multiply).
+ * Weight format read here (the pages name the steps, not a format):
+ *   - W is N x K 4-bit unsigned codes q(n, k) in 0..15, stored [N, K/2] bytes;
+ *     the 8 codes of k = 8w .. 8w+7 of a row form one little-endian 32-bit word
+ *     (bytes 4w .. 4w+3 of the row), in which code k = 8w + j sits at bits
+ *     4*(j/2) .. +3 for even j and at bits 16 + 4*(j/2) .. +3 for odd j (even
+ *     codes in the low half-word, odd codes in the high half-word);
+ *   - per row n and group g of G consecutive k: a scale s(n, g) in the operand
+ *     dtype (fp16 / bf16 bits, [N, K/G]) and a zero point z(n, g) (uint8, [N, K/G]);
+ *   - the weight is the operand-type value nearest (ties to even) to
+ *     (q - z) * s; the multiplication then runs on those values:
+ *       c(m, n) = sum_k a(m, k) * w(n, k)      (double, ascending k)
+ *       o(m, n) = relu ? max(c, +0) : c
+ * ======================================================================== */
+static uint32_t w4_code(const uint8_t *row, int64_t k)
+{
+    const int64_t w = k / 8;
+    const int j = (int)(k % 8);
+    const uint32_t word = (uint32_t)row[4 * w] | ((uint32_t)row[4 * w + 1] << 8) |
+                          ((uint32_t)row[4 * w + 2] << 16) | ((uint32_t)row[4 * w + 3] << 24);
+    const int shift = (j % 2 == 0) ? 4 * (j / 2) : 16 + 4 * (j / 2);
+    return (word >> shift) & 15u;
+}
+
+static double w4_weight(int dt, const uint8_t *Wq, const uint16_t *S, const uint8_t *Z, int64_t K, int64_t G,
+                        int64_t n, int64_t k)
+{
+    const int64_t KG = K / G;
+    const double q = (double)w4_code(Wq + n * (K / 2), k);
+    const double z = (double)Z[n * KG + k / G];
+    const double s = dec(dt, S[n * KG + k / G]);
+    return dec(dt, enc(dt, (q - z) * s));
+}
+
+static int w4_args_ok(int64_t M, int64_t N, int64_t K, int64_t G, int dt)
+{
+    return M >= 0 && N >= 0 && K >= 0 && G > 0 && K % G == 0 && K % 8 == 0 &&
+           (dt == ORACLE_F16 || dt == ORACLE_BF16);
+}
+
+/* Dequantized weights w(n, k) as doubles, [N, K]. */
+int oracle_w4_dequant(int64_t N, int64_t K, int64_t G, int ab_dtype, const uint8_t *Wq, const uint16_t *S,
+                      const uint8_t *Z, double *out)
+{
+    if (!w4_args_ok(0, N, K, G, ab_dtype)) return -1;
+    if (N * K == 0) return 0;
+    if (!Wq || !S || !Z || !out) return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) out[n * K + k] = w4_weight(ab_dtype, Wq, S, Z, K, G, n, k);
+    return 0;
+}
+
+/* Output rows [m0, m1) of C = act(A W^T); A [M, K] 16-bit bits of ab_dtype. */
+int oracle_w4gemm_rows(int64_t M, int64_t N, int64_t K, int64_t G, int ab_dtype, int relu, const uint16_t *A,
+                       const uint8_t *Wq, const uint16_t *S, const uint8_t *Z, int64_t m0, int64_t m1, double *out)
+{
+    if (!w4_args_ok(M, N, K, G, ab_dtype) || m0 < 0 || m1 < m0 || m1 > M) return -1;
+    if (m1 == m0 || N == 0) return 0;
+    if (K > 0 && (!A || !Wq || !S || !Z)) return -1;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(N * (K > 0 ? K : 1)));
+    double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    if (!w || !arow) { free(w); free(arow); return -2; }
+    if (K > 0) oracle_w4_dequant(N, K, G, ab_dtype, Wq, S, Z, w);
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t k = 0; k < K; ++k) arow[k] = dec(ab_dtype, A[m * K + k]);
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            const double *wr = w + n * K;
+            for (int64_t k = 0; k < K; ++k) acc += arow[k] * wr[k];
+            if (relu && !(acc > 0.0)) acc = 0.0;
+            out[(m - m0) * N + n] = acc;
+        }
+    }
+    free(w); free(arow);
+    return 0;
+}
+
+/* The same definition at selected outputs (pm[i], pn[i]), dequantizing each weight where used. */
+int oracle_w4gemm_points(int64_t M, int64_t N, int64_t K, int64_t G, int ab_dtype, int relu, const uint16_t *A,
+                         const uint8_t *Wq, const uint16_t *S, const uint8_t *Z, int64_t npts, const int64_t *pm,
+                         const int64_t *pn, double *out)
+{
+    if (!w4_args_ok(M, N, K, G, ab_dtype) || npts < 0) return -1;
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t m = pm[i], n = pn[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) return -1;
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += dec(ab_dtype, A[m * K + k]) * w4_weight(ab_dtype, Wq, S, Z, K, G, n, k);
+        if (relu && !(acc > 0.0)) acc = 0.0;
+        out[i] = acc;
+    }
     return 0;
 }

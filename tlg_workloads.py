@@ -332,3 +332,106 @@ def sample_attn_rows(case: AttnCase, count: int, seed: int = 11):
     pi += list(rng.integers(0, case.S, extra))
     ph += list(rng.integers(0, case.H, extra))
     return tuple(np.asarray(x, dtype=np.int64) for x in (pb, pi, ph))
+
+
+# ---------------------------------------------------------------------------
+# Dequant GEMM with 4-bit weights (the pages' "dequant GEMM": packed weights,
+# scale / zero point, convert, multiply): C = act(A W^T) with A [M, K] in the
+# operand dtype and W given as 4-bit codes [N, K/2] bytes, scales [N, K/G] in
+# the operand dtype and zero points [N, K/G] uint8.  pack_w4 below is the one
+# writer of the packed layout (8 codes of k = 8w..8w+7 per little-endian 32-bit
+# word, even k in the low half-word at nibbles 0..3, odd k in the high
+# half-word at nibbles 4..7).
+#
+# Recipe (the pages give no quantizer; this is the usual asymmetric one):
+#   * the same seeded CPU generator draws A (uniform in [-1, 1)) and then the
+#     float weights (N(0, 1));
+#   * per row and group of G weights: s = (max - min) / 15 rounded to the
+#     operand dtype (1 when the group is constant), z = round(-min / s) clamped
+#     to 0..15, q = round(w / s) + z clamped to 0..15;
+#   * "smallint": A holds integers in [lo, hi], codes are uniform in 0..15,
+#     every scale is 1 and every zero point 8, so the weights are the integers
+#     q - 8 and the fp32 sums are exact.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class W4Case:
+    name: str
+    M: int
+    N: int
+    K: int
+    G: int = 128
+    ab: str = "f16"
+    c: str = "f16"
+    relu: int = 0
+    dist: str = "normal"     # "normal" | "smallint"
+    seed: int = 0
+    lo: int = -4
+    hi: int = 4
+    note: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """One read of A, the packed weights, scales and zero points; one write of C."""
+        sc = 4 if self.c == "f32" else 2
+        kg = self.K // self.G
+        return 2 * self.M * self.K + self.N * self.K // 2 + 3 * self.N * kg + sc * self.M * self.N
+
+    def with_(self, **kw) -> "W4Case":
+        return replace(self, **kw)
+
+
+W4_CONFIGS = {
+    "w4a": W4Case("w4a", 16, 16384, 8192, seed=1501,
+                  note="decode-shaped C = A W^T, 16 x 16384 x 8192, 4-bit weights in groups of 128, fp16"),
+    "w4b": W4Case("w4b", 5, 1000, 768, G=64, ab="bf16", c="f32", relu=1, seed=1502,
+                  note="ragged 5 x 1000 x 768, groups of 64, bf16 activations, fp32 out, ReLU"),
+    "w4c": W4Case("w4c", 40, 4096, 4096, G=32, c="bf16", seed=1503,
+                  note="40 x 4096 x 4096 (three 16-row tiles), groups of 32, fp16 in, bf16 out"),
+}
+
+
+def pack_w4(q: np.ndarray) -> np.ndarray:
+    """[N, K] codes in 0..15 -> [N, K/2] bytes in the packed layout described above."""
+    q = np.asarray(q, dtype=np.uint32)
+    N, K = q.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    g = q.reshape(N, K // 8, 8)
+    word = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):
+        shift = 4 * (j // 2) + (16 if j % 2 else 0)
+        word |= (g[:, :, j] & 15) << shift
+    return word.astype("<u4").view(np.uint8).reshape(N, K // 2)
+
+
+def make_w4_inputs(case: W4Case):
+    """CPU tensors: A [M, K] (operand dtype), Wq [N, K/2] uint8, S [N, K/G] (operand dtype),
+    Z [N, K/G] uint8; plus the codes [N, K] (uint8) for tests of the format."""
+    if case.K % case.G or case.K % 8:
+        raise ValueError("K must be a multiple of the group size and of 8")
+    g = torch.Generator().manual_seed(case.seed)
+    dt = DTYPES[case.ab]
+    N, K, G = case.N, case.K, case.G
+    if case.dist == "smallint":
+        A = torch.randint(case.lo, case.hi + 1, (case.M, K), generator=g).to(dt)
+        q = torch.randint(0, 16, (N, K), generator=g).to(torch.uint8)
+        S = torch.ones((N, K // G), dtype=dt)
+        Z = torch.full((N, K // G), 8, dtype=torch.uint8)
+    elif case.dist == "normal":
+        A = (torch.rand((case.M, K), generator=g) * 2.0 - 1.0).to(dt)
+        w = torch.randn((N, K), generator=g).reshape(N, K // G, G)
+        mn, mx = w.amin(dim=2), w.amax(dim=2)
+        s = ((mx - mn) / 15.0).to(dt)
+        s = torch.where(s.float() > 0, s, torch.ones_like(s))
+        sf = s.float()
+        z = torch.clamp(torch.round(-mn / sf), 0, 15)
+        q = torch.clamp(torch.round(w / sf.unsqueeze(2)) + z.unsqueeze(2), 0, 15).to(torch.uint8).reshape(N, K)
+        S, Z = s.contiguous(), z.to(torch.uint8).contiguous()
+    else:
+        raise ValueError(f"unknown distribution {case.dist!r}")
+    Wq = torch.from_numpy(pack_w4(q.numpy()))
+    return A.contiguous(), Wq.contiguous(), S.contiguous(), Z.contiguous(), q
