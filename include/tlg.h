@@ -262,6 +262,37 @@ tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, in
                         int64_t heads, int64_t dim, int32_t dtype, int32_t causal, float softmax_scale,
                         void *stream);
 
+/*
+ * Dequant GEMM with 4-bit weights: the "dequant GEMM" of the overview page's
+ * table of representative operators (load packed weights, apply scale and zero
+ * point, convert, then multiply).  Shaped for decoding (few rows of A, one
+ * stream of the weights per 16 rows of A).
+ *
+ * Value computed, for 0 <= m < M, 0 <= n < N:
+ *   w(n,k)   = convert_rne((q(n,k) - Z[n*(K/G) + k/G]) * S[n*(K/G) + k/G])   (operand dtype)
+ *   acc(m,n) = sum_k A[m*K + k] * w(n,k)                                   (fp32 accumulate)
+ *   C[m*N + n] = convert_rne(epilogue == RELU ? max(acc, +0) : acc)
+ * Weight format: q(n,k) in 0..15 are stored [N, K/2] bytes; the eight codes of
+ * k = 8j .. 8j+7 of row n form the little-endian 32-bit word at bytes 4j..4j+3 of
+ * the row, code k = 8j + i at bits 4*(i/2) .. +3 for even i and at bits
+ * 16 + 4*(i/2) .. +3 for odd i.  S [N, K/G] holds scales in the operand dtype, Z
+ * [N, K/G] zero points (uint8, any value 0..255).
+ *
+ * A [M, K], S and C are dense row-major.  ab_dtype (A and S) in {TLG_F16,
+ * TLG_BF16}; c_dtype in {TLG_F16, TLG_BF16, TLG_F32}; epilogue NONE or RELU.
+ * Limits: G a positive multiple of 32, K % G == 0, K / G <= 256, M and N <= 2^24.
+ * A and Wq must be 16-byte aligned, S 2-byte aligned, C aligned to its element.
+ * C must not overlap A, Wq, S or Z.
+ *
+ * Ownership as tlg_gemm_run: the caller owns all buffers; the call allocates
+ * nothing, does not synchronise and enqueues at most one kernel on `stream`.
+ * M == 0 or N == 0 enqueues nothing.  Errors: TLG_ERR_INVALID_ARG (sizes,
+ * enums, group, overlap), TLG_ERR_UNSUPPORTED (K / G > 256), TLG_ERR_NULL,
+ * TLG_ERR_MISALIGNED, TLG_ERR_HIP.  Nothing is enqueued on error.
+ */
+tlg_status tlg_gemm_w4(const void *A, const void *Wq, const void *S, const void *Z, void *C, int64_t M, int64_t N,
+                       int64_t K, int64_t G, int32_t ab_dtype, int32_t c_dtype, int32_t epilogue, void *stream);
+
 /* Release a plan (and its workspace, if any; the caller first makes sure no run of
  * the plan is still in flight).  NULL is accepted (no-op, TLG_OK). */
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan);

@@ -91,6 +91,8 @@ def load_library():
         lib.tlg_gemm_tune.restype = i32
         lib.tlg_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_float, vp]
         lib.tlg_attn_fwd.restype = i32
+        lib.tlg_gemm_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp]
+        lib.tlg_gemm_w4.restype = i32
         lib.tlg_gemm_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         lib.tlg_gemm_query.restype = i32
         lib.tlg_gemm_describe.argtypes = [vp]
@@ -365,3 +367,46 @@ def attention_ptrs(q: int, k: int, v: int, o: int, batch: int, seq: int, heads: 
     """Raw-pointer form of attention (no checks beyond the library's own); returns the status."""
     return load_library().tlg_attn_fwd(q or None, k or None, v or None, o or None, batch, seq, heads, dim,
                                        _code(dtype), int(causal), float(scale), ctypes.c_void_p(stream_handle))
+
+
+def gemm_w4(A: torch.Tensor, Wq: torch.Tensor, S: torch.Tensor, Z: torch.Tensor, C: torch.Tensor | None = None, *,
+            group: int = 128, epilogue: str = "none", out_dtype=torch.float16, stream=None) -> torch.Tensor:
+    """Dequant GEMM C = act(A Wᵀ) with 4-bit weights (tlg_gemm_w4).  A [M, K] fp16/bf16;
+    Wq [N, K/2] uint8 packed codes; S [N, K/group] scales (A's dtype); Z [N, K/group] uint8
+    zero points.  Returns C (allocated when not given)."""
+    M, K = A.shape
+    N = Wq.shape[0]
+    for name, t, shape, dt in (("A", A, (M, K), None), ("Wq", Wq, (N, K // 2), torch.uint8),
+                               ("S", S, (N, K // group), A.dtype), ("Z", Z, (N, K // group), torch.uint8)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor, got {t.device}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if dt is not None and t.dtype != dt:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dt}")
+        if t.numel() and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if tuple(C.shape) != (M, N) or (C.numel() and not C.is_contiguous()):
+        raise ValueError("C must be a contiguous [M, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lib = load_library()
+    with torch.cuda.device(A.device):
+        st = lib.tlg_gemm_w4(A.data_ptr() or None, Wq.data_ptr() or None, S.data_ptr() or None,
+                             Z.data_ptr() or None, C.data_ptr() or None, M, N, K, int(group), _code(A.dtype),
+                             _code(C.dtype), EPILOGUES[epilogue], ctypes.c_void_p(s))
+    if st != 0:
+        raise TlgError("tlg_gemm_w4", st)
+    return C
+
+
+def gemm_w4_ptrs(a: int, wq: int, s: int, z: int, c: int, M: int, N: int, K: int, group: int, ab_dtype, c_dtype,
+                 relu: int = 0, stream_handle: int = 0) -> int:
+    """Raw-pointer form of gemm_w4 (no checks beyond the library's own); returns the status."""
+    return load_library().tlg_gemm_w4(a or None, wq or None, s or None, z or None, c or None, M, N, K, group,
+                                      _code(ab_dtype), _code(c_dtype), int(relu), ctypes.c_void_p(stream_handle))

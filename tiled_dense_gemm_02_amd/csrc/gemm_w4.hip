@@ -1,0 +1,222 @@
+// Dequant GEMM with 4-bit weights, C[M x N] = act(A W^T): the "dequant GEMM" of
+// the representative-operators table on the overview page (load packed
+// weights, apply scale and zero point, convert, then multiply), shaped for
+// decoding: few rows of A, a long stream of weights.
+//
+// Format (include/tlg.h states it in full): W is N x K unsigned 4-bit codes,
+// [N, K/2] bytes; the eight codes of k = 8w .. 8w+7 of a row form one
+// little-endian 32-bit word with the even k in the low half-word (nibbles 0..3)
+// and the odd k in the high half-word (nibbles 4..7).  Per row and group of G
+// consecutive k there is a scale s (operand dtype) and a zero point z (uint8);
+// the weight is the operand-type value nearest to (q - z) * s.
+//
+// gfx950 mapping.  A workgroup owns 16 rows x 64 columns of C and streams the
+// 64 packed weight rows once, like the fp16 skinny kernel, through a 3-slot LDS
+// ring of 32 KiB stages filled by 1 KiB direct loads: a stage holds 512 of K,
+// i.e. 256 bytes of each weight row and 1 KiB of each A row.  Before the ring
+// starts, the workgroup's scales and zero points are gathered into a 64 KiB LDS
+// table (one dword per row and group: z in the low half, s in the high half).
+// The eight waves take different 32-wide K steps of a stage.  For an MFMA
+// 16x16x32 weight fragment a lane needs eight consecutive codes of one row --
+// exactly one packed dword -- which it turns into four operand pairs:
+//   fp16: x = (d >> 4i) & 0x000F000F | 0x64006400 is the pair (1024 + q0, 1024 + q1)
+//         in fp16; x - (1024 + z) is q - z exactly; one packed fp16 multiply by s
+//         rounds (q - z) * s to nearest even;
+//   bf16: 2^23 + q built the same way in fp32, minus 2^23 + z, times s is exact in
+//         fp32; v_cvt_pk_bf16_f32 rounds the pair to nearest even.
+// The per-wave partial tiles are summed through LDS in a fixed order, then the
+// epilogue (ReLU, conversion, guarded stores) runs.
+#include "gemm_lds.hpp"
+
+namespace tlg {
+
+namespace {
+
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int T>
+__device__ inline u32x4 dequant8(uint32_t d, uint32_t e)
+{
+    u32x4 w;
+    if constexpr (T == DT_F16) {
+        const uint32_t z = e & 0xffffu;
+        const h16x2 mz = __builtin_bit_cast(h16x2, (0x6400u + z) * 0x10001u);
+        const h16x2 s2 = __builtin_bit_cast(h16x2, (e >> 16) * 0x10001u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h16x2 x = __builtin_bit_cast(h16x2, ((d >> (4 * i)) & 0x000f000fu) | 0x64006400u);
+            w[i] = __builtin_bit_cast(uint32_t, (x - mz) * s2);
+        }
+    } else {
+        const float zf = (float)(e & 0xffffu) + 8388608.0f;
+        const float s = __builtin_bit_cast(float, e & 0xffff0000u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __builtin_bit_cast(float, 0x4b000000u | ((d >> (4 * i)) & 15u)) - zf;
+            const float hi = __builtin_bit_cast(float, 0x4b000000u | ((d >> (16 + 4 * i)) & 15u)) - zf;
+            const f32x2 v = {lo * s, hi * s};
+            w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        }
+    }
+    return w;
+}
+
+}  // namespace
+
+template <int T_IN>
+__global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
+{
+    constexpr int WAVES = 8, MR = 16, NB = kW4NB, KST = 512, S = 3;
+    constexpr int BRB = KST / 2;                 // bytes of a weight row per stage
+    constexpr int ARB = KST * 2;                 // bytes of an A row per stage
+    constexpr int BBYTES = NB * BRB, ABYTES = MR * ARB;
+    constexpr int STAGE = BBYTES + ABYTES;
+    constexpr int BRPL = 1024 / BRB;             // weight rows per 1 KiB direct load
+    constexpr int BL = BBYTES / 1024, AL = ABYTES / 1024;
+    constexpr int LPW = (BL + AL) / WAVES;       // direct loads per wave per stage
+    constexpr int NS = NB / 16;                  // 16-column MFMA tiles
+    constexpr int KSTEPS = KST / 32, SPW = KSTEPS / WAVES;
+    static_assert(BRB == 256 && ARB == 1024 && BL % WAVES == 0 && AL % WAVES == 0, "stage layout");
+    static_assert(S * STAGE + kW4TableBytes <= 160 * 1024, "ring and table must fit in 160 KiB");
+    static_assert(WAVES * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
+
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+    __shared__ __attribute__((aligned(16))) uint32_t tab[kW4TableBytes / 4];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int m0 = blockIdx.y * MR, n0 = blockIdx.x * NB;
+    const int K = p.K, G = p.G, KG = K / G;
+    const int NST = (K + KST - 1) / KST;
+
+    // Scale / zero table of this workgroup's rows (rows past N: zero weights).
+    for (int i = threadIdx.x; i < NB * KG; i += WAVES * 64) {
+        const int r = i / KG, gi = i - r * KG;
+        uint32_t e = 0;
+        if (n0 + r < p.N) {
+            const int64_t idx = (int64_t)(n0 + r) * KG + gi;
+            e = (uint32_t)((const uint8_t*)p.Z)[idx] | ((uint32_t)((const uint16_t*)p.S)[idx] << 16);
+        }
+        tab[i] = e;
+    }
+    // The gathers above must be complete before the first direct load is issued
+    // (the ring's vmcnt accounting counts direct loads only).
+    wait_vmcnt<0>();
+
+    const uint32_t bld = (uint32_t)K / 2u, ald = (uint32_t)K * 2u;
+    const char* b_base = (const char*)p.Wq + (uint64_t)n0 * bld;
+    const char* a_base = (const char*)p.A + (uint64_t)m0 * ald;
+    const uint64_t b_bytes = (uint64_t)(p.N - n0) * bld;
+    const uint64_t a_bytes = (uint64_t)(p.M - m0) * ald;
+    const uint32_t lds0 = lds_addr_of(smem);
+
+    // Load q = i * WAVES + wave of a stage: q < BL fills weight rows q*BRPL ..
+    // (lane -> row q*BRPL + lane/16, chunk position lane%16); otherwise A row q-BL
+    // (lane -> chunk position lane).  Chunk c of row r sits at c ^ (r & 15).
+    auto issue = [&](int st) {
+        const int k0 = st * KST;
+        const uint64_t ob = (uint64_t)st * BRB, oa = (uint64_t)st * ARB;
+        const uint32_t slot = lds0 + (uint32_t)((st % S) * STAGE);
+        const i32x4 rb = rsrc_words(b_base + ob, b_bytes > ob ? b_bytes - ob : 0);
+        const i32x4 ra = rsrc_words(a_base + oa, a_bytes > oa ? a_bytes - oa : 0);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int q = i * WAVES + wave;
+            if (q < BL) {
+                const int row = q * BRPL + lane / 16;
+                const int c = (lane & 15) ^ (row & 15);
+                const bool ok = n0 + row < p.N && k0 + c * 32 < K;
+                dma16(rb, ok ? (uint32_t)row * bld + (uint32_t)c * 16u : kOOB,
+                      __builtin_amdgcn_readfirstlane(slot + (uint32_t)(q * 1024)));
+            } else {
+                const int row = q - BL;
+                const int c = lane ^ (row & 15);
+                const bool ok = m0 + row < p.M && k0 + c * 8 < K;
+                dma16(ra, ok ? (uint32_t)row * ald + (uint32_t)c * 16u : kOOB,
+                      __builtin_amdgcn_readfirstlane(slot + (uint32_t)(BBYTES + row * 1024)));
+            }
+        }
+    };
+
+    f32x4 acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st)
+        if (st < NST) issue(st);
+    for (int st = 0; st < NST; ++st) {
+        // Stage st has landed once at most S-2 newer stages are in flight; the
+        // barrier publishes every wave's part (and, the first time, the table)
+        // and frees the slot refilled next.
+        if (st + S - 2 < NST)
+            wait_vmcnt<(S - 2) * LPW>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (st + S - 1 < NST) issue(st + S - 1);
+        const char* bslot = smem + (st % S) * STAGE;
+        const char* aslot = bslot + BBYTES;
+#pragma unroll
+        for (int u = 0; u < SPW; ++u) {
+            const int ks = wave * SPW + u;
+            const int kg = st * KST + ks * 32;
+            if (kg >= K) break;                                  // uniform: past the end of K
+            const int gi = kg / G;
+            const int ac = ks * 4 + g;
+            const u32x4 af = *(const u32x4*)(aslot + r16 * ARB + ((ac ^ r16) << 4));
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const int row = j * 16 + r16;
+                const uint32_t d = *(const uint32_t*)(bslot + row * BRB + ((ks ^ (row & 15)) << 4) + 4 * g);
+                const u32x4 wf = dequant8<T_IN>(d, tab[row * KG + gi]);
+                // Weight fragment first: acc[j][e] is C[m0 + lane%16][n0 + 16j + 4(lane/16) + e].
+                acc[j] = mfma16x16x32<T_IN>(wf, af, acc[j]);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+
+    float* red = (float*)smem;   // [WAVES][NS][4][64]
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((wave * NS + j) * 4 + e) * 64 + lane] = acc[j][e];
+    __syncthreads();
+
+    const int m = m0 + r16;
+    for (int j = wave; j < NS; j += WAVES) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float s = red[(j * 4 + e) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) s += red[((w * NS + j) * 4 + e) * 64 + lane];
+            v[e] = s;
+        }
+        const int n = n0 + j * 16 + 4 * g;
+        if (m >= p.M || n >= p.N) continue;
+        const int count = min(4, p.N - n);
+        const bool vec_ok = p.c_vec != 0 && count == 4;
+        if (p.relu) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = relu(v[e]);
+        }
+        store_c4(p.C, p.c_dtype, (int64_t)m * p.N + n, vec_ok, v, count);
+    }
+}
+
+hipError_t launch_w4(const W4Params& p, int ab_dtype, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((p.N + kW4NB - 1) / kW4NB), (unsigned)((p.M + 15) / 16)), block(512);
+    if (ab_dtype == DT_F16)
+        hipLaunchKernelGGL(gemm_w4_kernel<DT_F16>, grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL(gemm_w4_kernel<DT_BF16>, grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace tlg

@@ -491,6 +491,38 @@ tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, in
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }
 
+tlg_status tlg_gemm_w4(const void* A, const void* Wq, const void* S, const void* Z, void* C, int64_t M, int64_t N,
+                       int64_t K, int64_t G, int32_t ab_dtype, int32_t c_dtype, int32_t epilogue, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
+    if (G <= 0 || G % 32 != 0 || K % G != 0) return TLG_ERR_INVALID_ARG;
+    if (ab_dtype != TLG_F16 && ab_dtype != TLG_BF16) return TLG_ERR_INVALID_ARG;
+    if (c_dtype != TLG_F16 && c_dtype != TLG_BF16 && c_dtype != TLG_F32) return TLG_ERR_INVALID_ARG;
+    if (epilogue != TLG_EPI_NONE && epilogue != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
+    if (K / G > kW4MaxGroups) return TLG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return TLG_OK;
+    if (!C || (K > 0 && (!A || !Wq || !S || !Z))) return TLG_ERR_NULL;
+    const uintptr_t a = (uintptr_t)A, w = (uintptr_t)Wq, sc = (uintptr_t)S, z = (uintptr_t)Z, c = (uintptr_t)C;
+    const int cb = elem_bytes(c_dtype);
+    if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
+    if (K > 0 && ((a % 16) || (w % 16) || (sc % 2))) return TLG_ERR_MISALIGNED;
+    const uint64_t kg = K > 0 ? (uint64_t)(K / G) : 0;
+    const uint64_t a_bytes = (uint64_t)M * (uint64_t)K * 2u, w_bytes = (uint64_t)N * (uint64_t)K / 2u;
+    const uint64_t s_bytes = (uint64_t)N * kg * 2u, z_bytes = (uint64_t)N * kg;
+    const uint64_t c_bytes = (uint64_t)M * (uint64_t)N * (uint64_t)cb;
+    if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, w, w_bytes) ||
+        ranges_overlap(c, c_bytes, sc, s_bytes) || ranges_overlap(c, c_bytes, z, z_bytes))
+        return TLG_ERR_INVALID_ARG;
+    W4Params wp{};
+    wp.A = A; wp.Wq = Wq; wp.S = S; wp.Z = Z; wp.C = C;
+    wp.M = (int)M; wp.N = (int)N; wp.K = (int)K; wp.G = K > 0 ? (int)G : 32;
+    wp.relu = epilogue == TLG_EPI_RELU;
+    wp.c_dtype = c_dtype;
+    wp.c_vec = (N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    const hipError_t err = launch_w4(wp, ab_dtype == TLG_F16 ? DT_F16 : DT_BF16, (hipStream_t)stream);
+    return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan)
 {
     delete plan;

@@ -123,4 +123,21 @@ struct AttnParams {
 };
 hipError_t launch_attn(const AttnParams& p, int dim, int dtype, int causal, hipStream_t stream);
 
+// 4-bit dequant GEMM (gemm_w4.hip): C = act(A W^T), A [M, K] (16-byte aligned,
+// K % 32 == 0), Wq [N, K/2] packed codes, S [N, K/G] operand dtype, Z [N, K/G]
+// uint8; G % 32 == 0, K % G == 0, K / G <= kW4MaxGroups.
+constexpr int kW4NB = 64;                      // columns of C per workgroup
+constexpr int kW4TableBytes = 64 * 1024;       // LDS table: one dword per weight row and group
+constexpr int kW4MaxGroups = kW4TableBytes / 4 / kW4NB;
+struct W4Params {
+    const void* A;
+    const void* Wq;
+    const void* S;
+    const void* Z;
+    void* C;
+    int M, N, K, G;
+    int relu, c_dtype, c_vec;
+};
+hipError_t launch_w4(const W4Params& p, int ab_dtype, hipStream_t stream);
+
 }  // namespace tlg
