@@ -47,8 +47,10 @@ KERNEL_SOURCES = {
     8: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     9: ["gemm_mx.hpp", "gemm_mx.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     "attn": ["attn_fwd.hpp", "attn_fwd.hip", "gemm_lds.hpp", "tlg_device.hpp"],
+    "w4": ["gemm_w4.hip", "gemm_lds.hpp", "tlg_device.hpp"],
 }
 ATTN_VARIANT = "attn"
+W4_VARIANT = "w4"
 
 
 def kernel_hash(variant: int) -> str:
@@ -78,7 +80,7 @@ def parse():
     # ~40 ms of launches: the clock settles only after tens of ms of MFMA load
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c5a", help="c1..c5b, a block-scaled workload mx1..mx3, "
-                    "or an attention workload fa1..fa4")
+                    "an attention workload fa1..fa4, or a dequant GEMM workload w4a..w4c")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -258,6 +260,106 @@ def measure_attn(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_m
             "describe": f"attn_fwd block=128x64 threads=256 dim={case.D} causal={case.causal} dtype={case.dtype}"}
 
 
+def measure_w4(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=0.0):
+    """measure() for a 4-bit dequant GEMM workload (tlg_gemm_w4)."""
+    import torch
+    import tiled_dense_gemm_02_amd as tlg
+    import tlg_workloads as W
+
+    dev = torch.device("cuda:0")
+    A, Wq, S, Z, _ = W.make_w4_inputs(case)
+    set_bytes = Wq.numel() + S.numel() * 2 + Z.numel() + A.numel() * 2
+    nsets = max(1, min(16, math.ceil(rotate_bytes / max(set_bytes, 1))))
+    sets = [tuple(t.to(dev) for t in (A, Wq, S, Z)) for _ in range(nsets)]
+    C = torch.empty((case.M, case.N), dtype=plan_out_dtype(case), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    tlg.gemm_w4(*sets[0], C, group=case.G, epilogue="relu" if case.relu else "none", stream=stream)
+    ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
+    c_ptr, sh = C.data_ptr(), stream.cuda_stream
+    status = 0
+
+    def launch(i):
+        a, w, sc, z = ptrs[i % nsets]
+        return tlg.gemm_w4_ptrs(a, w, sc, z, c_ptr, case.M, case.N, case.K, case.G, A.dtype, C.dtype, case.relu, sh)
+
+    for i in range(warmup):
+        status |= launch(i)
+    torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for i in range(20):
+            status |= launch(i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        per = max(w0.elapsed_time(w1) / 20, 1e-3)
+        for i in range(int(math.ceil(max(0.0, min_warm_ms - 20 * per) / per))):
+            status |= launch(i)
+        torch.cuda.synchronize()
+    if log:
+        log(f"[bench] {case.name}: w4 M={case.M} N={case.N} K={case.K} G={case.G} sets={nsets}")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        status |= launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError(f"tlg_gemm_w4 failed during the timed launches (status {status})")
+    return {"ms": start.elapsed_time(end) / steps, "wall_s": time.perf_counter() - t0, "C": C, "nsets": nsets,
+            "describe": f"gemm_w4 block=16x64x512 threads=512 group={case.G} {case.ab}->{case.c}"}
+
+
+def cpu_baseline_w4(case, C_gpu, rows):
+    """cpu_baseline() for a dequant GEMM workload: the oracle on the first `rows` output rows."""
+    import numpy as np
+    import tlg_workloads as W
+    from oracle import build_oracle, oracle as O
+    if not os.path.exists(O.LIB_PATH):
+        build_oracle.build()
+    A, Wq, S, Z, _ = W.make_w4_inputs(case)
+    t0 = time.perf_counter()
+    o = O.w4gemm(case.M, case.N, case.K, case.G, W.bits16(A), Wq.numpy(), W.bits16(S), Z.numpy(), dtype=case.ab,
+                 relu=case.relu, rows=(0, rows))
+    dt = time.perf_counter() - t0
+    sample_bytes = case.N * case.K // 2 + 3 * case.N * (case.K // case.G) + 2 * rows * case.K
+    gpu = C_gpu[:rows].float().cpu().numpy().astype(np.float64)
+    rel = 2.0 ** -8 if case.c == "bf16" else 2.0 ** -10
+    wmax = 15.0 * float(S.float().abs().max())
+    ok = bool((np.abs(gpu - o) <= rel * np.abs(o) + 1e-4 * np.sqrt(case.K) * wmax).all())
+    return {"value": sample_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {case.M} output rows of {case.name} (all weights dequantized once, "
+                      f"{2.0 * rows * case.N * case.K / 1e9:.1f} GFLOP, fp64 loops, {dt:.1f} s)",
+            "seconds": dt, "sample_matches_gpu": ok}
+
+
+def bench_w4(args, case, log):
+    """The JSON line of a dequant GEMM workload: HBM-bound (one read of the packed weights,
+    scales, zero points and A, one write of C)."""
+    r = measure_w4(case, args.steps, args.warmup, log=log, min_warm_ms=100.0)
+    ms = r["ms"]
+    gbs = case.algorithmic_bytes / (ms * 1e-3) / 1e9
+    tflops = case.flops / (ms * 1e-3) / 1e12
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+            "traffic": stored_traffic(args.workload, W4_VARIANT), "kernel": "gemm_w4",
+            "per_launch": {"flops": case.flops, "algorithmic_bytes": case.algorithmic_bytes, "avg_kernel_ms": ms}}
+    out = {"metric": "dequant GEMM GB/s (4-bit weights, fp32 accumulate) and % of HBM peak", "value": gbs,
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": f"u4/{case.ab}",
+           "data": "synthetic (seeded, see tlg_workloads.py)",
+           "config": {"workload": f"{case.name}: {case.note}", "M": case.M, "N": case.N, "K": case.K,
+                      "group": case.G, "ab_dtype": case.ab, "c_dtype": case.c, "plan": r["describe"],
+                      "operand_sets_rotated": r["nsets"], "TFLOP/s": tflops},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_w4(case, r["C"], {"w4a": 16, "w4b": 5, "w4c": 8}[case.name])
+    return out
+
+
 def plan_out_dtype(case):
     import torch
     return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.c]
@@ -378,6 +480,9 @@ def main():
         log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
         del x, y
 
+    if args.workload in W.W4_CONFIGS:
+        print(json.dumps(bench_w4(args, W.W4_CONFIGS[args.workload], log)), flush=True)
+        return
     if args.workload in W.ATTN_CONFIGS:
         print(json.dumps(bench_attn(args, W.ATTN_CONFIGS[args.workload], log)), flush=True)
         return
@@ -415,17 +520,18 @@ def main():
 
     if not args.no_secondary:
         sec = []
-        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3", "fa3"):
+        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3", "fa3", "w4a"):
             if name == args.workload:
                 continue
-            sec_mx, sec_attn = name in W.MX_CONFIGS, name in W.ATTN_CONFIGS
-            c2 = W.MX_CONFIGS[name] if sec_mx else W.ATTN_CONFIGS[name] if sec_attn else W.CONFIGS[name]
-            fn = measure_mx if sec_mx else measure_attn if sec_attn else measure
+            sec_mx, sec_attn, sec_w4 = name in W.MX_CONFIGS, name in W.ATTN_CONFIGS, name in W.W4_CONFIGS
+            c2 = (W.MX_CONFIGS[name] if sec_mx else W.ATTN_CONFIGS[name] if sec_attn else
+                  W.W4_CONFIGS[name] if sec_w4 else W.CONFIGS[name])
+            fn = measure_mx if sec_mx else measure_attn if sec_attn else measure_w4 if sec_w4 else measure
             rr = fn(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
             t = rr["ms"] * 1e-3
             entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
                      "GB/s": c2.algorithmic_bytes / t / 1e9,
-                     "plan": rr["describe"] if sec_attn else rr["plan"].describe()}
+                     "plan": rr["describe"] if (sec_attn or sec_w4) else rr["plan"].describe()}
             entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.fmt if sec_mx else c2.dtype if sec_attn else c2.ab]
             entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS
             sec.append(entry)

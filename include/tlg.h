@@ -280,14 +280,14 @@ tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, in
  *
  * A [M, K], S and C are dense row-major.  ab_dtype (A and S) in {TLG_F16,
  * TLG_BF16}; c_dtype in {TLG_F16, TLG_BF16, TLG_F32}; epilogue NONE or RELU.
- * Limits: G a positive multiple of 32, K % G == 0, K / G <= 256, M and N <= 2^24.
+ * Limits: G a positive multiple of 32, K % G == 0, K / G <= 255, M and N <= 2^24.
  * A and Wq must be 16-byte aligned, S 2-byte aligned, C aligned to its element.
  * C must not overlap A, Wq, S or Z.
  *
  * Ownership as tlg_gemm_run: the caller owns all buffers; the call allocates
  * nothing, does not synchronise and enqueues at most one kernel on `stream`.
  * M == 0 or N == 0 enqueues nothing.  Errors: TLG_ERR_INVALID_ARG (sizes,
- * enums, group, overlap), TLG_ERR_UNSUPPORTED (K / G > 256), TLG_ERR_NULL,
+ * enums, group, overlap), TLG_ERR_UNSUPPORTED (K / G > 255), TLG_ERR_NULL,
  * TLG_ERR_MISALIGNED, TLG_ERR_HIP.  Nothing is enqueued on error.
  */
 tlg_status tlg_gemm_w4(const void *A, const void *Wq, const void *S, const void *Z, void *C, int64_t M, int64_t N,

@@ -103,7 +103,7 @@ def test_small_integers_exact(ab, c):
 
 
 EDGES = [(1, 1, 32, 32), (1, 64, 32, 32), (16, 65, 64, 64), (17, 130, 544, 32), (3, 257, 1536, 256),
-         (2, 129, 8192, 32), (4, 100, 0, 32)]
+         (2, 129, 8160, 32), (4, 100, 0, 32)]
 
 
 @pytest.mark.parametrize("shape", EDGES, ids=lambda s: "x".join(map(str, s)))
@@ -134,6 +134,6 @@ def test_error_paths_enqueue_nothing():
     assert tlg.gemm_w4_ptrs(pa + 8, pw, ps, pz, pc, 16, 64, 256, 128, f16, f16) == -4     # A misaligned
     assert tlg.gemm_w4_ptrs(pa, pw, ps, pz, pa, 16, 64, 256, 128, f16, f16) == -1         # C overlaps A
     assert tlg.gemm_w4_ptrs(pa, pw, ps, pz, pc, 16, 64, 256, 96, f16, f16) == -1          # group 96
-    assert tlg.gemm_w4_ptrs(pa, pw, ps, pz, pc, 16, 64, 256 * 257, 256, f16, f16) == -2   # K/G > 256
+    assert tlg.gemm_w4_ptrs(pa, pw, ps, pz, pc, 16, 64, 256 * 257, 256, f16, f16) == -2   # K/G > 255
     torch.cuda.synchronize()
     assert bool((C == 7.0).all())

@@ -11,12 +11,14 @@
 // the weight is the operand-type value nearest to (q - z) * s.
 //
 // gfx950 mapping.  A workgroup owns 16 rows x 64 columns of C and streams the
-// 64 packed weight rows once, like the fp16 skinny kernel, through a 3-slot LDS
-// ring of 32 KiB stages filled by 1 KiB direct loads: a stage holds 512 of K,
-// i.e. 256 bytes of each weight row and 1 KiB of each A row.  Before the ring
-// starts, the workgroup's scales and zero points are gathered into a 64 KiB LDS
-// table (one dword per row and group: z in the low half, s in the high half).
-// The eight waves take different 32-wide K steps of a stage.  For an MFMA
+// 64 packed weight rows once, like the fp16 skinny kernel, through an LDS ring
+// of 32 KiB stages filled by 1 KiB direct loads: a stage holds 512 of K, i.e.
+// 256 bytes of each weight row and 1 KiB of each A row.  The workgroup's scales
+// and zero points are gathered into an LDS table (one dword per row and group:
+// z in the low half, s in the high half) while the first stages load; the table
+// takes what the ring leaves of 160 KiB (4 slots when K/G <= 128, else 3).
+// The sixteen waves (four per SIMD, to hide the latency of each wave's chain of
+// LDS read, dequantization and MFMA) take different 32-wide K steps of a stage.  For an MFMA
 // 16x16x32 weight fragment a lane needs eight consecutive codes of one row --
 // exactly one packed dword -- which it turns into four operand pairs:
 //   fp16: x = (d >> 4i) & 0x000F000F | 0x64006400 is the pair (1024 + q0, 1024 + q1)
@@ -36,8 +38,11 @@ typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// mask (0x000F000F, in an SGPR) and magic (0x64006400, in a VGPR) come in as
+// opaque values: with literal constants the compiler cannot fuse the mask and
+// the or into one v_and_or_b32 (a VOP3 instruction takes no literal on gfx950).
 template <int T>
-__device__ inline u32x4 dequant8(uint32_t d, uint32_t e)
+__device__ inline u32x4 dequant8(uint32_t d, uint32_t e, uint32_t mask, uint32_t magic)
 {
     u32x4 w;
     if constexpr (T == DT_F16) {
@@ -46,7 +51,7 @@ __device__ inline u32x4 dequant8(uint32_t d, uint32_t e)
         const h16x2 s2 = __builtin_bit_cast(h16x2, (e >> 16) * 0x10001u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const h16x2 x = __builtin_bit_cast(h16x2, ((d >> (4 * i)) & 0x000f000fu) | 0x64006400u);
+            const h16x2 x = __builtin_bit_cast(h16x2, ((d >> (4 * i)) & mask) | magic);
             w[i] = __builtin_bit_cast(uint32_t, (x - mz) * s2);
         }
     } else {
@@ -65,45 +70,40 @@ __device__ inline u32x4 dequant8(uint32_t d, uint32_t e)
 
 }  // namespace
 
-template <int T_IN>
-__global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
+// S: ring slots (S-1 stages in flight); the scale / zero table gets the rest of
+// the 160 KiB: 64 KiB (K/G <= 256) with 3 slots, 32 KiB (K/G <= 128) with 4.
+template <int T_IN, int S, int KST>
+__global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
 {
-    constexpr int WAVES = 8, MR = 16, NB = kW4NB, KST = 512, S = 3;
+    constexpr int WAVES = kW4Threads / 64, MR = 16, NB = kW4NB;
     constexpr int BRB = KST / 2;                 // bytes of a weight row per stage
     constexpr int ARB = KST * 2;                 // bytes of an A row per stage
+    constexpr int BCH = BRB / 16;                // 16-byte chunks of a weight row per stage
     constexpr int BBYTES = NB * BRB, ABYTES = MR * ARB;
     constexpr int STAGE = BBYTES + ABYTES;
     constexpr int BRPL = 1024 / BRB;             // weight rows per 1 KiB direct load
+    constexpr int APL = ARB / 1024;              // 1 KiB direct loads per A row
     constexpr int BL = BBYTES / 1024, AL = ABYTES / 1024;
     constexpr int LPW = (BL + AL) / WAVES;       // direct loads per wave per stage
     constexpr int NS = NB / 16;                  // 16-column MFMA tiles
     constexpr int KSTEPS = KST / 32, SPW = KSTEPS / WAVES;
-    static_assert(BRB == 256 && ARB == 1024 && BL % WAVES == 0 && AL % WAVES == 0, "stage layout");
-    static_assert(S * STAGE + kW4TableBytes <= 160 * 1024, "ring and table must fit in 160 KiB");
+    static_assert(BRB >= 256 && BRB <= 1024 && ARB >= 1024 && BL % WAVES == 0 && AL % WAVES == 0, "stage layout");
+    static_assert(KSTEPS % WAVES == 0 && SPW >= 1, "every wave takes whole K steps of a stage");
+    constexpr int TABLE = 160 * 1024 - S * STAGE;
+    static_assert(TABLE >= 16 * 1024 && TABLE <= kW4TableBytes, "ring and table must fit in 160 KiB");
     static_assert(WAVES * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
-    __shared__ __attribute__((aligned(16))) uint32_t tab[kW4TableBytes / 4];
+    __shared__ __attribute__((aligned(16))) uint32_t tab[TABLE / 4];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const int m0 = blockIdx.y * MR, n0 = blockIdx.x * NB;
     const int K = p.K, G = p.G, KG = K / G;
+    // Table row stride: odd, so the 16 rows a fragment reads at one group sit in
+    // 16 different banks (an even stride such as 64 put them all in one bank).
+    const int KGP = KG | 1;
     const int NST = (K + KST - 1) / KST;
-
-    // Scale / zero table of this workgroup's rows (rows past N: zero weights).
-    for (int i = threadIdx.x; i < NB * KG; i += WAVES * 64) {
-        const int r = i / KG, gi = i - r * KG;
-        uint32_t e = 0;
-        if (n0 + r < p.N) {
-            const int64_t idx = (int64_t)(n0 + r) * KG + gi;
-            e = (uint32_t)((const uint8_t*)p.Z)[idx] | ((uint32_t)((const uint16_t*)p.S)[idx] << 16);
-        }
-        tab[i] = e;
-    }
-    // The gathers above must be complete before the first direct load is issued
-    // (the ring's vmcnt accounting counts direct loads only).
-    wait_vmcnt<0>();
 
     const uint32_t bld = (uint32_t)K / 2u, ald = (uint32_t)K * 2u;
     const char* b_base = (const char*)p.Wq + (uint64_t)n0 * bld;
@@ -113,8 +113,9 @@ __global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
     const uint32_t lds0 = lds_addr_of(smem);
 
     // Load q = i * WAVES + wave of a stage: q < BL fills weight rows q*BRPL ..
-    // (lane -> row q*BRPL + lane/16, chunk position lane%16); otherwise A row q-BL
-    // (lane -> chunk position lane).  Chunk c of row r sits at c ^ (r & 15).
+    // (lane -> row q*BRPL + lane/BCH, chunk position lane%BCH); otherwise 1 KiB of
+    // A row (q-BL)/APL (lane -> chunk position ((q-BL)%APL)*64 + lane).  Chunk c of
+    // row r sits at c ^ (r & 15).
     auto issue = [&](int st) {
         const int k0 = st * KST;
         const uint64_t ob = (uint64_t)st * BRB, oa = (uint64_t)st * ARB;
@@ -125,17 +126,17 @@ __global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
         for (int i = 0; i < LPW; ++i) {
             const int q = i * WAVES + wave;
             if (q < BL) {
-                const int row = q * BRPL + lane / 16;
-                const int c = (lane & 15) ^ (row & 15);
+                const int row = q * BRPL + lane / BCH;
+                const int c = (lane % BCH) ^ (row & 15);
                 const bool ok = n0 + row < p.N && k0 + c * 32 < K;
                 dma16(rb, ok ? (uint32_t)row * bld + (uint32_t)c * 16u : kOOB,
                       __builtin_amdgcn_readfirstlane(slot + (uint32_t)(q * 1024)));
             } else {
-                const int row = q - BL;
-                const int c = lane ^ (row & 15);
+                const int row = (q - BL) / APL;
+                const int c = (((q - BL) % APL) * 64 + lane) ^ (row & 15);
                 const bool ok = m0 + row < p.M && k0 + c * 8 < K;
                 dma16(ra, ok ? (uint32_t)row * ald + (uint32_t)c * 16u : kOOB,
-                      __builtin_amdgcn_readfirstlane(slot + (uint32_t)(BBYTES + row * 1024)));
+                      __builtin_amdgcn_readfirstlane(slot + (uint32_t)(BBYTES + (q - BL) * 1024)));
             }
         }
     };
@@ -143,10 +144,29 @@ __global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
     f32x4 acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t mask = __builtin_amdgcn_readfirstlane(p.nibble_mask);
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
         if (st < NST) issue(st);
+    // Scale / zero table of this workgroup's rows (rows past N: zero weights).
+    for (int i = threadIdx.x; i < NB * KG; i += WAVES * 64) {
+        const int r = i / KG, gi = i - r * KG;
+        const int slot_i = r * KGP + gi;
+        uint32_t e = 0;
+        if (n0 + r < p.N) {
+            const int64_t idx = (int64_t)(n0 + r) * KG + gi;
+            e = (uint32_t)((const uint8_t*)p.Z)[idx] | ((uint32_t)((const uint16_t*)p.S)[idx] << 16);
+        }
+        tab[slot_i] = e;
+    }
+    // The gathers above overlap the first stages' direct loads.  They are waited
+    // for here, together with everything issued before them: the ring's vmcnt
+    // accounting below counts direct loads only.
+    wait_vmcnt<0>();
+
     for (int st = 0; st < NST; ++st) {
         // Stage st has landed once at most S-2 newer stages are in flight; the
         // barrier publishes every wave's part (and, the first time, the table)
@@ -162,16 +182,16 @@ __global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int ks = wave * SPW + u;
-            const int kg = st * KST + ks * 32;
-            if (kg >= K) break;                                  // uniform: past the end of K
-            const int gi = kg / G;
+            // K steps past the end of K read zeros from A and W (range-checked
+            // loads); their group index is clamped so the table read stays inside.
+            const int gi = min((st * KST + ks * 32) / G, KG - 1);
             const int ac = ks * 4 + g;
             const u32x4 af = *(const u32x4*)(aslot + r16 * ARB + ((ac ^ r16) << 4));
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
                 const int row = j * 16 + r16;
                 const uint32_t d = *(const uint32_t*)(bslot + row * BRB + ((ks ^ (row & 15)) << 4) + 4 * g);
-                const u32x4 wf = dequant8<T_IN>(d, tab[row * KG + gi]);
+                const u32x4 wf = dequant8<T_IN>(d, tab[row * KGP + gi], mask, magic);
                 // Weight fragment first: acc[j][e] is C[m0 + lane%16][n0 + 16j + 4(lane/16) + e].
                 acc[j] = mfma16x16x32<T_IN>(wf, af, acc[j]);
             }
@@ -209,14 +229,22 @@ __global__ void __launch_bounds__(512) gemm_w4_kernel(W4Params p)
     }
 }
 
+template <int S, int KST>
+static hipError_t launch_w4_s(const W4Params& p, int ab_dtype, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((p.N + kW4NB - 1) / kW4NB), (unsigned)((p.M + 15) / 16)), block(kW4Threads);
+    if (ab_dtype == DT_F16)
+        hipLaunchKernelGGL((gemm_w4_kernel<DT_F16, S, KST>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_w4_kernel<DT_BF16, S, KST>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_w4(const W4Params& p, int ab_dtype, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((p.N + kW4NB - 1) / kW4NB), (unsigned)((p.M + 15) / 16)), block(512);
-    if (ab_dtype == DT_F16)
-        hipLaunchKernelGGL(gemm_w4_kernel<DT_F16>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(gemm_w4_kernel<DT_BF16>, grid, block, 0, stream, p);
-    return hipGetLastError();
+    const int groups = (p.K / p.G) | 1;          // the kernel's padded table row
+    if (kW4NB * groups * 4 <= 32 * 1024) return launch_w4_s<2, 1024>(p, ab_dtype, stream);
+    return launch_w4_s<3, 512>(p, ab_dtype, stream);
 }
 
 }  // namespace tlg

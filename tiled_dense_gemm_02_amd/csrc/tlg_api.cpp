@@ -519,6 +519,7 @@ tlg_status tlg_gemm_w4(const void* A, const void* Wq, const void* S, const void*
     wp.relu = epilogue == TLG_EPI_RELU;
     wp.c_dtype = c_dtype;
     wp.c_vec = (N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    wp.nibble_mask = 0x000F000Fu;
     const hipError_t err = launch_w4(wp, ab_dtype == TLG_F16 ? DT_F16 : DT_BF16, (hipStream_t)stream);
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }

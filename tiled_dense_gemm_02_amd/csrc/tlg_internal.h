@@ -127,8 +127,9 @@ hipError_t launch_attn(const AttnParams& p, int dim, int dtype, int causal, hipS
 // K % 32 == 0), Wq [N, K/2] packed codes, S [N, K/G] operand dtype, Z [N, K/G]
 // uint8; G % 32 == 0, K % G == 0, K / G <= kW4MaxGroups.
 constexpr int kW4NB = 64;                      // columns of C per workgroup
+constexpr int kW4Threads = 1024;               // 16 waves
 constexpr int kW4TableBytes = 64 * 1024;       // LDS table: one dword per weight row and group
-constexpr int kW4MaxGroups = kW4TableBytes / 4 / kW4NB;
+constexpr int kW4MaxGroups = kW4TableBytes / 4 / kW4NB - 1;   // rows padded to an odd number of groups
 struct W4Params {
     const void* A;
     const void* Wq;
@@ -137,6 +138,7 @@ struct W4Params {
     void* C;
     int M, N, K, G;
     int relu, c_dtype, c_vec;
+    uint32_t nibble_mask;   // 0x000F000F (a kernel argument so that it lives in an SGPR)
 };
 hipError_t launch_w4(const W4Params& p, int ab_dtype, hipStream_t stream);
 
