@@ -48,6 +48,12 @@ class Oracle:
         lib.oracle_mx_decode.argtypes = [i32, vp, i64, vp]
         lib.oracle_mx_decode.restype = i32
         f64 = ctypes.c_double
+        lib.oracle_sp_expand.argtypes = [i64, i64, i32, vp, vp, vp]
+        lib.oracle_sp_expand.restype = i32
+        lib.oracle_spgemm_rows.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i64, i64, vp]
+        lib.oracle_spgemm_rows.restype = i32
+        lib.oracle_spgemm_points.argtypes = [i64, i64, i64, i32, i32, vp, vp, vp, i64, vp, vp, vp]
+        lib.oracle_spgemm_points.restype = i32
         lib.oracle_w4_dequant.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp]
         lib.oracle_w4_dequant.restype = i32
         lib.oracle_w4gemm_rows.argtypes = [i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, i64, i64, vp]
@@ -148,6 +154,36 @@ class Oracle:
                                          out.ctypes.data)
         if rc != 0:
             raise ValueError(f"oracle_attn_points failed with {rc}")
+        return out
+
+    def sp_expand(self, N, K, Wv_bits, Wm, *, dtype="f16") -> np.ndarray:
+        """Dense weights w(n, k) of a 2:4 compressed [N, K] operand, float64."""
+        Wv, Wm = _u16(Wv_bits), _u8(Wm)
+        out = np.empty((N, K), dtype=np.float64)
+        if self.lib.oracle_sp_expand(N, K, _code(dtype), _ptr(Wv), _ptr(Wm), out.ctypes.data) != 0:
+            raise ValueError("oracle_sp_expand failed")
+        return out
+
+    def spgemm(self, M, N, K, A_bits, Wv_bits, Wm, *, dtype="f16", relu=0, rows=None) -> np.ndarray:
+        """2:4 sparse GEMM o(m, n) = act(sum_k a(m,k) w(n,k)) in float64 for rows=(m0, m1)."""
+        A, Wv, Wm = _u16(A_bits), _u16(Wv_bits), _u8(Wm)
+        m0, m1 = (0, M) if rows is None else rows
+        out = np.empty((m1 - m0, N), dtype=np.float64)
+        rc = self.lib.oracle_spgemm_rows(M, N, K, _code(dtype), int(relu), _ptr(A), _ptr(Wv), _ptr(Wm), m0, m1,
+                                         out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_spgemm_rows failed with {rc}")
+        return out
+
+    def spgemm_points(self, M, N, K, A_bits, Wv_bits, Wm, ms, ns, *, dtype="f16", relu=0) -> np.ndarray:
+        A, Wv, Wm = _u16(A_bits), _u16(Wv_bits), _u8(Wm)
+        ms = np.ascontiguousarray(ms, dtype=np.int64)
+        ns = np.ascontiguousarray(ns, dtype=np.int64)
+        out = np.empty(ms.shape[0], dtype=np.float64)
+        rc = self.lib.oracle_spgemm_points(M, N, K, _code(dtype), int(relu), _ptr(A), _ptr(Wv), _ptr(Wm),
+                                           ms.shape[0], ms.ctypes.data, ns.ctypes.data, out.ctypes.data)
+        if rc != 0:
+            raise ValueError(f"oracle_spgemm_points failed with {rc}")
         return out
 
     def w4_dequant(self, N, K, G, Wq, S_bits, Z, *, dtype="f16") -> np.ndarray:
@@ -285,6 +321,18 @@ def attn(*args, **kw):
 
 def attn_points(*args, **kw):
     return default().attn_points(*args, **kw)
+
+
+def sp_expand(*args, **kw):
+    return default().sp_expand(*args, **kw)
+
+
+def spgemm(*args, **kw):
+    return default().spgemm(*args, **kw)
+
+
+def spgemm_points(*args, **kw):
+    return default().spgemm_points(*args, **kw)
 
 
 def w4_dequant(*args, **kw):

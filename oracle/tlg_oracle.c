@@ -1,8 +1,8 @@
 /*
  * CPU oracle for the tiled dense GEMM  C = act(A·B)  — TEST INFRASTRUCTURE ONLY.
  * Further sections below hold the block-scaled (MX) GEMM, the attention
- * forward pass and the 4-bit dequant GEMM, each with its own statement of
- * what it computes.
+ * forward pass, the 4-bit dequant GEMM and the 2:4 structured-sparse GEMM,
+ * each with its own statement of what it computes.
  *
  * Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
  * load this library.  It shares no code, header, table or helper with the HIP
@@ -659,5 +659,94 @@ int oracle_w4gemm_points(int64_t M, int64_t N, int64_t K, int64_t G, int ab_dtyp
         if (relu && !(acc > 0.0)) acc = 0.0;
         out[i] = acc;
     }
+    return 0;
+}
+
+/* ===========================================================================
+ * 2:4 structured-sparse GEMM (the pages' T.gemm_sp: "2:4 structured sparse
+ * GEMM" in the overview page's table of compute primitives, tied there to the
+ * hardware's sparse matrix instructions).  Reading used here: the sparse
+ * operand is the weight matrix W [N, K] of C = act(A W^T), given compressed:
+ *   - every group of four consecutive k of a row holds two stored values,
+ *     Wv[n, 2q] and Wv[n, 2q+1] for group q (Wv is [N, K/2] in the operand dtype);
+ *   - their positions inside the group, two 2-bit fields per value pair, in
+ *     Wm [N, K/8] bytes: byte n*(K/8) + q/2 holds group q's positions at bits
+ *     4*(q%2) (first value) and 4*(q%2) + 2 (second value);
+ *   - the dense w(n, k) is the sum of the stored values whose position is k
+ *     (two values at one position add; positions without a value are zero).
+ *   c(m, n) = sum_k a(m, k) * w(n, k)      (double, ascending k)
+ *   o(m, n) = relu ? max(c, +0) : c
+ * ======================================================================== */
+static void sp_expand_row(int dt, const uint16_t *Wv, const uint8_t *Wm, int64_t K, int64_t n, double *w)
+{
+    for (int64_t k = 0; k < K; ++k) w[k] = 0.0;
+    for (int64_t q = 0; q < K / 4; ++q) {
+        const uint32_t byte = Wm[n * (K / 8) + q / 2];
+        const int sh = 4 * (int)(q % 2);
+        const int p0 = (int)((byte >> sh) & 3u), p1 = (int)((byte >> (sh + 2)) & 3u);
+        w[4 * q + p0] += dec(dt, Wv[n * (K / 2) + 2 * q]);
+        w[4 * q + p1] += dec(dt, Wv[n * (K / 2) + 2 * q + 1]);
+    }
+}
+
+static int sp_args_ok(int64_t M, int64_t N, int64_t K, int dt)
+{
+    return M >= 0 && N >= 0 && K >= 0 && K % 8 == 0 && (dt == ORACLE_F16 || dt == ORACLE_BF16);
+}
+
+/* Dense w(n, k), [N, K]. */
+int oracle_sp_expand(int64_t N, int64_t K, int ab_dtype, const uint16_t *Wv, const uint8_t *Wm, double *out)
+{
+    if (!sp_args_ok(0, N, K, ab_dtype)) return -1;
+    if (N * K == 0) return 0;
+    if (!Wv || !Wm || !out) return -1;
+    for (int64_t n = 0; n < N; ++n) sp_expand_row(ab_dtype, Wv, Wm, K, n, out + n * K);
+    return 0;
+}
+
+/* Output rows [m0, m1) of C = act(A W^T). */
+int oracle_spgemm_rows(int64_t M, int64_t N, int64_t K, int ab_dtype, int relu, const uint16_t *A,
+                       const uint16_t *Wv, const uint8_t *Wm, int64_t m0, int64_t m1, double *out)
+{
+    if (!sp_args_ok(M, N, K, ab_dtype) || m0 < 0 || m1 < m0 || m1 > M) return -1;
+    if (m1 == m0 || N == 0) return 0;
+    if (K > 0 && (!A || !Wv || !Wm)) return -1;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *arow = (double *)malloc(sizeof(double) * (size_t)((m1 - m0) * (K > 0 ? K : 1)));
+    if (!w || !arow) { free(w); free(arow); return -2; }
+    for (int64_t m = m0; m < m1; ++m)
+        for (int64_t k = 0; k < K; ++k) arow[(m - m0) * K + k] = dec(ab_dtype, A[m * K + k]);
+    for (int64_t n = 0; n < N; ++n) {
+        sp_expand_row(ab_dtype, Wv, Wm, K, n, w);
+        for (int64_t m = m0; m < m1; ++m) {
+            double acc = 0.0;
+            const double *ar = arow + (m - m0) * K;
+            for (int64_t k = 0; k < K; ++k) acc += ar[k] * w[k];
+            if (relu && !(acc > 0.0)) acc = 0.0;
+            out[(m - m0) * N + n] = acc;
+        }
+    }
+    free(w); free(arow);
+    return 0;
+}
+
+/* The same definition at selected outputs (pm[i], pn[i]). */
+int oracle_spgemm_points(int64_t M, int64_t N, int64_t K, int ab_dtype, int relu, const uint16_t *A,
+                         const uint16_t *Wv, const uint8_t *Wm, int64_t npts, const int64_t *pm,
+                         const int64_t *pn, double *out)
+{
+    if (!sp_args_ok(M, N, K, ab_dtype) || npts < 0) return -1;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    if (!w) return -2;
+    for (int64_t i = 0; i < npts; ++i) {
+        const int64_t m = pm[i], n = pn[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) { free(w); return -1; }
+        sp_expand_row(ab_dtype, Wv, Wm, K, n, w);
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) acc += dec(ab_dtype, A[m * K + k]) * w[k];
+        if (relu && !(acc > 0.0)) acc = 0.0;
+        out[i] = acc;
+    }
+    free(w);
     return 0;
 }

@@ -435,3 +435,96 @@ def make_w4_inputs(case: W4Case):
         raise ValueError(f"unknown distribution {case.dist!r}")
     Wq = torch.from_numpy(pack_w4(q.numpy()))
     return A.contiguous(), Wq.contiguous(), S.contiguous(), Z.contiguous(), q
+
+
+# ---------------------------------------------------------------------------
+# 2:4 structured-sparse GEMM: C = act(A W^T) with W [N, K] holding at most two
+# values in every group of four consecutive k, given compressed (compress_24
+# below is the one writer of the metadata): Wv [N, K/2] values in the operand
+# dtype, two per group in order; Wm [N, K/8] bytes, group q's two positions at
+# bits 4*(q%2) and 4*(q%2) + 2 of byte q/2 of the row.
+#
+# Recipe: the seeded generator draws A (uniform in [-1, 1), or N(0,1)/sqrt(K/2)
+# for "normal"), then per group two distinct positions (uniform, ascending) and
+# their values (uniform in [-1, 1), or N(0, 1)); "smallint": integer A and values.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class SpCase:
+    name: str
+    M: int
+    N: int
+    K: int
+    ab: str = "f16"
+    c: str = "f16"
+    relu: int = 0
+    dist: str = "uniform"    # "uniform" | "normal" | "smallint"
+    seed: int = 0
+    lo: int = -4
+    hi: int = 4
+    note: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        """Multiply-adds with the stored (nonzero) weights only: 2 * M * N * K/2."""
+        return self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        sc = 4 if self.c == "f32" else 2
+        return 2 * self.M * self.K + self.N * self.K + self.N * self.K // 8 + sc * self.M * self.N
+
+    def with_(self, **kw) -> "SpCase":
+        return replace(self, **kw)
+
+
+SP_CONFIGS = {
+    "sp1": SpCase("sp1", 256, 256, 256, relu=1, seed=1601,
+                  note="C=ReLU(A W^T) 256^3 with 2:4 sparse W, fp16"),
+    "sp2": SpCase("sp2", 1000, 1500, 768, ab="bf16", c="f32", seed=1602,
+                  note="ragged 1000x1500x768, 2:4 sparse W, bf16 in, fp32 out"),
+    "sp3": SpCase("sp3", 8192, 8192, 8192, dist="normal", seed=1603,
+                  note="8192^3 with 2:4 sparse W (4096 stored values per row), fp16"),
+}
+
+
+def compress_24(positions: np.ndarray) -> np.ndarray:
+    """Positions [N, K/2] (0..3; two per group of four k, in the order of the stored
+    values) -> Wm [N, K/8] uint8."""
+    pos = np.asarray(positions, dtype=np.uint8) & 3
+    N, H = pos.shape
+    if H % 4:
+        raise ValueError("K must be a multiple of 8")
+    p = pos.reshape(N, H // 4, 4)            # two groups (four positions) per byte
+    return (p[:, :, 0] | (p[:, :, 1] << 2) | (p[:, :, 2] << 4) | (p[:, :, 3] << 6)).astype(np.uint8)
+
+
+def make_sp_inputs(case: SpCase):
+    """CPU tensors A [M, K], Wv [N, K/2] (operand dtype), Wm [N, K/8] uint8, plus the dense
+    weights [N, K] as float64 (for tests of the format)."""
+    if case.K % 8:
+        raise ValueError("K must be a multiple of 8")
+    g = torch.Generator().manual_seed(case.seed)
+    dt = DTYPES[case.ab]
+    M, N, K = case.M, case.N, case.K
+    if case.dist == "smallint":
+        A = torch.randint(case.lo, case.hi + 1, (M, K), generator=g).to(dt)
+    elif case.dist == "normal":
+        A = (torch.randn((M, K), generator=g) / math.sqrt(max(K // 2, 1))).to(dt)
+    else:
+        A = (torch.rand((M, K), generator=g) * 2.0 - 1.0).to(dt)
+    # two distinct ascending positions per group: one of the six pairs
+    pairs = torch.tensor([[0, 1], [0, 2], [0, 3], [1, 2], [1, 3], [2, 3]], dtype=torch.int64)
+    choice = torch.randint(0, 6, (N, K // 4), generator=g)
+    pos = pairs[choice].reshape(N, K // 2)
+    if case.dist == "smallint":
+        vals = torch.randint(case.lo, case.hi + 1, (N, K // 2), generator=g).to(dt)
+    elif case.dist == "normal":
+        vals = torch.randn((N, K // 2), generator=g).to(dt)
+    else:
+        vals = (torch.rand((N, K // 2), generator=g) * 2.0 - 1.0).to(dt)
+    Wm = compress_24(pos.numpy())
+    dense = np.zeros((N, K), dtype=np.float64)
+    q = np.arange(K // 2) // 2
+    rows = np.arange(N)[:, None]
+    np.add.at(dense, (rows, 4 * q[None, :] + pos.numpy()), vals.double().numpy())
+    return A.contiguous(), vals.contiguous(), torch.from_numpy(Wm).contiguous(), dense
