@@ -293,6 +293,38 @@ tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, in
 tlg_status tlg_gemm_w4(const void *A, const void *Wq, const void *S, const void *Z, void *C, int64_t M, int64_t N,
                        int64_t K, int64_t G, int32_t ab_dtype, int32_t c_dtype, int32_t epilogue, void *stream);
 
+/*
+ * 2:4 structured-sparse GEMM: the pages' T.gemm_sp (a "2:4 structured sparse
+ * GEMM" on the hardware's sparse matrix instructions; overview page, table of
+ * compute primitives), here on gfx950's v_smfmac_f32_16x16x64.  The sparse
+ * operand is the weight matrix W [N, K] of C = act(A W^T): every group of four
+ * consecutive k of a row holds two stored values (the others are zero).
+ *
+ * Format: Wv [N, K/2] holds the stored values in the operand dtype, two per
+ * group in order (Wv[n*(K/2) + 2q], Wv[n*(K/2) + 2q + 1] for group q, which
+ * covers k = 4q .. 4q+3).  Wm [N, K/8] bytes hold their positions inside the
+ * group: byte n*(K/8) + q/2 carries group q's first position at bits
+ * 4*(q%2) .. +1 and its second at bits 4*(q%2) + 2 .. +3.  Two values at one
+ * position add.
+ *
+ * Value computed, for 0 <= m < M, 0 <= n < N:
+ *   acc(m,n) = sum_k A[m*K + k] * w(n,k)      (fp32 accumulate)
+ *   C[m*N + n] = convert_rne(epilogue == RELU ? max(acc, +0) : acc)
+ * A [M, K] and C are dense row-major.  ab_dtype (A and Wv) in {TLG_F16,
+ * TLG_BF16}; c_dtype in {TLG_F16, TLG_BF16, TLG_F32}; epilogue NONE or RELU.
+ * Limits: K % 64 == 0 (whole K tiles), M and N <= 2^24, K <= 2^22.  A and Wv
+ * must be 16-byte aligned, Wm 4-byte aligned, C aligned to its element; C must
+ * not overlap A, Wv or Wm.
+ *
+ * Ownership as tlg_gemm_run: the call allocates nothing, does not synchronise
+ * and enqueues at most one kernel on `stream`.  M == 0 or N == 0 enqueues
+ * nothing; K == 0 writes act(0).  Errors: TLG_ERR_INVALID_ARG (sizes, enums,
+ * overlap), TLG_ERR_UNSUPPORTED (K % 64 != 0), TLG_ERR_NULL, TLG_ERR_MISALIGNED,
+ * TLG_ERR_HIP.  Nothing is enqueued on error.
+ */
+tlg_status tlg_gemm_sp(const void *A, const void *Wv, const void *Wm, void *C, int64_t M, int64_t N, int64_t K,
+                       int32_t ab_dtype, int32_t c_dtype, int32_t epilogue, void *stream);
+
 /* Release a plan (and its workspace, if any; the caller first makes sure no run of
  * the plan is still in flight).  NULL is accepted (no-op, TLG_OK). */
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan);

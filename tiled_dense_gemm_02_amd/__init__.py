@@ -93,6 +93,8 @@ def load_library():
         lib.tlg_attn_fwd.restype = i32
         lib.tlg_gemm_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp]
         lib.tlg_gemm_w4.restype = i32
+        lib.tlg_gemm_sp.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+        lib.tlg_gemm_sp.restype = i32
         lib.tlg_gemm_query.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         lib.tlg_gemm_query.restype = i32
         lib.tlg_gemm_describe.argtypes = [vp]
@@ -410,3 +412,45 @@ def gemm_w4_ptrs(a: int, wq: int, s: int, z: int, c: int, M: int, N: int, K: int
     """Raw-pointer form of gemm_w4 (no checks beyond the library's own); returns the status."""
     return load_library().tlg_gemm_w4(a or None, wq or None, s or None, z or None, c or None, M, N, K, group,
                                       _code(ab_dtype), _code(c_dtype), int(relu), ctypes.c_void_p(stream_handle))
+
+
+def gemm_sp(A: torch.Tensor, Wv: torch.Tensor, Wm: torch.Tensor, C: torch.Tensor | None = None, *,
+            epilogue: str = "none", out_dtype=torch.float16, stream=None) -> torch.Tensor:
+    """2:4 structured-sparse GEMM C = act(A Wᵀ) (tlg_gemm_sp).  A [M, K] fp16/bf16; Wv [N, K/2]
+    stored values (A's dtype); Wm [N, K/8] uint8 positions.  Returns C (allocated when not given)."""
+    M, K = A.shape
+    N = Wv.shape[0]
+    for name, t, shape, dt in (("A", A, (M, K), None), ("Wv", Wv, (N, K // 2), A.dtype),
+                               ("Wm", Wm, (N, K // 8), torch.uint8)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor, got {t.device}")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if dt is not None and t.dtype != dt:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dt}")
+        if t.numel() and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if tuple(C.shape) != (M, N) or (C.numel() and not C.is_contiguous()):
+        raise ValueError("C must be a contiguous [M, N] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lib = load_library()
+    with torch.cuda.device(A.device):
+        st = lib.tlg_gemm_sp(A.data_ptr() or None, Wv.data_ptr() or None, Wm.data_ptr() or None,
+                             C.data_ptr() or None, M, N, K, _code(A.dtype), _code(C.dtype), EPILOGUES[epilogue],
+                             ctypes.c_void_p(s))
+    if st != 0:
+        raise TlgError("tlg_gemm_sp", st)
+    return C
+
+
+def gemm_sp_ptrs(a: int, wv: int, wm: int, c: int, M: int, N: int, K: int, ab_dtype, c_dtype, relu: int = 0,
+                 stream_handle: int = 0) -> int:
+    """Raw-pointer form of gemm_sp (no checks beyond the library's own); returns the status."""
+    return load_library().tlg_gemm_sp(a or None, wv or None, wm or None, c or None, M, N, K, _code(ab_dtype),
+                                      _code(c_dtype), int(relu), ctypes.c_void_p(stream_handle))

@@ -524,6 +524,38 @@ tlg_status tlg_gemm_w4(const void* A, const void* Wq, const void* S, const void*
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }
 
+tlg_status tlg_gemm_sp(const void* A, const void* Wv, const void* Wm, void* C, int64_t M, int64_t N, int64_t K,
+                       int32_t ab_dtype, int32_t c_dtype, int32_t epilogue, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
+    if (ab_dtype != TLG_F16 && ab_dtype != TLG_BF16) return TLG_ERR_INVALID_ARG;
+    if (c_dtype != TLG_F16 && c_dtype != TLG_BF16 && c_dtype != TLG_F32) return TLG_ERR_INVALID_ARG;
+    if (epilogue != TLG_EPI_NONE && epilogue != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
+    if (K % 64 != 0) return TLG_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return TLG_OK;
+    if (ceil_div(M, 256) * ceil_div(N, 256) > INT32_MAX) return TLG_ERR_INVALID_ARG;
+    if (!C || (K > 0 && (!A || !Wv || !Wm))) return TLG_ERR_NULL;
+    const uintptr_t a = (uintptr_t)A, wv = (uintptr_t)Wv, wm = (uintptr_t)Wm, c = (uintptr_t)C;
+    const int cb = elem_bytes(c_dtype);
+    if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
+    if (K > 0 && ((a % 16) || (wv % 16) || (wm % 4))) return TLG_ERR_MISALIGNED;
+    const uint64_t a_bytes = (uint64_t)M * (uint64_t)K * 2u, wv_bytes = (uint64_t)N * (uint64_t)K;
+    const uint64_t wm_bytes = (uint64_t)N * (uint64_t)K / 8u, c_bytes = (uint64_t)M * (uint64_t)N * (uint64_t)cb;
+    if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, wv, wv_bytes) ||
+        ranges_overlap(c, c_bytes, wm, wm_bytes))
+        return TLG_ERR_INVALID_ARG;
+    SpParams sp{};
+    sp.A = A; sp.Wv = Wv; sp.Wm = Wm; sp.C = C;
+    sp.M = (int)M; sp.N = (int)N; sp.K = (int)K;
+    sp.relu = epilogue == TLG_EPI_RELU;
+    sp.c_dtype = c_dtype;
+    sp.c_vec = (N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    sp.tiles_m = (int)ceil_div(M, 256);
+    sp.tiles_n = (int)ceil_div(N, 256);
+    const hipError_t err = launch_sp(sp, ab_dtype == TLG_F16 ? DT_F16 : DT_BF16, (hipStream_t)stream);
+    return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan)
 {
     delete plan;

@@ -142,4 +142,17 @@ struct W4Params {
 };
 hipError_t launch_w4(const W4Params& p, int ab_dtype, hipStream_t stream);
 
+// 2:4 structured-sparse GEMM (gemm_sp.hip): C = act(A W^T), A [M, K], Wv [N, K/2]
+// compressed values, Wm [N, K/8] positions; K % 64 == 0.
+struct SpParams {
+    const void* A;
+    const void* Wv;
+    const void* Wm;
+    void* C;
+    int M, N, K;
+    int relu, c_dtype, c_vec;
+    int tiles_m, tiles_n;
+};
+hipError_t launch_sp(const SpParams& p, int ab_dtype, hipStream_t stream);
+
 }  // namespace tlg
