@@ -48,9 +48,11 @@ KERNEL_SOURCES = {
     9: ["gemm_mx.hpp", "gemm_mx.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     "attn": ["attn_fwd.hpp", "attn_fwd.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     "w4": ["gemm_w4.hip", "gemm_lds.hpp", "tlg_device.hpp"],
+    "sp": ["gemm_sp.hip", "gemm_lds.hpp", "tlg_device.hpp"],
 }
 ATTN_VARIANT = "attn"
 W4_VARIANT = "w4"
+SP_VARIANT = "sp"
 
 
 def kernel_hash(variant: int) -> str:
@@ -80,7 +82,8 @@ def parse():
     # ~40 ms of launches: the clock settles only after tens of ms of MFMA load
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c5a", help="c1..c5b, a block-scaled workload mx1..mx3, "
-                    "an attention workload fa1..fa4, or a dequant GEMM workload w4a..w4c")
+                    "an attention workload fa1..fa4, a dequant GEMM workload w4a..w4c, "
+                    "or a 2:4 sparse GEMM workload sp1..sp3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -360,6 +363,101 @@ def bench_w4(args, case, log):
     return out
 
 
+def measure_sp(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=0.0):
+    """measure() for a 2:4 structured-sparse GEMM workload (tlg_gemm_sp)."""
+    import torch
+    import tiled_dense_gemm_02_amd as tlg
+    import tlg_workloads as W
+
+    dev = torch.device("cuda:0")
+    A, Wv, Wm, _ = W.make_sp_inputs(case)
+    set_bytes = A.numel() * 2 + Wv.numel() * 2 + Wm.numel()
+    nsets = max(1, min(8, math.ceil(rotate_bytes / max(set_bytes, 1))))
+    sets = [tuple(t.to(dev) for t in (A, Wv, Wm)) for _ in range(nsets)]
+    C = torch.empty((case.M, case.N), dtype=plan_out_dtype(case), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    tlg.gemm_sp(*sets[0], C, epilogue="relu" if case.relu else "none", stream=stream)
+    ptrs = [tuple(t.data_ptr() for t in st) for st in sets]
+    c_ptr, sh = C.data_ptr(), stream.cuda_stream
+    status = 0
+
+    def launch(i):
+        a, wv, wm = ptrs[i % nsets]
+        return tlg.gemm_sp_ptrs(a, wv, wm, c_ptr, case.M, case.N, case.K, A.dtype, C.dtype, case.relu, sh)
+
+    for i in range(warmup):
+        status |= launch(i)
+    torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
+        for i in range(20):
+            status |= launch(i)
+        w1.record(stream)
+        torch.cuda.synchronize()
+        per = max(w0.elapsed_time(w1) / 20, 1e-3)
+        for i in range(int(math.ceil(max(0.0, min_warm_ms - 20 * per) / per))):
+            status |= launch(i)
+        torch.cuda.synchronize()
+    if log:
+        log(f"[bench] {case.name}: sp M={case.M} N={case.N} K={case.K} sets={nsets}")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        status |= launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    if status != 0:
+        raise RuntimeError(f"tlg_gemm_sp failed during the timed launches (status {status})")
+    return {"ms": start.elapsed_time(end) / steps, "wall_s": time.perf_counter() - t0, "C": C, "nsets": nsets,
+            "describe": f"gemm_sp block=256x256x64 threads=512 {case.ab}->{case.c}"}
+
+
+def bench_sp(args, case, log):
+    """The JSON line of a 2:4 sparse GEMM workload.  FLOPs count the stored (nonzero)
+    weights only (M*N*K), priced against the dense MFMA peak of the operand dtype, which
+    is the same fraction as the instruction's dense-equivalent rate against its own peak."""
+    r = measure_sp(case, args.steps, args.warmup, log=log, min_warm_ms=100.0)
+    ms = r["ms"]
+    tflops = case.flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[case.ab]
+    roof = {"bound": "mfma", "achieved": tflops, "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak,
+            "traffic": stored_traffic(args.workload, SP_VARIANT), "kernel": "gemm_sp",
+            "per_launch": {"flops": case.flops, "algorithmic_bytes": case.algorithmic_bytes, "avg_kernel_ms": ms}}
+    out = {"metric": "2:4 sparse GEMM TFLOP/s of stored-weight multiply-adds (fp32 accumulate) and % of dense MFMA peak",
+           "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": case.ab,
+           "data": "synthetic (seeded, see tlg_workloads.py)",
+           "config": {"workload": f"{case.name}: {case.note}", "M": case.M, "N": case.N, "K": case.K,
+                      "ab_dtype": case.ab, "c_dtype": case.c, "plan": r["describe"],
+                      "operand_sets_rotated": r["nsets"], "dense_equivalent_TFLOP/s": 2 * tflops},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import tlg_workloads as W
+        from oracle import build_oracle, oracle as O
+        if not os.path.exists(O.LIB_PATH):
+            build_oracle.build()
+        rows = {"sp1": 256, "sp2": 1000, "sp3": 64}[case.name]
+        A, Wv, Wm, _ = W.make_sp_inputs(case)
+        t0 = time.perf_counter()
+        o = O.spgemm(case.M, case.N, case.K, W.bits16(A), W.bits16(Wv), Wm.numpy(), dtype=case.ab, relu=case.relu,
+                     rows=(0, rows))
+        dt = time.perf_counter() - t0
+        gpu = r["C"][:rows].float().cpu().numpy().astype(np.float64)
+        ok = bool((np.abs(gpu - o) <= O.tolerance(o, case.K, case.c)).all())
+        flops = float(rows) * case.N * case.K
+        out["cpu_baseline"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {rows} of {case.M} output rows of {case.name} "
+                                         f"({flops / 1e9:.1f} GFLOP of stored-weight multiply-adds, fp64 loops, {dt:.1f} s)",
+                               "seconds": dt, "sample_matches_gpu": ok}
+    return out
+
+
 def plan_out_dtype(case):
     import torch
     return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.c]
@@ -480,6 +578,9 @@ def main():
         log("[bench] copy calibration: 1 GiB read + 1 GiB write done")
         del x, y
 
+    if args.workload in W.SP_CONFIGS:
+        print(json.dumps(bench_sp(args, W.SP_CONFIGS[args.workload], log)), flush=True)
+        return
     if args.workload in W.W4_CONFIGS:
         print(json.dumps(bench_w4(args, W.W4_CONFIGS[args.workload], log)), flush=True)
         return
@@ -520,18 +621,20 @@ def main():
 
     if not args.no_secondary:
         sec = []
-        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3", "fa3", "w4a"):
+        for name in ("c3", "c5b", "c2", "c4", "c1", "mx3", "fa3", "w4a", "sp3"):
             if name == args.workload:
                 continue
             sec_mx, sec_attn, sec_w4 = name in W.MX_CONFIGS, name in W.ATTN_CONFIGS, name in W.W4_CONFIGS
+            sec_sp = name in W.SP_CONFIGS
             c2 = (W.MX_CONFIGS[name] if sec_mx else W.ATTN_CONFIGS[name] if sec_attn else
-                  W.W4_CONFIGS[name] if sec_w4 else W.CONFIGS[name])
-            fn = measure_mx if sec_mx else measure_attn if sec_attn else measure_w4 if sec_w4 else measure
+                  W.W4_CONFIGS[name] if sec_w4 else W.SP_CONFIGS[name] if sec_sp else W.CONFIGS[name])
+            fn = (measure_mx if sec_mx else measure_attn if sec_attn else measure_w4 if sec_w4 else
+                  measure_sp if sec_sp else measure)
             rr = fn(c2, max(10, args.steps // 2), 40, log=log, min_warm_ms=100.0)
             t = rr["ms"] * 1e-3
             entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": c2.flops / t / 1e12,
                      "GB/s": c2.algorithmic_bytes / t / 1e9,
-                     "plan": rr["describe"] if (sec_attn or sec_w4) else rr["plan"].describe()}
+                     "plan": rr["describe"] if (sec_attn or sec_w4 or sec_sp) else rr["plan"].describe()}
             entry["mfma_frac"] = entry["TFLOP/s"] / PEAK_TFLOPS[c2.fmt if sec_mx else c2.dtype if sec_attn else c2.ab]
             entry["hbm_frac"] = entry["GB/s"] / PEAK_HBM_GBS
             sec.append(entry)
