@@ -284,3 +284,31 @@ def test_attention_validation_happens_before_any_launch():
     assert f(p, ok[1], ok[2], p + 4096, 1, 64, 2, 64, 1, 1, 0.125, None) == -1   # O overlaps Q
     with pytest.raises(ValueError):
         tlg.attention(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
+
+
+def test_dequant_and_sparse_validation_happens_before_any_launch():
+    """tlg_gemm_w4 and tlg_gemm_sp reject bad requests with distinct statuses before
+    touching a device (these pointers are never dereferenced)."""
+    lib = tlg.load_library()
+    p = 1 << 20
+    a, w, s, z, c = p, p + (1 << 24), p + (2 << 24), p + (3 << 24), p + (4 << 24)
+    w4 = lib.tlg_gemm_w4
+    assert w4(a, w, s, z, c, -1, 64, 256, 128, 1, 1, 0, None) == -1          # negative M
+    assert w4(a, w, s, z, c, 16, 64, 256, 96, 1, 1, 0, None) == -1           # group not a multiple of 32
+    assert w4(a, w, s, z, c, 16, 64, 200, 32, 1, 1, 0, None) == -1          # K % G
+    assert w4(a, w, s, z, c, 16, 64, 256, 128, 3, 1, 0, None) == -1         # fp32 operands
+    assert w4(a, w, s, z, c, 16, 64, 256, 128, 1, 1, 2, None) == -1         # epilogue
+    assert w4(a, w, s, z, c, 16, 64, 32 * 256, 32, 1, 1, 0, None) == -2     # K / G = 256 > 255
+    assert w4(None, None, None, None, None, 0, 64, 256, 128, 1, 1, 0, None) == 0
+    assert w4(None, w, s, z, c, 16, 64, 256, 128, 1, 1, 0, None) == -3
+    assert w4(a + 8, w, s, z, c, 16, 64, 256, 128, 1, 1, 0, None) == -4
+    assert w4(a, w, s + 1, z, c, 16, 64, 256, 128, 1, 1, 0, None) == -4
+    assert w4(a, w, s, z, a + 64, 16, 64, 256, 128, 1, 1, 0, None) == -1    # C overlaps A
+    sp = lib.tlg_gemm_sp
+    assert sp(a, w, z, c, 64, 64, -64, 1, 1, 0, None) == -1
+    assert sp(a, w, z, c, 64, 64, 96, 1, 1, 0, None) == -2                 # K % 64
+    assert sp(a, w, z, c, 64, 64, 128, 4, 1, 0, None) == -1                # FP8 operands
+    assert sp(None, None, None, None, 0, 64, 128, 1, 1, 0, None) == 0
+    assert sp(a, None, z, c, 64, 64, 128, 1, 1, 0, None) == -3
+    assert sp(a, w, z + 2, c, 64, 64, 128, 1, 1, 0, None) == -4           # metadata 4-byte aligned
+    assert sp(a, w, z, w + 16, 64, 64, 128, 1, 1, 0, None) == -1          # C overlaps Wv
