@@ -12,11 +12,11 @@
 //
 // gfx950 mapping.  A workgroup owns 16 rows x 64 columns of C and streams the
 // 64 packed weight rows once, like the fp16 skinny kernel, through an LDS ring
-// of 32 KiB stages filled by 1 KiB direct loads: a stage holds 512 of K, i.e.
-// 256 bytes of each weight row and 1 KiB of each A row.  The workgroup's scales
-// and zero points are gathered into an LDS table (one dword per row and group:
-// z in the low half, s in the high half) while the first stages load; the table
-// takes what the ring leaves of 160 KiB (4 slots when K/G <= 128, else 3).
+// of three 32 KiB stages filled by 1 KiB direct loads: a stage holds 512 of K,
+// i.e. 256 bytes of each weight row and 1 KiB of each A row.  The workgroup's
+// scales and zero points are gathered into an LDS table (one dword per group and
+// row) while the first stages load; the table takes the other 64 KiB of the
+// 160 KiB.
 // The sixteen waves (four per SIMD, to hide the latency of each wave's chain of
 // LDS read, dequantization and MFMA) take different 32-wide K steps of a stage.  For an MFMA
 // 16x16x32 weight fragment a lane needs eight consecutive codes of one row --
@@ -41,14 +41,17 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // mask (0x000F000F, in an SGPR) and magic (0x64006400, in a VGPR) come in as
 // opaque values: with literal constants the compiler cannot fuse the mask and
 // the or into one v_and_or_b32 (a VOP3 instruction takes no literal on gfx950).
+// e is the table entry of the fragment's row and group: for fp16 the fp16 value
+// 1024 + z in the low half and s in the high half (the packed subtract and
+// multiply read each half for both lanes through their operand selects); for
+// bf16, z in the low half and s in the high half.
 template <int T>
 __device__ inline u32x4 dequant8(uint32_t d, uint32_t e, uint32_t mask, uint32_t magic)
 {
     u32x4 w;
     if constexpr (T == DT_F16) {
-        const uint32_t z = e & 0xffffu;
-        const h16x2 mz = __builtin_bit_cast(h16x2, (0x6400u + z) * 0x10001u);
-        const h16x2 s2 = __builtin_bit_cast(h16x2, (e >> 16) * 0x10001u);
+        const h16x2 ev = __builtin_bit_cast(h16x2, e);
+        const h16x2 mz = ev.xx, s2 = ev.yy;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const h16x2 x = __builtin_bit_cast(h16x2, ((d >> (4 * i)) & mask) | magic);
@@ -70,8 +73,8 @@ __device__ inline u32x4 dequant8(uint32_t d, uint32_t e, uint32_t mask, uint32_t
 
 }  // namespace
 
-// S: ring slots (S-1 stages in flight); the scale / zero table gets the rest of
-// the 160 KiB: 64 KiB (K/G <= 256) with 3 slots, 32 KiB (K/G <= 128) with 4.
+// S: ring slots (S-1 stages in flight) of KST-wide stages; the scale / zero table
+// gets the rest of the 160 KiB.
 template <int T_IN, int S, int KST>
 __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
 {
@@ -94,15 +97,17 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     static_assert(WAVES * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+    // Scale / zero table, [group][row of the workgroup], row r of group gi at
+    // gi * NB + (r ^ (gi & 15)): the 16 rows a fragment reads at one group are a
+    // permutation of 16 consecutive dwords (16 banks), and the gather below, whose
+    // consecutive threads take consecutive groups of one row, writes 16 banks.
     __shared__ __attribute__((aligned(16))) uint32_t tab[TABLE / 4];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, r16 = lane & 15;
     const int m0 = blockIdx.y * MR, n0 = blockIdx.x * NB;
     const int K = p.K, G = p.G, KG = K / G;
-    // Table row stride: odd, so the 16 rows a fragment reads at one group sit in
-    // 16 different banks (an even stride such as 64 put them all in one bank).
-    const int KGP = KG | 1;
     const int NST = (K + KST - 1) / KST;
 
     const uint32_t bld = (uint32_t)K / 2u, ald = (uint32_t)K * 2u;
@@ -115,28 +120,50 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     // Load q = i * WAVES + wave of a stage: q < BL fills weight rows q*BRPL ..
     // (lane -> row q*BRPL + lane/BCH, chunk position lane%BCH); otherwise 1 KiB of
     // A row (q-BL)/APL (lane -> chunk position ((q-BL)%APL)*64 + lane).  Chunk c of
-    // row r sits at c ^ (r & 15).
+    // row r sits at c ^ (r & 15).  A lane's offset inside the stage and the first k
+    // of its chunk do not change from stage to stage; rows past M or N read zeros.
+    uint32_t voff[LPW], kc[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int q = i * WAVES + wave;
+        if (q < BL) {
+            const int row = q * BRPL + lane / BCH;
+            const int c = (lane % BCH) ^ (row & 15);
+            voff[i] = n0 + row < p.N ? (uint32_t)row * bld + (uint32_t)c * 16u : kOOB;
+            kc[i] = (uint32_t)c * 32u;
+        } else {
+            const int row = (q - BL) / APL;
+            const int c = (((q - BL) % APL) * 64 + lane) ^ (row & 15);
+            voff[i] = m0 + row < p.M ? (uint32_t)row * ald + (uint32_t)c * 16u : kOOB;
+            kc[i] = (uint32_t)c * 8u;
+        }
+    }
     auto issue = [&](int st) {
         const int k0 = st * KST;
         const uint64_t ob = (uint64_t)st * BRB, oa = (uint64_t)st * ARB;
         const uint32_t slot = lds0 + (uint32_t)((st % S) * STAGE);
-        const i32x4 rb = rsrc_words(b_base + ob, b_bytes > ob ? b_bytes - ob : 0);
-        const i32x4 ra = rsrc_words(a_base + oa, a_bytes > oa ? a_bytes - oa : 0);
+        // st < NST, so ob < K/2 <= b_bytes and oa < 2K <= a_bytes (n0 < N, m0 < M).
+        const i32x4 rb = rsrc_words(b_base + ob, b_bytes - ob);
+        const i32x4 ra = rsrc_words(a_base + oa, a_bytes - oa);
+        if (k0 + KST <= K) {
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-            const int q = i * WAVES + wave;
-            if (q < BL) {
-                const int row = q * BRPL + lane / BCH;
-                const int c = (lane % BCH) ^ (row & 15);
-                const bool ok = n0 + row < p.N && k0 + c * 32 < K;
-                dma16(rb, ok ? (uint32_t)row * bld + (uint32_t)c * 16u : kOOB,
-                      __builtin_amdgcn_readfirstlane(slot + (uint32_t)(q * 1024)));
-            } else {
-                const int row = (q - BL) / APL;
-                const int c = (((q - BL) % APL) * 64 + lane) ^ (row & 15);
-                const bool ok = m0 + row < p.M && k0 + c * 8 < K;
-                dma16(ra, ok ? (uint32_t)row * ald + (uint32_t)c * 16u : kOOB,
-                      __builtin_amdgcn_readfirstlane(slot + (uint32_t)(BBYTES + (q - BL) * 1024)));
+            for (int i = 0; i < LPW; ++i) {
+                const int q = i * WAVES + wave;
+                if (q < BL)
+                    dma16(rb, voff[i], __builtin_amdgcn_readfirstlane(slot + (uint32_t)(q * 1024)));
+                else
+                    dma16(ra, voff[i], __builtin_amdgcn_readfirstlane(slot + (uint32_t)(BBYTES + (q - BL) * 1024)));
+            }
+        } else {
+            // The stage reaches past K: chunks at or past K read zeros.
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                const int q = i * WAVES + wave;
+                const uint32_t off = k0 + (int)kc[i] < K ? voff[i] : kOOB;
+                if (q < BL)
+                    dma16(rb, off, __builtin_amdgcn_readfirstlane(slot + (uint32_t)(q * 1024)));
+                else
+                    dma16(ra, off, __builtin_amdgcn_readfirstlane(slot + (uint32_t)(BBYTES + (q - BL) * 1024)));
             }
         }
     };
@@ -154,18 +181,33 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     // Scale / zero table of this workgroup's rows (rows past N: zero weights).
     for (int i = threadIdx.x; i < NB * KG; i += WAVES * 64) {
         const int r = i / KG, gi = i - r * KG;
-        const int slot_i = r * KGP + gi;
         uint32_t e = 0;
         if (n0 + r < p.N) {
             const int64_t idx = (int64_t)(n0 + r) * KG + gi;
-            e = (uint32_t)((const uint8_t*)p.Z)[idx] | ((uint32_t)((const uint16_t*)p.S)[idx] << 16);
+            const uint32_t z = ((const uint8_t*)p.Z)[idx];
+            e = (T_IN == DT_F16 ? 0x6400u + z : z) | ((uint32_t)((const uint16_t*)p.S)[idx] << 16);
         }
-        tab[slot_i] = e;
+        tab[gi * NB + (r ^ (gi & 15))] = e;
     }
     // The gathers above overlap the first stages' direct loads.  They are waited
     // for here, together with everything issued before them: the ring's vmcnt
     // accounting below counts direct loads only.
     wait_vmcnt<0>();
+
+    // Per K step u of this wave: LDS offsets of its A and weight fragments inside
+    // a slot, and its group index, advanced stage by stage (the quotient and
+    // remainder of st * KST + ks * 32 by G).
+    uint32_t aoff[SPW], woff[SPW];
+    int gq[SPW], gr[SPW];
+    const int kst_q = KST / G, kst_r = KST - kst_q * G;
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) {
+        const int ks = wave * SPW + u;
+        aoff[u] = (uint32_t)(BBYTES + r16 * ARB + (((ks * 4 + g) ^ r16) << 4));
+        woff[u] = (uint32_t)(r16 * BRB + ((ks ^ r16) << 4) + 4 * g);
+        gq[u] = (ks * 32) / G;
+        gr[u] = ks * 32 - gq[u] * G;
+    }
 
     for (int st = 0; st < NST; ++st) {
         // Stage st has landed once at most S-2 newer stages are in flight; the
@@ -177,24 +219,24 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
             wait_vmcnt<0>();
         __syncthreads();
         if (st + S - 1 < NST) issue(st + S - 1);
-        const char* bslot = smem + (st % S) * STAGE;
-        const char* aslot = bslot + BBYTES;
+        const char* slot = smem + (st % S) * STAGE;
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
-            const int ks = wave * SPW + u;
             // K steps past the end of K read zeros from A and W (range-checked
             // loads); their group index is clamped so the table read stays inside.
-            const int gi = min((st * KST + ks * 32) / G, KG - 1);
-            const int ac = ks * 4 + g;
-            const u32x4 af = *(const u32x4*)(aslot + r16 * ARB + ((ac ^ r16) << 4));
+            const int gi = min(gq[u], KG - 1);
+            const uint32_t* trow = tab + gi * NB + (r16 ^ (gi & 15));
+            const u32x4 af = *(const u32x4*)(slot + aoff[u]);
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-                const int row = j * 16 + r16;
-                const uint32_t d = *(const uint32_t*)(bslot + row * BRB + ((ks ^ (row & 15)) << 4) + 4 * g);
-                const u32x4 wf = dequant8<T_IN>(d, tab[row * KGP + gi], mask, magic);
+                const uint32_t d = *(const uint32_t*)(slot + woff[u] + j * 16 * BRB);
+                const u32x4 wf = dequant8<T_IN>(d, trow[j * 16], mask, magic);
                 // Weight fragment first: acc[j][e] is C[m0 + lane%16][n0 + 16j + 4(lane/16) + e].
                 acc[j] = mfma16x16x32<T_IN>(wf, af, acc[j]);
             }
+            gq[u] += kst_q;
+            gr[u] += kst_r;
+            if (gr[u] >= G) { gr[u] -= G; ++gq[u]; }
         }
     }
     wait_vmcnt<0>();
@@ -240,10 +282,12 @@ static hipError_t launch_w4_s(const W4Params& p, int ab_dtype, hipStream_t strea
     return hipGetLastError();
 }
 
+// Three slots of 512-wide stages leave a 64 KiB table (K/G <= 256).  On the
+// 16 x 16384 x 8192 decode shape they beat two slots of 1024-wide stages (one
+// stage in flight) and four of 512 (less work per wave between barriers).
 hipError_t launch_w4(const W4Params& p, int ab_dtype, hipStream_t stream)
 {
-    const int groups = (p.K / p.G) | 1;          // the kernel's padded table row
-    if (kW4NB * groups * 4 <= 32 * 1024) return launch_w4_s<2, 1024>(p, ab_dtype, stream);
+    static_assert(kW4NB * kW4MaxGroups * 4 <= kW4TableBytes, "table");
     return launch_w4_s<3, 512>(p, ab_dtype, stream);
 }
 

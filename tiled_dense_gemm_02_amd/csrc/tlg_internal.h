@@ -129,7 +129,7 @@ hipError_t launch_attn(const AttnParams& p, int dim, int dtype, int causal, hipS
 constexpr int kW4NB = 64;                      // columns of C per workgroup
 constexpr int kW4Threads = 1024;               // 16 waves
 constexpr int kW4TableBytes = 64 * 1024;       // LDS table: one dword per weight row and group
-constexpr int kW4MaxGroups = kW4TableBytes / 4 / kW4NB - 1;   // rows padded to an odd number of groups
+constexpr int kW4MaxGroups = 255;              // the documented limit (the table holds 256 groups)
 struct W4Params {
     const void* A;
     const void* Wq;
