@@ -237,8 +237,10 @@ tlg_status tlg_gemm_tune(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
  *   keys allowed:  j in [0, seq), and j <= i when causal != 0 (the page's rule)
  *   s_j  = softmax_scale * sum_d Q[b,i,h,d] * K[b,j,h,d]          (fp32)
  *   O[b,i,h,:] = convert_rne( sum_j p_j V[b,j,h,:] / sum_j p_j ),
- *   p_j  = exp(s_j - max_j s_j), rounded to the operand type before the second
- *          product (the page rounds its probability tile to fp16), fp32 sums.
+ *   p_j  = exp(s_j - m), rounded to the operand type before the second product
+ *          (the page rounds its probability tile to fp16), fp32 sums; m is a
+ *          reference maximum that the kernel keeps within 8 (log2 units) below
+ *          max_j s_j * log2(e), so p_j <= 256 and O is the softmax whatever m is.
  * The page's scale is 1/sqrt(dim); the caller passes it (any finite value).
  *
  * Layout: Q, K, V and O are dense [batch, seq, heads, dim] tensors; element

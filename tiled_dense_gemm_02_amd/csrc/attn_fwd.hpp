@@ -151,23 +151,33 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
     }
 
     // Direct loads: load i of this lane fills row r0 + 4 i RPK of a tile, chunk
-    // position lane % CH; the swizzle of that row is the same for every i.
+    // position lane % CH; the swizzle of that row is the same for every i.  The
+    // block's first key goes into the buffer resource, so the lane offsets do not
+    // change from block to block; the resource ends with position S-1's row of
+    // this head, so keys at or past S (whose rows start at least a row stride
+    // further on) read zeros.
     const int r0 = wave * RPK + lane / CH;
     const int ck = (lane % CH) ^ Lay::swz_k(r0);
     const int cv = (lane % CH) ^ Lay::swz_v(r0);
-    const i32x4 rk = rsrc_words((const char*)p.K + head_off, head_bytes);
-    const i32x4 rv = rsrc_words((const char*)p.V + head_off, head_bytes);
+    uint32_t offk[LK], offv[LK];
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+        const uint32_t base = (uint32_t)(r0 + i * NW * RPK) * stride;
+        offk[i] = base + (uint32_t)ck * 16u;
+        offv[i] = base + (uint32_t)cv * 16u;
+    }
+    const char* kbase = (const char*)p.K + head_off;
+    const char* vbase = (const char*)p.V + head_off;
     const uint32_t lds0 = lds_addr_of(smem);
     auto issue = [&](int kb) {
-        const uint32_t slot = lds0 + (uint32_t)((kb & 1) * SLOT) + (uint32_t)wave * 1024u;
+        const uint32_t slot = lds0 + (uint32_t)((kb & 1) * SLOT) + (uint32_t)__builtin_amdgcn_readfirstlane(wave) * 1024u;
+        const uint64_t ob = (uint64_t)kb * BN * stride;   // < head_bytes: block kb starts before S
+        const i32x4 rk = rsrc_words(kbase + ob, head_bytes - ob);
+        const i32x4 rv = rsrc_words(vbase + ob, head_bytes - ob);
 #pragma unroll
         for (int i = 0; i < LK; ++i) {
-            const int key = kb * BN + r0 + i * NW * RPK;
-            const uint32_t base = (uint32_t)key * stride;
-            dma16(rk, key < S ? base + (uint32_t)ck * 16u : kOOB,
-                  __builtin_amdgcn_readfirstlane(slot + (uint32_t)(i * NW * 1024)));
-            dma16(rv, key < S ? base + (uint32_t)cv * 16u : kOOB,
-                  __builtin_amdgcn_readfirstlane(slot + (uint32_t)(TILE + i * NW * 1024)));
+            dma16(rk, offk[i], __builtin_amdgcn_readfirstlane(slot + (uint32_t)(i * NW * 1024)));
+            dma16(rv, offv[i], __builtin_amdgcn_readfirstlane(slot + (uint32_t)(TILE + i * NW * 1024)));
         }
     };
 
@@ -186,6 +196,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
     const u32x4 ones = u32x4{one2, one2, one2, one2};
     const float c = p.scale_log2;
     constexpr float SENT = NEG ? INFINITY : -INFINITY;   // masked raw score, ignored by the row extreme
+    constexpr float kSlack = 8.0f;                        // P <= 2^8 between moves of the reference
 
     const int wq0 = q0 + wave * WROWS;          // first query row of this wave
     issue(0);
@@ -244,11 +255,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
                 for (int t = 1; t < 16; ++t) mloc = NEG ? fminf(mloc, sv[t]) : fmaxf(mloc, sv[t]);
                 mloc = NEG ? wave_min4(mloc) : wave_max4(mloc);
                 const float mblk = mloc == SENT ? -INFINITY : mloc * c;
-                const float m_new = fmaxf(m_run[rt], mblk);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                // The row's reference maximum moves only when the block's maximum
+                // exceeds it by more than kSlack (log2 units, from -inf always).
+                // Until then P = 2^(s*c - reference) stays at or below 2^kSlack,
+                // well inside the operand type, and O and l keep the same
+                // reference, so O / l is unchanged; O is rescaled far less often.
+                const bool move = mblk > m_run[rt] + kSlack;
+                const float m_ref = move ? mblk : m_run[rt];
+                const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
                 alpha[rt] = __builtin_amdgcn_exp2f(m_run[rt] - m_use);
-                rescale = rescale || alpha[rt] != 1.0f;
-                m_run[rt] = m_new;
+                rescale = rescale || move;
+                m_run[rt] = m_ref;
                 float pv[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) pv[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[t], c, -m_use));
@@ -262,8 +279,8 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
                     pf[rt][kk] = u32x4{pack_op<T>(pv[8 * kk + 0], pv[8 * kk + 1]), pack_op<T>(pv[8 * kk + 2], pv[8 * kk + 3]),
                                        pack_op<T>(pv[8 * kk + 4], pv[8 * kk + 5]), pack_op<T>(pv[8 * kk + 6], pv[8 * kk + 7])};
             }
-            // O and the row sums are rescaled only when some row's maximum moved
-            // (alpha is exactly 1 otherwise).
+            // O and the row sums are rescaled only when some row's reference
+            // maximum moved (alpha is exactly 1 for the others).
             if (__any(rescale)) {
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
