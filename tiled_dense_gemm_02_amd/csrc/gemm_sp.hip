@@ -18,11 +18,12 @@
 // in the block-scaled kernel.
 //
 // The tile program is the block-scaled kernel's: 256 x 256 output tiles, a K
-// loop over 64-wide K tiles, a two-slot LDS ring filled by direct loads, 8 waves
+// loop over 64-wide K tiles, a three-slot LDS ring filled by direct loads, 8 waves
 // of 128 x 64 outputs, 32 sparse MFMAs per wave and K tile issued row-block-major
 // with the eight A fragments rotating through four buffers and the four weight
 // fragments resident, the ring barrier after MFMA 20, then the loads of the
-// tile two ahead, one per MFMA.
+// tile three ahead, one per MFMA.  A K tile takes 50 KiB (A 32, values 16,
+// positions 2), so three slots fit in 160 KiB and two tiles stay in flight.
 #include "gemm_lds.hpp"
 
 namespace tlg {
@@ -77,12 +78,14 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
     constexpr int LEAD = 3 * FN;
     constexpr int BPOS = FN * FM - LEAD;
     constexpr int R = 1;
+    constexpr int S = 3;                               // ring slots
     static_assert(FM % NBUF == 0 && LEAD == FN * (NBUF - 1), "rotation of the A fragment buffers");
-    static_assert(2 * STAGE <= 160 * 1024, "two ring slots must fit in 160 KiB");
+    static_assert(S * STAGE <= 160 * 1024, "the ring must fit in 160 KiB");
+    static_assert((S - 2) * L < 64, "vmcnt range");
     static_assert((MI - BPOS + R - 1) / R >= L, "all loads of a tile fit after the barrier");
     static_assert(WMB == NW * 256 && LW >= 1, "one 4-byte metadata load per wave covers 32 rows");
 
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -122,7 +125,7 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
         TileRes r;
         r.k0 = t * BK;
         r.ra = opa.rsrc(r.k0);
-        r.slot = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t & 1) * STAGE));
+        r.slot = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t % S) * STAGE));
         r.ok = t < TP;
         return r;
     };
@@ -162,15 +165,17 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
         fi[j] = (int)*(const unsigned short*)(slot + OpA::BYTES + WVB + row * 8 + 2 * g);
     };
 
-    {
-        const TileRes r0 = tile_res(0);
+    // Prologue: tiles 0 .. S-2 in flight; once tile 0 has landed, tile S-1 too.
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) {
+        const TileRes r0 = tile_res(t);
 #pragma unroll
         for (int i = 0; i < L; ++i) issue_one(r0, i);
     }
-    wait_vmcnt<0>();
+    wait_vmcnt<(S - 2) * L>();
     __syncthreads();
     {
-        const TileRes r1 = tile_res(1);
+        const TileRes r1 = tile_res(S - 1);
 #pragma unroll
         for (int i = 0; i < L; ++i) issue_one(r1, i);
     }
@@ -180,18 +185,19 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
     for (int j = 0; j < FN; ++j) read_w(smem, j);
 
     for (int t = 0; t < TP; ++t) {
-        const char* cur = smem + (t & 1) * STAGE;
-        const char* nxt = smem + ((t + 1) & 1) * STAGE;
-        const TileRes rl = tile_res(t + 2);
+        const char* cur = smem + (t % S) * STAGE;
+        const char* nxt = smem + ((t + 1) % S) * STAGE;
+        const TileRes rl = tile_res(t + S);
         __builtin_amdgcn_s_setprio(1);
         static_for<MI + 1>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             if constexpr (m == BPOS) {
                 // Every read of this tile's slot has been issued; once they have
-                // returned and tile t+1 has landed, the barrier publishes tile t+1
-                // and frees this slot for tile t+2.
+                // returned and tile t+1 has landed (tiles up to t+S-1 may still be
+                // in flight), the barrier publishes tile t+1 and frees this slot
+                // for tile t+S.
                 __builtin_amdgcn_s_setprio(0);
-                wait_vmcnt_lgkm0<0>();
+                wait_vmcnt_lgkm0<(S - 2) * L>();
                 __syncthreads();
                 __builtin_amdgcn_s_setprio(1);
             }
