@@ -106,6 +106,16 @@ def test_explicit_scale_and_flat_keys():
     _full(W.AttnCase("sharp-bf16", 1, 300, 2, 64, causal=1, scale=0.9, dtype="bf16", seed=1403))
 
 
+@pytest.mark.parametrize("dist", ["ramp_up", "ramp_down"])
+def test_score_ramps(dist):
+    """Scores rising along the keys by ~0.2 (log2 units) per position: a row's reference
+    maximum then moves only every few dozen keys, and unnormalised probabilities up to
+    2^8 are rounded to the operand type in between.  Falling scores: it never moves
+    after the first key, and most probabilities are tiny."""
+    _full(W.AttnCase(f"{dist}-f16", 2, 777, 2, 64, causal=1, dist=dist, seed=1420))
+    _full(W.AttnCase(f"{dist}-bf16-d128", 1, 520, 2, 128, causal=0, dist=dist, dtype="bf16", seed=1421))
+
+
 @pytest.mark.parametrize("scale", [-0.3, -2.0, 0.0])
 def test_negative_and_zero_scale(scale):
     """A negative scale turns the row maximum of the scaled scores into the scale times the

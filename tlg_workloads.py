@@ -266,7 +266,7 @@ class AttnCase:
     D: int
     causal: int = 1
     dtype: str = "f16"
-    dist: str = "normal"     # "normal" | "uniform_keys"
+    dist: str = "normal"     # "normal" | "uniform_keys" | "ramp_up" | "ramp_down"
     scale: float | None = None   # None: 1/sqrt(D), the page's choice
     seed: int = 0
     note: str = field(default="", compare=False)
@@ -314,6 +314,15 @@ def make_attn_inputs(case: AttnCase):
     v = torch.randn(case.shape, generator=g)
     if case.dist == "uniform_keys":
         k = torch.zeros(case.shape)
+    elif case.dist in ("ramp_up", "ramp_down"):
+        # Scores that rise (fall) by about 0.2 in log2 units per key position: every
+        # query is close to the first axis and key j's first coordinate is j steps.
+        sign = 1.0 if case.dist == "ramp_up" else -1.0
+        step = sign * 0.2 / (math.log2(math.e) * case.softmax_scale)
+        q = 0.1 * q
+        q[..., 0] = 1.0
+        k = 0.1 * k
+        k[..., 0] = step * torch.arange(case.S, dtype=torch.float32).view(1, case.S, 1)
     elif case.dist != "normal":
         raise ValueError(f"unknown distribution {case.dist!r}")
     dt = DTYPES[case.dtype]
