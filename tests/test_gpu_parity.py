@@ -97,13 +97,15 @@ def test_config5b_skinny_full():
 
 
 # ---------------------------------------------------------------- exactness
-@pytest.mark.parametrize("variant", ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk", "tile128",
-                                     "skinny"])
+# The skinny kernel takes A stored [M,K] and B stored [N,K] only (tA=0, tB=1).
+_EXACT_CASES = [(v, tA, tB) for v in ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk", "tile128",
+                                      "skinny"]
+                for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)] if v != "skinny" or (tA, tB) == (0, 1)]
+
+
+@pytest.mark.parametrize("variant,tA,tB", _EXACT_CASES)
 @pytest.mark.parametrize("ab", ["f16", "bf16"])
-@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
 def test_small_integers_exact(variant, ab, tA, tB):
-    if variant == "skinny" and (tA, tB) != (0, 1):
-        pytest.skip("the skinny kernel takes A stored [M,K] and B stored [N,K] only")
     # 300 rows: ragged for the 128 tile; the 256 tile needs 128-bit loads, so with A
     # stored [K, M] its M must be a multiple of 8 (304)
     M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304, "tile128dma": 304,
