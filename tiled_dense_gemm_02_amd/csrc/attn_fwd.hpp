@@ -55,16 +55,34 @@ struct AttnLds {
     __device__ static int swz_v(int r) { return 2 * ((r / RPB) % (CH / 2)); }
 };
 
+// Extremes over the lanes l, l^16, l^32 and l^48 (one score row's four key
+// groups).  gfx950's row swaps do it in registers: with the value in both
+// operands, v_permlane16_swap leaves lane l with x[l] and x[l^16] in its two
+// results, v_permlane32_swap with x[l] and x[l^32].  (A lane shuffle would be a
+// round trip through LDS, waited for twice per row tile and key block.)
+__device__ inline u32x2 swap16(float x)
+{
+    return __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+}
+__device__ inline u32x2 swap32(float x)
+{
+    return __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+}
+
 __device__ inline float wave_max4(float x)
 {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    const u32x2 a = swap16(x);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const u32x2 b = swap32(x);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float wave_min4(float x)
 {
-    x = fminf(x, __shfl_xor(x, 16));
-    return fminf(x, __shfl_xor(x, 32));
+    const u32x2 a = swap16(x);
+    x = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const u32x2 b = swap32(x);
+    return fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -217,16 +235,28 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) sacc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            // K fragments of step ks+1 are read while step ks's 8 MFMAs run (two
+            // register buffers; the fences keep the compiler from moving a read
+            // next to its first use, where its LDS latency would be exposed).
+            u32x4 kf[2][4];
+            auto read_k = [&](int ks, u32x4* dst) {
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     const int row = kt * 16 + r16;
-                    const int c = ks * 4 + g;
-                    const u32x4 kf = *(const u32x4*)(kt_base + row * RB + ((c ^ Lay::swz_k(row)) << 4));
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) sacc[rt][kt] = mfma16x16x32<T>(kf, qf[rt][ks], sacc[rt][kt]);
+                    const int cc = ks * 4 + g;
+                    dst[kt] = *(const u32x4*)(kt_base + row * RB + ((cc ^ Lay::swz_k(row)) << 4));
                 }
+            };
+            read_k(0, kf[0]);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) read_k(ks + 1, kf[(ks + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) sacc[rt][kt] = mfma16x16x32<T>(kf[ks & 1][kt], qf[rt][ks], sacc[rt][kt]);
+                __builtin_amdgcn_sched_barrier(0);
             }
 
             const bool need_mask = (kb0 + BN > S) || (CAUSAL && kb0 + BN - 1 > wq0);
@@ -297,20 +327,34 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) lacc[rt] = mfma16x16x32<T>(ones, pf[rt][kk], lacc[rt]);
 
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int s = r16;
-                const int chunk = 2 * dt + ((s & 3) >> 1);
-                const int half = (s & 1) * 8;
+            // V fragments of output tile dt+VPD are read while tile dt's 4 MFMAs
+            // run (a ring of VPD+1 register buffers, fenced as above).
+            constexpr int VPD = D == 128 ? 2 : 1;
+            u32x4 vfr[VPD + 1][2];
+            auto read_v = [&](int dt, u32x4* dst) {
+                const int sx = r16;
+                const int chunk = 2 * dt + ((sx & 3) >> 1);
+                const int half = (sx & 1) * 8;
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
-                    const int klo = kk * 32 + 4 * g + (s >> 2), khi = klo + 16;
+                    const int klo = kk * 32 + 4 * g + (sx >> 2), khi = klo + 16;
                     const u32x2 lo = lds_read_tr16(vt_base + klo * RB + ((chunk ^ Lay::swz_v(klo)) << 4) + half);
                     const u32x2 hi = lds_read_tr16(vt_base + khi * RB + ((chunk ^ Lay::swz_v(khi)) << 4) + half);
-                    const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) oacc[rt][dt] = mfma16x16x32<T>(vf, pf[rt][kk], oacc[rt][dt]);
+                    dst[kk] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
+            };
+#pragma unroll
+            for (int dt = 0; dt < VPD; ++dt) read_v(dt, vfr[dt]);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                if (dt + VPD < DT) read_v(dt + VPD, vfr[(dt + VPD) % (VPD + 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt)
+                        oacc[rt][dt] = mfma16x16x32<T>(vfr[dt % (VPD + 1)][kk], pf[rt][kk], oacc[rt][dt]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // The next block has landed (this lane's loads) and every wave is done
