@@ -562,7 +562,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              f"multi-GPU sharding is described in DESIGN.md but not built", file=sys.stderr)
+              f"the sharding across GPUs is not built", file=sys.stderr)
         sys.exit(2)
     import torch
     import tlg_workloads as W
