@@ -561,7 +561,7 @@ def bench_attn(args, case, log):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               f"the sharding across GPUs is not built", file=sys.stderr)
         sys.exit(2)
     import torch
