@@ -67,7 +67,9 @@ typedef enum {
     TLG_VARIANT_TILE_256_DMA = 6, /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
     TLG_VARIANT_TILE_128_DMA = 7, /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
     TLG_VARIANT_TILE_128_DMA_SPLITK = 8, /* as 7, K split over several workgroups per tile (plan owns a workspace) */
-    TLG_VARIANT_MX_256 = 9     /* block-scaled FP8: 256x256x128, 8 wave64s, scaled MFMA 16x16x128 */
+    TLG_VARIANT_MX_256 = 9,    /* block-scaled FP8: 256x256x128, 8 wave64s, scaled MFMA 16x16x128 */
+    TLG_VARIANT_TILE_64_DMA = 10 /* 64x128x64, 8 wave64s, 4-slot ring of direct loads; A stored [M,K] only
+                                    (transpose_A == 0); grids of at most 128 tiles of 128x128 */
 } tlg_variant;
 
 typedef enum {
@@ -150,7 +152,7 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  *   C    : device pointer to the packed M x N output (read when clear_accum == 0).
  * A and B must be aligned to their element size, and to 16 bytes when the plan
  * uses 128-bit loads for them (tlg_plan_info.vec_a / vec_b == 8), except that
- * the direct-load variants (TILE_256_DMA, TILE_128_DMA, TILE_128_DMA_SPLITK) take K-contiguous
+ * the direct-load variants (TILE_256_DMA, TILE_128_DMA, TILE_128_DMA_SPLITK, TILE_64_DMA) take K-contiguous
  * operands (A with transpose_A == 0, B with transpose_B == 1) at element
  * alignment and any K; C to its element size.  C must not overlap A or B.
  * Returns TLG_ERR_NULL, TLG_ERR_MISALIGNED, TLG_ERR_INVALID_ARG (overlap) or

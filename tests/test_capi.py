@@ -57,7 +57,7 @@ def test_create_rejects_bad_arguments():
     assert _create(4, 4, 4, tA=2)[0] == INVALID
     assert _create(4, 4, 4, clear=3)[0] == INVALID
     assert _create(4, 4, 4, epi=2)[0] == INVALID
-    assert _create(4, 4, 4, variant=10)[0] == INVALID
+    assert _create(4, 4, 4, variant=11)[0] == INVALID
     assert _create(4, 4, 4, variant=9)[0] == UNSUPPORTED                # the block-scaled kernel needs FP8
     assert _create(100, 100, 777, tA=1, tB=1, variant=8)[0] == UNSUPPORTED
     # forced variants that cannot run the request
@@ -87,12 +87,17 @@ def test_variant_choice_and_geometry_for_the_workloads():
                           transpose_B=case.transpose_B, epilogue="relu" if case.relu else "none",
                           variant=variant)
 
+    # at most 128 tiles of 128x128 with A stored [M,K]: 64x128 tiles
     i = info(C["c1"])
-    assert (i.variant, i.block_m, i.grid, i.k_tiles, i.splits) == (7, 128, 4, 4, 1)
-    # 1024^3: 64 tiles of 128x128, 16 K tiles each (too short a K to split)
+    assert (i.variant, i.block_m, i.block_n, i.grid, i.k_tiles, i.splits) == (10, 64, 128, 8, 4, 1)
+    # 1024^3: 64 tiles of 128x128 (too short a K to split) -> 128 tiles of 64x128, 16 K tiles each
     i = info(C["c2"])
-    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (7, 128, 128, 64, 64, 16)
-    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (4, 512, 4 * 2 * 128 * 64 * 2, 1, 0)
+    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (10, 64, 128, 64, 128, 16)
+    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (4, 512, 4 * (64 + 128) * 64 * 2, 1, 0)
+    i = info(C["c2"], "tile128dma")
+    assert (i.variant, i.block_m, i.grid, i.lds_bytes) == (7, 128, 64, 4 * 2 * 128 * 64 * 2)
+    # A stored [K,M]: 64-row tiles of an M-contiguous operand do not exist
+    assert tlg.select(1024, 1024, 1024, transpose_A=True).variant == 7
     # forced split: 4 ranges of 4 K tiles (256 workgroups)
     i = info(C["c2"], "tile128dma_sk")
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles, i.splits) == (8, 128, 128, 64, 256, 4, 4)
@@ -100,7 +105,7 @@ def test_variant_choice_and_geometry_for_the_workloads():
     i = info(C["c3"])
     assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (6, 256, 256, 64, 131072, 512)
     i = info(C["c4"])
-    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (7, 8, 8, 8 * 12, 13, 1)
+    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (10, 8, 8, 16 * 12, 13, 1)
     # forced split of 1000x1500x777: 8 x 12 = 96 tiles, 13 K tiles -> 2 ranges (7 + 6 K tiles)
     i = info(C["c4"], "tile128dma_sk")
     assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (8, 8, 8, 8 * 12 * 2, 7, 2)
@@ -126,7 +131,7 @@ def test_split_k_choice():
             continue
         s = i.splits
         per = -(-kt // s)
-        assert i.variant == (8 if s > 1 else 7)
+        assert i.variant == (8 if s > 1 else 10)
         assert 1 <= s <= 8 and per >= 2 and (s - 1) * per < kt
         assert i.k_tiles == per and i.grid == tiles * s
         assert s == 8 or tiles * s <= 256 or s == 1
@@ -166,7 +171,7 @@ def test_run_validation_happens_before_any_launch():
     assert g.run_ptrs(4096, 8192, 0) == NULL
     # (every pointer set below fails validation: nothing is ever launched on them)
     # direct loads: K-contiguous A at element alignment, B stored [K, N] at 16 bytes
-    assert g.info.variant == 7
+    assert g.info.variant == 10
     assert g.run_ptrs(4096 + 1, 1 << 20, 1 << 21) == MISALIGNED     # A not element-aligned
     assert g.run_ptrs(4096, (1 << 20) + 2, 1 << 21) == MISALIGNED   # B not 16-byte aligned
     assert g.run_ptrs(4096, (1 << 20) + 8, 1 << 21) == MISALIGNED

@@ -98,9 +98,15 @@ def test_config5b_skinny_full():
 
 # ---------------------------------------------------------------- exactness
 # The skinny kernel takes A stored [M,K] and B stored [N,K] only (tA=0, tB=1).
-_EXACT_CASES = [(v, tA, tB) for v in ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk", "tile128",
-                                      "skinny"]
-                for tA, tB in [(0, 0), (0, 1), (1, 0), (1, 1)] if v != "skinny" or (tA, tB) == (0, 1)]
+# The 64x128 direct-load kernel takes A stored [M,K] only (tA=0).
+def _layouts_of(v, layouts=((0, 0), (0, 1), (1, 0), (1, 1))):
+    return [(tA, tB) for tA, tB in layouts
+            if (v != "skinny" or (tA, tB) == (0, 1)) and (v != "tile64dma" or tA == 0)]
+
+
+_EXACT_CASES = [(v, tA, tB) for v in ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk", "tile64dma",
+                                      "tile128", "skinny"]
+                for tA, tB in _layouts_of(v)]
 
 
 @pytest.mark.parametrize("variant,tA,tB", _EXACT_CASES)
@@ -109,7 +115,7 @@ def test_small_integers_exact(variant, ab, tA, tB):
     # 300 rows: ragged for the 128 tile; the 256 tile needs 128-bit loads, so with A
     # stored [K, M] its M must be a multiple of 8 (304)
     M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304, "tile128dma": 304,
-         "tile128dma_sk": 304}[variant]
+         "tile128dma_sk": 304, "tile64dma": 300}[variant]
     case = W.GemmCase("smallint", M, 264, 200, ab=ab, c="f32", transpose_A=tA, transpose_B=tB,
                       dist="smallint", seed=77, relu=1)
     _full_check(case, variant=variant, exact=True)
@@ -119,17 +125,19 @@ def test_small_integers_exact(variant, ab, tA, tB):
 RAGGED = [1, 15, 17, 31, 33, 64, 65, 127, 129, 257]
 
 
-@pytest.mark.parametrize("variant", ["tile128", "tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk"])
-@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("variant,tA,tB", [(v, tA, tB) for v in ["tile128", "tile256", "tile256w8", "tile256dma",
+                                                                   "tile128dma", "tile128dma_sk", "tile64dma"]
+                                           for tA, tB in _layouts_of(v)])
 def test_ragged_sweep(variant, tA, tB):
     rng = np.random.default_rng(1000 + 10 * tA + tB + {"tile128": 0, "tile256": 100, "tile256w8": 200, "tile256dma": 300,
-                                                       "tile128dma": 400, "tile128dma_sk": 500}[variant])
+                                                       "tile128dma": 400, "tile128dma_sk": 500,
+                                                       "tile64dma": 600}[variant])
     for it in range(6):
         M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
         r8 = lambda x: (x + 7) // 8 * 8
         if variant in ("tile256", "tile256w8"):     # 128-bit register-staged loads: every extent % 8 == 0
             M, N, K = r8(M), r8(N), r8(K)
-        elif variant in ("tile256dma", "tile128dma", "tile128dma_sk"):   # only M/N-contiguous rows need % 8 == 0
+        elif variant in ("tile256dma", "tile128dma", "tile128dma_sk", "tile64dma"):   # only M/N-contiguous rows need % 8 == 0
             M = r8(M) if tA else M
             N = N if tB else r8(N)
         ab = "f16" if it % 2 == 0 else "bf16"
@@ -139,8 +147,8 @@ def test_ragged_sweep(variant, tA, tB):
         _full_check(case, variant=variant, guard=1024)
 
 
-@pytest.mark.parametrize("variant", ["tile256dma", "tile128dma", "tile128dma_sk"])
-@pytest.mark.parametrize("tA,tB", [(0, 0), (0, 1), (1, 1)])
+@pytest.mark.parametrize("variant,tA,tB", [(v, tA, tB) for v in ["tile256dma", "tile128dma", "tile128dma_sk", "tile64dma"]
+                                           for tA, tB in _layouts_of(v, ((0, 0), (0, 1), (1, 1)))])
 def test_direct_loads_unaligned_k_and_base(variant, tA, tB):
     """K-contiguous operands at any K and at a base address 2 bytes off 16-byte alignment:
     unaligned 128-bit loads plus the trimmed K tail."""
@@ -167,6 +175,7 @@ def test_skinny_rows(M):
 def test_accumulate_onto_c():
     for variant, tB in (("tile128", 0), ("tile256", 0), ("tile256w8", 0), ("tile256dma", 0), ("tile256dma", 1),
                         ("tile128dma", 0), ("tile128dma", 1), ("tile128dma_sk", 0), ("tile128dma_sk", 1),
+                        ("tile64dma", 0), ("tile64dma", 1),
                         ("skinny", 1)):
         for c in ("f16", "f32"):
             case = W.GemmCase(f"accum-{variant}-{c}", 16 if variant == "skinny" else 264, 200, 136,

@@ -590,6 +590,18 @@ inline hipError_t dispatch_lds128(const GemmParams& p, int tA, int tB, hipStream
     return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T>(p, tA, tB, s);
 }
 
+// 64 x 128 tiles (grids of at most 128 tiles of 128 x 128: twice the workgroups
+// in one wave): 8 waves of 32 x 32, 4-slot ring, barrier after 2 of the last K
+// step's 4 MFMAs, one direct load per MFMA.  The LDS layout takes M/N-contiguous
+// rows of 128..512 elements only, so A must be K-contiguous (transpose_A == 0).
+template <int T>
+inline hipError_t dispatch_lds64(const GemmParams& p, int tA, int tB, hipStream_t s)
+{
+    if (tA) return hipErrorInvalidValue;
+    if (tB) return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, true, false>(p, s);
+    return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, false, false>(p, s);
+}
+
 // The same 128 x 128 kernel with K split over p.splits workgroups per tile.
 template <int T>
 inline hipError_t dispatch_lds128_sk(const GemmParams& p, int tA, int tB, hipStream_t s)

@@ -20,4 +20,9 @@ hipError_t launch_lds128sk_bf16(const GemmParams& p, int transpose_A, int transp
     return dispatch_lds128_sk<DT_BF16>(p, transpose_A, transpose_B, stream);
 }
 
+hipError_t launch_lds64_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream)
+{
+    return dispatch_lds64<DT_BF16>(p, transpose_A, transpose_B, stream);
+}
+
 }  // namespace tlg

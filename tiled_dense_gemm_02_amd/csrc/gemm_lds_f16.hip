@@ -20,4 +20,9 @@ hipError_t launch_lds128sk_f16(const GemmParams& p, int transpose_A, int transpo
     return dispatch_lds128_sk<DT_F16>(p, transpose_A, transpose_B, stream);
 }
 
+hipError_t launch_lds64_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream)
+{
+    return dispatch_lds64<DT_F16>(p, transpose_A, transpose_B, stream);
+}
+
 }  // namespace tlg

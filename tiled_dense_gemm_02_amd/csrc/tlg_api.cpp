@@ -76,6 +76,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_TILE_128_DMA: return "tile128dma";
     case TLG_VARIANT_TILE_128_DMA_SPLITK: return "tile128dma_sk";
     case TLG_VARIANT_MX_256: return "mx256";
+    case TLG_VARIANT_TILE_64_DMA: return "tile64dma";
     default: return "?";
     }
 }
@@ -130,7 +131,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_MX_256 || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_64_DMA || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
     if (is_mx(ab)) {
         // Block-scaled FP8: A stored [M, K], B stored [N, K], whole 128-wide K
@@ -183,20 +184,27 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
             return TLG_ERR_UNSUPPORTED;
         if ((forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA ||
-             forced == TLG_VARIANT_TILE_128_DMA_SPLITK) && !dma_ok)
+             forced == TLG_VARIANT_TILE_128_DMA_SPLITK || forced == TLG_VARIANT_TILE_64_DMA) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
+        if (forced == TLG_VARIANT_TILE_64_DMA && tA) return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
         variant = TLG_VARIANT_SKINNY;
     } else if (dma_ok) {
         // 256x256 tiles once they fill every CU, else 128x128 tiles (4x the workgroups);
         // fewer than 128 of those with a long K: split K as well.  The exchange of
         // partial tiles costs ~5-10 us per launch (measured on MI355X), which a
-        // split repays only from about 48 K tiles (K >= 3072) on.
+        // split repays only from about 48 K tiles (K >= 3072) on.  Otherwise, at
+        // most 128 tiles of 128x128 and A stored [M,K]: 64x128 tiles, twice the
+        // workgroups in one wave (measured on MI355X: 1024^3 12.9 -> 11.8 us,
+        // 1000x1500x777 bf16 12.7 -> 10.9 us; at 2048^3, 256 tiles of 128x128,
+        // they are 1.5x slower).
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), kt = ceil_div(K, 64);
         if (ceil_div(M, 256) * ceil_div(N, 256) >= 256)
             variant = TLG_VARIANT_TILE_256_DMA;
         else if (t128 < 128 && kt >= kSplitMinKTiles && choose_splits(t128, kt) >= 2)
             variant = TLG_VARIANT_TILE_128_DMA_SPLITK;
+        else if (t128 <= 128 && !tA)
+            variant = TLG_VARIANT_TILE_64_DMA;
         else
             variant = TLG_VARIANT_TILE_128_DMA;
     } else {
@@ -218,10 +226,11 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         }
     }
     if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
-        variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
+        variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA) {
         const int64_t b = (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_256_W8 ||
                            variant == TLG_VARIANT_TILE_256_DMA) ? 256 : 128;
-        if (ceil_div(M, b) * ceil_div(N, b) * splits > INT32_MAX) return TLG_ERR_INVALID_ARG;
+        const int64_t bm = variant == TLG_VARIANT_TILE_64_DMA ? kLds64BM : b;
+        if (ceil_div(M, bm) * ceil_div(N, b) * splits > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
         if (ceil_div(M, kSkinnyRows) > 65535 || ceil_div(N, kSkinnyNB) > INT32_MAX) return TLG_ERR_INVALID_ARG;
     }
@@ -230,7 +239,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
     p->variant = variant;
     const bool dma = variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
-                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK;
+                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA;
     p->vec_a = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : va;
     p->vec_b = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : vb;
     if (dma) {
@@ -273,6 +282,13 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
             p->ws_partials_bytes = (size_t)tiles * splits * kLds128BM * kLds128BN * sizeof(float);
             p->ws_bytes = p->ws_partials_bytes + (size_t)((tiles * sizeof(unsigned) + 255) / 256 * 256);
         }
+    } else if (variant == TLG_VARIANT_TILE_64_DMA) {
+        in.block_m = kLds64BM; in.block_n = kLds64BN; in.block_k = kLdsBK;
+        in.stages = kLds64Stages;
+        in.threads = kLdsThreads;
+        in.grid = ceil_div(M, kLds64BM) * ceil_div(N, kLds64BN);
+        in.lds_bytes = (int64_t)kLds64Stages * (kLds64BM + kLds64BN) * kLdsBK * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
     } else if (variant == TLG_VARIANT_SKINNY) {
         in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
         in.stages = kSkinnyStages;
@@ -409,6 +425,11 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
         err = p.ab == TLG_F16 ? launch_lds128_f16(gp, p.tA, p.tB, (hipStream_t)stream)
                               : launch_lds128_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
+    } else if (p.variant == TLG_VARIANT_TILE_64_DMA) {
+        gp.tiles_m = (int)ceil_div(p.M, kLds64BM);
+        gp.tiles_n = (int)ceil_div(p.N, kLds64BN);
+        err = p.ab == TLG_F16 ? launch_lds64_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                              : launch_lds64_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else if (p.variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
         gp.tiles_m = (int)ceil_div(p.M, kLds128BM);
         gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
@@ -618,8 +639,9 @@ struct TuneCandidate {
 std::vector<TuneCandidate> tune_space(int64_t M, int64_t N)
 {
     std::vector<TuneCandidate> c = {{TLG_VARIANT_TILE_256_DMA, 0}, {TLG_VARIANT_TILE_128_DMA, 0},
-                                    {TLG_VARIANT_SKINNY, 0},       {TLG_VARIANT_TILE_256_W8, 0},
-                                    {TLG_VARIANT_TILE_256, 0},     {TLG_VARIANT_TILE_128, 0}};
+                                    {TLG_VARIANT_TILE_64_DMA, 0},  {TLG_VARIANT_SKINNY, 0},
+                                    {TLG_VARIANT_TILE_256_W8, 0},  {TLG_VARIANT_TILE_256, 0},
+                                    {TLG_VARIANT_TILE_128, 0}};
     if (ceil_div(M, 128) * ceil_div(N, 128) < 256)
         for (int s = 2; s <= kMaxSplits; ++s) c.push_back({TLG_VARIANT_TILE_128_DMA_SPLITK, s});
     return c;

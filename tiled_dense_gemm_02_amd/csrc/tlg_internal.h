@@ -89,12 +89,16 @@ hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
 // fill the chip with 256x256 tiles.
 constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64, kLdsStages = 2, kLdsThreads = 512;
 constexpr int kLds128BM = 128, kLds128BN = 128, kLds128Stages = 4;
+constexpr int kLds64BM = 64, kLds64BN = 128, kLds64Stages = 4;
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128sk_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128sk_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+// 64 x 128 tiles; A must be K-contiguous (transpose_A == 0).
+hipError_t launch_lds64_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds64_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 
 // Block-scaled FP8 GEMM (gemm_mx.hip).  A [M,K], B [N,K] FP8 bytes; SA [M,K/32],
 // SB [N,K/32] E8M0 bytes; K % 128 == 0.
