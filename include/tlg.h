@@ -205,8 +205,10 @@ typedef struct {
  * plan for the same request as tlg_gemm_create, choosing the kernel variant,
  * and for the split-K variant the number of K ranges, by timing every
  * candidate that can serve the request on the caller's buffers.  Candidates:
- * every variant of tlg_variant but EMPTY, and the split-K variant with 2..8
- * ranges when the output has fewer than 256 tiles of 128 x 128.  A candidate
+ * the fp16/bf16 variants of tlg_variant (TILE_256_DMA, TILE_128_DMA, TILE_64_DMA,
+ * SKINNY, TILE_256_W8, TILE_256, TILE_128), and the split-K variant with 2..8
+ * ranges when the output has fewer than 256 tiles of 128 x 128 (block-scaled
+ * requests are refused, see tlg_gemm_run_mx).  A candidate
  * that refuses the request (TLG_ERR_UNSUPPORTED) or the buffers' alignment
  * (TLG_ERR_MISALIGNED) is skipped.
  *   A, B, C, stream : as for tlg_gemm_run.  C is overwritten, and with
