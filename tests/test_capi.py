@@ -98,6 +98,10 @@ def test_variant_choice_and_geometry_for_the_workloads():
     assert (i.variant, i.block_m, i.grid, i.lds_bytes) == (7, 128, 64, 4 * 2 * 128 * 64 * 2)
     # A stored [K,M]: 64-row tiles of an M-contiguous operand do not exist
     assert tlg.select(1024, 1024, 1024, transpose_A=True).variant == 7
+    with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
+        tlg.select(1024, 1024, 1024, transpose_A=True, variant="tile64dma")
+    # B stored [N, K] is fine: 1000x1500x777 forced
+    assert tlg.select(1000, 1500, 777, "bf16", "f32", transpose_B=True, variant="tile64dma").grid == 16 * 12
     # forced split: 4 ranges of 4 K tiles (256 workgroups)
     i = info(C["c2"], "tile128dma_sk")
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles, i.splits) == (8, 128, 128, 64, 256, 4, 4)
