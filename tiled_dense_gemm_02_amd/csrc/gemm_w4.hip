@@ -93,6 +93,7 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     static_assert(BRB >= 256 && BRB <= 1024 && ARB >= 1024 && BL % WAVES == 0 && AL % WAVES == 0, "stage layout");
     static_assert(KSTEPS % WAVES == 0 && SPW >= 1, "every wave takes whole K steps of a stage");
     constexpr int TABLE = 160 * 1024 - S * STAGE;
+    static_assert(S >= 2, "at least one stage in flight");
     static_assert(TABLE >= 16 * 1024 && TABLE <= kW4TableBytes, "ring and table must fit in 160 KiB");
     static_assert(WAVES * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
 
@@ -175,8 +176,11 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     uint32_t magic;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
+    // Stages 0 .. S-3 go out before the table gather, stage S-2 after the wait
+    // below (the prologue then waits for one stage fewer; stage S-2 is first
+    // needed S-2 stages later).
 #pragma unroll
-    for (int st = 0; st < S - 1; ++st)
+    for (int st = 0; st < S - 2; ++st)
         if (st < NST) issue(st);
     // Scale / zero table of this workgroup's rows (rows past N: zero weights).
     for (int i = threadIdx.x; i < NB * KG; i += WAVES * 64) {
@@ -193,6 +197,7 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     // for here, together with everything issued before them: the ring's vmcnt
     // accounting below counts direct loads only.
     wait_vmcnt<0>();
+    if (S - 2 < NST) issue(S - 2);
 
     // Per K step u of this wave: LDS offsets of its A and weight fragments inside
     // a slot, and its group index, advanced stage by stage (the quotient and
