@@ -138,7 +138,8 @@ tlg_status tlg_gemm_select(tlg_plan_info *info, int64_t M, int64_t N, int64_t K,
 /*
  * As tlg_gemm_create, but forces a kernel variant (tlg_variant).  Returns
  * TLG_ERR_UNSUPPORTED when the forced variant cannot run the request (the
- * skinny variant needs transpose_A == 0, transpose_B == 1 and K % 8 == 0).
+ * skinny variant needs transpose_A == 0, transpose_B == 1 and K % 8 == 0;
+ * TILE_64_DMA needs transpose_A == 0).
  */
 tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
                                    int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
