@@ -64,6 +64,16 @@ def kernel_hash(variant: int) -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_constant(name: str) -> int:
+    """A launch constant of the kernels, read from their internal header (for labels)."""
+    import re
+    with open(os.path.join(ROOT, "tiled_dense_gemm_02_amd", "csrc", "tlg_internal.h")) as fh:
+        m = re.search(rf"constexpr int {name} = (\d+);", fh.read())
+    if not m:
+        raise RuntimeError(f"{name} not found in tlg_internal.h")
+    return int(m.group(1))
+
+
 def stored_traffic(workload: str, variant: int):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken
     on the current kernel source; else None."""
@@ -315,7 +325,8 @@ def measure_w4(case, steps, warmup, rotate_bytes=1 << 30, log=None, min_warm_ms=
     if status != 0:
         raise RuntimeError(f"tlg_gemm_w4 failed during the timed launches (status {status})")
     return {"ms": start.elapsed_time(end) / steps, "wall_s": time.perf_counter() - t0, "C": C, "nsets": nsets,
-            "describe": f"gemm_w4 block=16x64x512 threads=512 group={case.G} {case.ab}->{case.c}"}
+            "describe": f"gemm_w4 block=16x64x512 threads={kernel_constant('kW4Threads')} group={case.G} "
+                        f"{case.ab}->{case.c}"}
 
 
 def cpu_baseline_w4(case, C_gpu, rows):

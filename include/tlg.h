@@ -98,6 +98,20 @@ typedef struct {
 
 /*
  * Create a plan for C[M,N] = act(A·B).
+ *
+ * create / run / destroy are this library's counterpart of the host wrapper the
+ * pages' compiler generates around a tile program ("NVIDIA backend codegen"
+ * chapter, section 4.2 "host/device split and wrapper generation": an extern "C"
+ * init() that does the one-time set-up and an extern "C" call() that launches
+ * the kernel on the caller's stream, both returning an int status).  Here the
+ * one-time part is create (validation, variant choice, launch geometry, the
+ * workspace of a split-K plan) and the launch part is run.  The argument checks
+ * that the pages' generated host stub performs before a launch (overview page,
+ * "automatically generated host checks": null data pointers, dtypes, shapes,
+ * alignment/contiguity assumptions) are performed by create (sizes, enums,
+ * flags) and run (pointers, alignment, overlap, device) and reported as a
+ * status instead of a launch.
+ *
  *   M, N, K      : 0 <= M, N <= 2^24, 0 <= K <= 2^22.  M or N == 0 is a no-op plan;
  *                  K == 0 gives C = act(clear_accum ? 0 : C) (the empty sum).
  *   ab_dtype     : TLG_F16 or TLG_BF16 (A and B); TLG_E4M3 / TLG_E5M2 for the
@@ -112,7 +126,7 @@ typedef struct {
  * block-scaled request other than the one tlg_gemm_run_mx describes),
  * TLG_ERR_NOMEM if the plan cannot be allocated.  Plans with K split over
  * several workgroups per tile (tlg_plan_info.splits > 1, chosen for output grids
- * of fewer than 128 tiles of 128x128 with at least 8 K tiles of 64) allocate a
+ * of fewer than 128 tiles of 128x128 with at least 48 K tiles of 64) allocate a
  * device workspace here (tlg_plan_info.workspace_bytes: fp32 partial tiles plus
  * one counter per tile), on the device current at the call, zero its counters
  * and wait for that to finish (TLG_ERR_HIP if any of it fails); other plans do
@@ -147,7 +161,9 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
                                    int32_t variant);
 
 /*
- * Enqueue C = act(A·B) on `stream` (a hipStream_t; NULL is the null stream).
+ * Enqueue C = act(A·B) on `stream` (a hipStream_t; NULL is the null stream): the
+ * launch half of the host wrapper (codegen chapter, section 4.2.2: call() runs
+ * the host checks, then launches on the given stream and returns a status).
  *   A, B : device pointers to the packed operands (read only).  May be NULL only
  *          when K == 0 or M*N == 0.
  *   C    : device pointer to the packed M x N output (read when clear_accum == 0).
@@ -219,8 +235,8 @@ typedef struct {
  *   results         : receives up to max_results entries (may be NULL when
  *                     max_results == 0), one per candidate timed, in the order
  *                     timed; *n_results (may be NULL) gets the number written.
- * The choice is cached per (current device, M, N, K, dtypes, flags, epilogue)
- * for the life of the process: a later call with the same key times nothing
+ * The choice is cached per (current device, M, N, K, dtypes, flags, epilogue,
+ * whether each of A, B and C is 16-byte aligned) for the life of the process: a later call with the same key times nothing
  * (*n_results = 0) and returns a new plan of the cached choice.  The choice
  * depends on timings and so may differ between processes.  Synchronises the
  * stream.  Returns the errors of tlg_gemm_create and tlg_gemm_run,
@@ -333,7 +349,10 @@ tlg_status tlg_gemm_sp(const void *A, const void *Wv, const void *Wm, void *C, i
                        int32_t ab_dtype, int32_t c_dtype, int32_t epilogue, void *stream);
 
 /* Release a plan (and its workspace, if any; the caller first makes sure no run of
- * the plan is still in flight).  NULL is accepted (no-op, TLG_OK). */
+ * the plan is still in flight).  NULL is accepted (no-op, TLG_OK).  The pages'
+ * generated wrapper has no counterpart (its module lives as long as the
+ * process); a plan here owns host memory and possibly a device workspace, so it
+ * is released explicitly. */
 tlg_status tlg_gemm_destroy(tlg_gemm_t plan);
 
 /* Fill *info with the plan's launch facts.  TLG_ERR_NULL for a NULL argument. */

@@ -304,6 +304,7 @@ def gemm_mx(A: torch.Tensor, SA: torch.Tensor, B: torch.Tensor, SB: torch.Tensor
 
 
 _plan_cache: dict = {}
+_has_workspace: dict = {}
 
 
 def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, *, transpose_A: bool = False,
@@ -319,6 +320,16 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, *, tra
         C = torch.empty((M, N), dtype=out_dtype, device=A.device)
     key = (A.device, M, N, K, A.dtype, C.dtype, bool(transpose_A), bool(transpose_B), bool(clear_accum),
            epilogue, variant)
+    # A plan with a workspace (split-K) must not run on two streams at once, and this
+    # helper hides its plans from the caller: such plans are kept one per stream, so
+    # calls on different streams never share a workspace.  Plans without one are shared.
+    has_ws = _has_workspace.get(key)
+    if has_ws is None:
+        has_ws = _has_workspace[key] = bool(select(M, N, K, A.dtype, C.dtype, transpose_A=transpose_A,
+                                                   transpose_B=transpose_B, clear_accum=clear_accum,
+                                                   epilogue=epilogue, variant=variant).workspace_bytes)
+    if has_ws:
+        key = key + (torch.cuda.current_stream(A.device).cuda_stream,)
     plan = _plan_cache.get(key)
     if plan is None:
         # a split-K plan's workspace goes to the device current at creation: A's

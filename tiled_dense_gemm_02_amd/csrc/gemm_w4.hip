@@ -279,12 +279,12 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
 template <int S, int KST>
 static hipError_t launch_w4_s(const W4Params& p, int ab_dtype, hipStream_t stream)
 {
+    W4Params args = p;
+    void* kargs[] = {&args};
     const dim3 grid((unsigned)((p.N + kW4NB - 1) / kW4NB), (unsigned)((p.M + 15) / 16)), block(kW4Threads);
-    if (ab_dtype == DT_F16)
-        hipLaunchKernelGGL((gemm_w4_kernel<DT_F16, S, KST>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((gemm_w4_kernel<DT_BF16, S, KST>), grid, block, 0, stream, p);
-    return hipGetLastError();
+    const void* fn = ab_dtype == DT_F16 ? (const void*)&gemm_w4_kernel<DT_F16, S, KST>
+                                        : (const void*)&gemm_w4_kernel<DT_BF16, S, KST>;
+    return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 
 // Three slots of 512-wide stages leave a 64 KiB table (K/G <= 256).  On the

@@ -522,6 +522,7 @@ tlg_status tlg_gemm_w4(const void* A, const void* Wq, const void* S, const void*
     if (epilogue != TLG_EPI_NONE && epilogue != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
     if (K / G > kW4MaxGroups) return TLG_ERR_UNSUPPORTED;
     if (M == 0 || N == 0) return TLG_OK;
+    if (ceil_div(M, 16) > 65535) return TLG_ERR_INVALID_ARG;   // row blocks of 16 go in the grid's y dimension
     if (!C || (K > 0 && (!A || !Wq || !S || !Z))) return TLG_ERR_NULL;
     const uintptr_t a = (uintptr_t)A, w = (uintptr_t)Wq, sc = (uintptr_t)S, z = (uintptr_t)Z, c = (uintptr_t)C;
     const int cb = elem_bytes(c_dtype);
@@ -614,16 +615,25 @@ const char* tlg_version(void) { return "tlg 0.1.0 (gfx950)"; }
 // and the best configuration kept in a cache keyed by device and problem.
 namespace {
 
+// The alignment class of the buffers is part of the key: a choice timed on
+// 16-byte-aligned operands may be a variant that refuses 2-byte-aligned ones.
 struct TuneKey {
     int dev;
     int64_t M, N, K;
     int ab, c, tA, tB, clear, epi;
+    int align;   // bit 0: A 16-byte aligned, bit 1: B, bit 2: C
     bool operator<(const TuneKey& o) const
     {
-        return std::tie(dev, M, N, K, ab, c, tA, tB, clear, epi) <
-               std::tie(o.dev, o.M, o.N, o.K, o.ab, o.c, o.tA, o.tB, o.clear, o.epi);
+        return std::tie(dev, M, N, K, ab, c, tA, tB, clear, epi, align) <
+               std::tie(o.dev, o.M, o.N, o.K, o.ab, o.c, o.tA, o.tB, o.clear, o.epi, o.align);
     }
 };
+
+int align_class(const void* A, const void* B, const void* C)
+{
+    return (((uintptr_t)A % 16 == 0) ? 1 : 0) | (((uintptr_t)B % 16 == 0) ? 2 : 0) |
+           (((uintptr_t)C % 16 == 0) ? 4 : 0);
+}
 
 std::mutex g_tune_mu;
 std::map<TuneKey, std::pair<int, int>> g_tune_cache;   // -> (variant, forced splits)
@@ -672,7 +682,8 @@ tlg_status tlg_gemm_tune(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int32
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return TLG_ERR_HIP;
-    const TuneKey key{dev, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue};
+    const TuneKey key{dev, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                      align_class(A, B, C)};
     {
         std::lock_guard<std::mutex> lock(g_tune_mu);
         auto it = g_tune_cache.find(key);
