@@ -164,15 +164,21 @@ class Oracle:
             raise ValueError("oracle_sp_expand failed")
         return out
 
-    def spgemm(self, M, N, K, A_bits, Wv_bits, Wm, *, dtype="f16", relu=0, rows=None) -> np.ndarray:
-        """2:4 sparse GEMM o(m, n) = act(sum_k a(m,k) w(n,k)) in float64 for rows=(m0, m1)."""
+    def spgemm(self, M, N, K, A_bits, Wv_bits, Wm, *, dtype="f16", relu=0, rows=None,
+               nthreads=1) -> np.ndarray:
+        """2:4 sparse GEMM o(m, n) = act(sum_k a(m,k) w(n,k)) in float64 for rows=(m0, m1).
+        With nthreads > 1 the rows are cut into that many ranges, each computed by one
+        call of the same C routine on its own thread (the calls release the GIL)."""
         A, Wv, Wm = _u16(A_bits), _u16(Wv_bits), _u8(Wm)
         m0, m1 = (0, M) if rows is None else rows
         out = np.empty((m1 - m0, N), dtype=np.float64)
-        rc = self.lib.oracle_spgemm_rows(M, N, K, _code(dtype), int(relu), _ptr(A), _ptr(Wv), _ptr(Wm), m0, m1,
-                                         out.ctypes.data)
-        if rc != 0:
-            raise ValueError(f"oracle_spgemm_rows failed with {rc}")
+
+        def part(r0, r1):
+            return self.lib.oracle_spgemm_rows(M, N, K, _code(dtype), int(relu), _ptr(A), _ptr(Wv), _ptr(Wm),
+                                               r0, r1, out.ctypes.data + (r0 - m0) * N * 8)
+        for rc in _row_ranges(part, m0, m1, nthreads):
+            if rc != 0:
+                raise ValueError(f"oracle_spgemm_rows failed with {rc}")
         return out
 
     def spgemm_points(self, M, N, K, A_bits, Wv_bits, Wm, ms, ns, *, dtype="f16", relu=0) -> np.ndarray:
@@ -247,6 +253,17 @@ class Oracle:
 
 
 MX_CODES = {"e4m3": 10, "e5m2": 11, "e8m0": 12}
+
+
+def _row_ranges(part, m0, m1, nthreads):
+    """Run part(r0, r1) over nthreads contiguous ranges of [m0, m1); returns the results."""
+    n = max(1, min(int(nthreads), m1 - m0))
+    if n == 1:
+        return [part(m0, m1)]
+    import concurrent.futures as cf
+    bounds = [m0 + (m1 - m0) * i // n for i in range(n + 1)]
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        return list(ex.map(lambda i: part(bounds[i], bounds[i + 1]), range(n)))
 
 
 def _u8(x):

@@ -142,7 +142,8 @@ def test_sparse_8192_small_integers_exact():
     torch.cuda.synchronize()
     gpu = out_values(C)
     del C
-    o = O.spgemm(case.M, case.N, case.K, W.bits16(A), W.bits16(Wv), Wm.numpy(), dtype=case.ab, relu=0)
+    o = O.spgemm(case.M, case.N, case.K, W.bits16(A), W.bits16(Wv), Wm.numpy(), dtype=case.ab, relu=0,
+                 nthreads=16)
     want = O.rne_out(o.reshape(-1), "f32").reshape(o.shape)
     bad = gpu != want
     assert not bad.any(), f"{int(bad.sum())} inexact outputs; first {np.argwhere(bad)[:5].tolist()}"
