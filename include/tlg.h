@@ -79,7 +79,9 @@ typedef enum {
     TLG_ERR_NULL = -3,         /* null plan, output handle or data pointer        */
     TLG_ERR_MISALIGNED = -4,   /* pointer not aligned as the plan requires        */
     TLG_ERR_HIP = -5,          /* the HIP runtime reported an error at launch     */
-    TLG_ERR_NOMEM = -6         /* host allocation of the plan failed              */
+    TLG_ERR_NOMEM = -6,        /* host allocation of the plan failed              */
+    TLG_ERR_TOO_LARGE = -7     /* tlg_gemm_run_noalloc: the request needs more scratch
+                                  than the library's static buffer holds           */
 } tlg_status;
 
 /* Plan facts, for tests and the benchmark. */
@@ -181,6 +183,38 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  * share the workspace, so issue them on one stream or order them by events.
  */
 tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): plan and run in one call,
+ * allocating nothing.  Same arguments and result as tlg_gemm_create (automatic
+ * variant) followed by tlg_gemm_run of that plan; the same kernel runs, so C is
+ * bit-identical to that pair's.
+ *
+ * The plan is built on the stack and discarded.  When the automatic choice splits
+ * K (tlg_plan_info.splits > 1), its fp32 partial tiles and per-tile counters live
+ * in a static device buffer of the library instead of a plan workspace: 16 MiB of
+ * partial tiles plus 4 KiB of counters, one copy per GPU, held until the process
+ * ends.  The automatic choice always fits (it splits only grids of fewer than 128
+ * tiles of 128 x 128, into at most 256 partial tiles); a request that would need
+ * more is refused with TLG_ERR_TOO_LARGE.  The first call on a device looks up
+ * the buffer's device address and enqueues a small kernel on `stream` that zeroes
+ * the counters; every split-K launch returns the counters it uses to zero.
+ *
+ * All calls on one GPU share that GPU's buffer, which keeps the last call's
+ * contents: two calls whose split-K launches overlap in time on one GPU (on
+ * different streams, or one captured in a graph replayed concurrently with
+ * another) race on it and give wrong results; order them on one stream or by
+ * events.  Calls whose automatic plan does not split K use no scratch and may
+ * overlap freely.
+ *
+ * Errors: those of tlg_gemm_create (except TLG_ERR_NOMEM) and tlg_gemm_run, plus
+ * TLG_ERR_UNSUPPORTED for block-scaled dtypes (use tlg_gemm_run_mx) or a device
+ * index of 64 or more, TLG_ERR_TOO_LARGE as above.  Nothing is enqueued on error.
+ */
+tlg_status tlg_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                                int32_t transpose_A, int32_t transpose_B, int32_t clear_accum,
+                                int32_t epilogue, const void *A, const void *B, void *C, void *stream);
 
 /*
  * Block-scaled ("MX") GEMM: the block-scaled MMA of the codegen chapter

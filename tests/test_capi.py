@@ -321,3 +321,23 @@ def test_dequant_and_sparse_validation_happens_before_any_launch():
     assert sp(a, None, z, c, 64, 64, 128, 1, 1, 0, None) == -3
     assert sp(a, w, z + 2, c, 64, 64, 128, 1, 1, 0, None) == -4           # metadata 4-byte aligned
     assert sp(a, w, z, w + 16, 64, 64, 128, 1, 1, 0, None) == -1          # C overlaps Wv
+
+
+def test_noalloc_entry_point_host_checks():
+    """tlg_gemm_run_noalloc refuses bad requests before touching a device: the plan
+    checks of create, the pointer checks of run, block-scaled dtypes; M or N == 0 is a
+    no-op that needs no pointers."""
+    lib = tlg.load_library()
+    f = lib.tlg_gemm_run_noalloc
+    a = ctypes.c_void_p(0x10000)
+    assert f(-1, 4, 4, 1, 1, 0, 0, 1, 0, a, a, a, None) == INVALID
+    assert f(4, 4, 1 << 23, 1, 1, 0, 0, 1, 0, a, a, a, None) == INVALID
+    assert f(4, 4, 4, 3, 1, 0, 0, 1, 0, a, a, a, None) == UNSUPPORTED       # fp32 operands
+    assert f(4, 4, 128, 4, 1, 0, 1, 1, 0, a, a, a, None) == UNSUPPORTED     # E4M3: tlg_gemm_run_mx
+    assert f(4, 4, 4, 1, 1, 2, 0, 1, 0, a, a, a, None) == INVALID           # flag not 0/1
+    assert f(4, 4, 4, 1, 1, 0, 0, 1, 0, None, a, a, None) == NULL
+    assert f(4, 4, 4, 1, 1, 0, 0, 1, 0, a, a, None, None) == NULL
+    assert f(0, 4, 4, 1, 1, 0, 0, 1, 0, None, None, None, None) == OK        # empty output: nothing to do
+    # C overlapping A
+    assert f(64, 64, 64, 1, 1, 0, 0, 1, 0, a, ctypes.c_void_p(0x900000), a, None) == INVALID
+    assert lib.tlg_status_string(-7) == b"TLG_ERR_TOO_LARGE"

@@ -15,7 +15,7 @@ import threading
 
 import torch
 
-__all__ = ["Gemm", "gemm", "gemm_mx", "select", "tune", "PlanInfo", "TuneResult", "TlgError", "lib_path", "load_library",
+__all__ = ["Gemm", "gemm", "gemm_mx", "gemm_noalloc", "select", "tune", "PlanInfo", "TuneResult", "TlgError", "lib_path", "load_library",
            "status_name", "VARIANTS", "F16", "BF16", "F32", "E4M3", "E5M2"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,7 @@ VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "til
 EPILOGUES = {"none": 0, "relu": 1}
 
 STATUS = {0: "TLG_OK", -1: "TLG_ERR_INVALID_ARG", -2: "TLG_ERR_UNSUPPORTED", -3: "TLG_ERR_NULL",
-          -4: "TLG_ERR_MISALIGNED", -5: "TLG_ERR_HIP", -6: "TLG_ERR_NOMEM"}
+          -4: "TLG_ERR_MISALIGNED", -5: "TLG_ERR_HIP", -6: "TLG_ERR_NOMEM", -7: "TLG_ERR_TOO_LARGE"}
 
 
 class TlgError(RuntimeError):
@@ -79,6 +79,8 @@ def load_library():
         lib.tlg_gemm_create_variant.restype = i32
         lib.tlg_gemm_run.argtypes = [vp, vp, vp, vp, vp]
         lib.tlg_gemm_run.restype = i32
+        lib.tlg_gemm_run_noalloc.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        lib.tlg_gemm_run_noalloc.restype = i32
         lib.tlg_gemm_run_mx.argtypes = [vp, vp, vp, vp, vp, vp, vp]
         lib.tlg_gemm_run_mx.restype = i32
         lib.tlg_gemm_destroy.argtypes = [vp]
@@ -338,6 +340,35 @@ def gemm(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None, *, tra
                         clear_accum=clear_accum, epilogue=epilogue, variant=variant)
         _plan_cache[key] = plan
     return plan.run(A, B, C)
+
+
+def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, transpose_A: bool = False,
+                 transpose_B: bool = False, clear_accum: bool = True, epilogue: str = "none",
+                 stream=None) -> torch.Tensor:
+    """C = act(A·B) through tlg_gemm_run_noalloc: planned and launched in one call that
+    allocates nothing (a split-K choice uses the library's static scratch, shared by
+    all such calls on the GPU: calls that overlap in time race).  C must be given."""
+    M = A.shape[1] if transpose_A else A.shape[0]
+    K = A.shape[0] if transpose_A else A.shape[1]
+    N = B.shape[0] if transpose_B else B.shape[1]
+    probe = Gemm.__new__(Gemm)
+    probe.M, probe.N, probe.K = M, N, K
+    probe.ab_code, probe.c_code = _code(A.dtype), _code(C.dtype)
+    probe.transpose_A, probe.transpose_B = bool(transpose_A), bool(transpose_B)
+    probe._h = None
+    probe._check(A, B, C)
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    lib = load_library()
+    with torch.cuda.device(C.device):
+        st = lib.tlg_gemm_run_noalloc(M, N, K, _code(A.dtype), _code(C.dtype), int(bool(transpose_A)),
+                                      int(bool(transpose_B)), int(bool(clear_accum)), EPILOGUES[epilogue],
+                                      A.data_ptr() or None, B.data_ptr() or None, C.data_ptr() or None,
+                                      ctypes.c_void_p(s))
+    if st != 0:
+        raise TlgError("tlg_gemm_run_noalloc", st)
+    return C
 
 
 def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor | None = None, *,

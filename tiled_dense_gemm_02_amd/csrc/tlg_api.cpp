@@ -375,15 +375,18 @@ tlg_status tlg_gemm_select(tlg_plan_info* info, int64_t M, int64_t N, int64_t K,
     return st;
 }
 
-tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, void* stream)
+}  // extern "C"
+
+namespace {
+
+// The host checks of a run (pointers, alignment, overlap); TLG_OK when the plan may
+// be launched on these buffers.
+tlg_status check_run(const tlg_gemm_s& p, const void* A, const void* B, const void* C)
 {
-    if (!plan) return TLG_ERR_NULL;
-    const tlg_gemm_s& p = *plan;
     if (is_mx(p.ab)) return TLG_ERR_INVALID_ARG;   // needs its scales: tlg_gemm_run_mx
     if (p.variant == TLG_VARIANT_EMPTY) return TLG_OK;
     if (!C) return TLG_ERR_NULL;
     if (p.K > 0 && (!A || !B)) return TLG_ERR_NULL;
-
     const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
     const int cb = elem_bytes(p.c);
     if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
@@ -395,13 +398,18 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
     const uint64_t c_bytes = (uint64_t)p.M * (uint64_t)p.N * (uint64_t)cb;
     if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, b, b_bytes))
         return TLG_ERR_INVALID_ARG;
+    return TLG_OK;
+}
 
-    if (p.ws) {
-        int dev = -1;
-        if (hipGetDevice(&dev) != hipSuccess) return TLG_ERR_HIP;
-        if (dev != p.device) return TLG_ERR_INVALID_ARG;   // the workspace lives on the plan's device
-    }
-
+// One launch of a checked 16-bit plan.  ws / counters: the split-K partial tiles
+// and per-tile counters (the plan's own workspace, or the static scratch of
+// tlg_gemm_run_noalloc); unused by the other variants.
+tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* C, void* stream, float* ws,
+                       unsigned* counters)
+{
+    if (p.variant == TLG_VARIANT_EMPTY) return TLG_OK;
+    const uintptr_t c = (uintptr_t)C;
+    const int cb = elem_bytes(p.c);
     GemmParams gp{};
     gp.A = A; gp.B = B; gp.C = C;
     gp.M = (int)p.M; gp.N = (int)p.N; gp.K = (int)p.K;
@@ -434,8 +442,8 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         gp.tiles_m = (int)ceil_div(p.M, kLds128BM);
         gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
         gp.splits = p.splits;
-        gp.ws = (float*)p.ws;
-        gp.counters = (unsigned*)((char*)p.ws + p.ws_partials_bytes);
+        gp.ws = ws;
+        gp.counters = counters;
         err = p.ab == TLG_F16 ? launch_lds128sk_f16(gp, p.tA, p.tB, (hipStream_t)stream)
                               : launch_lds128sk_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else {
@@ -446,6 +454,111 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, 
         err = launch_tile(cfg, gp, p.ab, p.tA, p.tB, p.vec_a, p.vec_b, (hipStream_t)stream);
     }
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of tlg_gemm_run_noalloc: the split-K partial tiles and per-tile
+// counters of a request, in a file-scope device array instead of a plan-owned
+// allocation.  Every GPU the library runs on holds one copy of it (at its own
+// address) until the process ends.  Host code never passes the array's name to a
+// kernel (in host code that name is a host-side stand-in, not a device address):
+// the device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and kept in g_scratch_ptr.
+//   [0, kScratchPartialBytes)                  fp32 partial tiles
+//   [kScratchPartialBytes, + kScratchCounterBytes)  one counter per output tile
+// The automatic plan never needs more: it splits K only for fewer than 128 tiles
+// of 128 x 128, into at most 256 / tiles ranges (tiles x ranges <= 256 partial
+// tiles of 64 KiB).
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchPartialBytes = size_t(256) * kLds128BM * kLds128BN * sizeof(float);   // 16 MiB
+constexpr size_t kScratchCounterBytes = 4096;                                                 // 1024 counters
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchPartialBytes + kScratchCounterBytes];
+
+// Zero n 32-bit words (a kernel rather than hipMemsetAsync, so that the clear
+// may be recorded into a captured graph).
+__global__ void tlg_fill_zero_u32(unsigned* p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device (nullptr: not set up)
+
+// Device address of the current device's scratch.  First call on a device: look
+// the address up and zero the counters with a kernel on `stream` (ordered before
+// the caller's launch).  The split-K kernel returns every counter it uses to zero,
+// so the counters stay zero between calls.
+tlg_status scratch_for_current_device(void* stream, char** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TLG_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return TLG_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TLG_ERR_HIP;
+        constexpr int n = (int)(kScratchCounterBytes / sizeof(unsigned));
+        void* args_p = (char*)ptr + kScratchPartialBytes;
+        int args_n = n;
+        void* kargs[] = {&args_p, &args_n};
+        if (hipLaunchKernel((const void*)&tlg_fill_zero_u32, dim3((n + 255) / 256), dim3(256), kargs, 0,
+                            (hipStream_t)stream) != hipSuccess)
+            return TLG_ERR_HIP;
+        g_scratch_ptr[dev] = (char*)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return TLG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tlg_status tlg_gemm_run(tlg_gemm_t plan, const void* A, const void* B, void* C, void* stream)
+{
+    if (!plan) return TLG_ERR_NULL;
+    const tlg_gemm_s& p = *plan;
+    const tlg_status st = check_run(p, A, B, C);
+    if (st != TLG_OK || p.variant == TLG_VARIANT_EMPTY) return st;
+    if (p.ws) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess) return TLG_ERR_HIP;
+        if (dev != p.device) return TLG_ERR_INVALID_ARG;   // the workspace lives on the plan's device
+    }
+    return launch_plan(p, A, B, C, stream, (float*)p.ws, (unsigned*)((char*)p.ws + p.ws_partials_bytes));
+}
+
+tlg_status tlg_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
+                                int32_t transpose_A, int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
+                                const void* A, const void* B, void* C, void* stream)
+{
+    if (ab_dtype == TLG_E4M3 || ab_dtype == TLG_E5M2) return TLG_ERR_UNSUPPORTED;   // block-scaled: tlg_gemm_run_mx
+    tlg_gemm_s p;   // on the stack: plan_build is host work only and allocates nothing
+    tlg_status st = plan_build(&p, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
+                               TLG_VARIANT_AUTO);
+    if (st != TLG_OK) return st;
+    st = check_run(p, A, B, C);
+    if (st != TLG_OK || p.variant == TLG_VARIANT_EMPTY) return st;
+    float* ws = nullptr;
+    unsigned* counters = nullptr;
+    if (p.ws_bytes) {
+        const size_t tiles = (size_t)(ceil_div(M, kLds128BM) * ceil_div(N, kLds128BN));
+        if (p.ws_partials_bytes > kScratchPartialBytes || tiles * sizeof(unsigned) > kScratchCounterBytes)
+            return TLG_ERR_TOO_LARGE;
+        char* base = nullptr;
+        st = scratch_for_current_device(stream, &base);
+        if (st != TLG_OK) return st;
+        ws = (float*)base;
+        counters = (unsigned*)(base + kScratchPartialBytes);
+    }
+    return launch_plan(p, A, B, C, stream, ws, counters);
 }
 
 tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const void* B, const void* SB, void* C,
@@ -603,11 +716,14 @@ const char* tlg_status_string(int32_t status)
     case TLG_ERR_MISALIGNED: return "TLG_ERR_MISALIGNED";
     case TLG_ERR_HIP: return "TLG_ERR_HIP";
     case TLG_ERR_NOMEM: return "TLG_ERR_NOMEM";
+    case TLG_ERR_TOO_LARGE: return "TLG_ERR_TOO_LARGE";
     default: return "TLG_ERR_UNKNOWN";
     }
 }
 
-const char* tlg_version(void) { return "tlg 0.1.0 (gfx950)"; }
+const char* tlg_version(void) { return "tlg 0.2.0 (gfx950)"; }
+
+}  // extern "C"
 
 // Autotuning, after the pages' autotuner (overview page, "autotuning" section):
 // a search space of kernel configurations pruned by what each can serve, every
@@ -658,6 +774,8 @@ std::vector<TuneCandidate> tune_space(int64_t M, int64_t N)
 }
 
 }  // namespace
+
+extern "C" {
 
 tlg_status tlg_gemm_tune(tlg_gemm_t* out, int64_t M, int64_t N, int64_t K, int32_t ab_dtype, int32_t c_dtype,
                          int32_t transpose_A, int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
