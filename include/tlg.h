@@ -68,8 +68,12 @@ typedef enum {
     TLG_VARIANT_TILE_128_DMA = 7, /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
     TLG_VARIANT_TILE_128_DMA_SPLITK = 8, /* as 7, K split over several workgroups per tile (plan owns a workspace) */
     TLG_VARIANT_MX_256 = 9,    /* block-scaled FP8: 256x256x128, 8 wave64s, scaled MFMA 16x16x128 */
-    TLG_VARIANT_TILE_64_DMA = 10 /* 64x128x64, 8 wave64s, 4-slot ring of direct loads; A stored [M,K] only
+    TLG_VARIANT_TILE_64_DMA = 10, /* 64x128x64, 8 wave64s, 4-slot ring of direct loads; A stored [M,K] only
                                     (transpose_A == 0); grids of at most 128 tiles of 128x128 */
+    TLG_VARIANT_TILE_256_DMA_STREAMK = 11, /* as 6, persistent: 256 workgroups (one per CU) take the tiles
+                                    of all but the last wave whole, then equal shares of the remaining
+                                    tiles' K iterations (stream-K); the plan owns a workspace */
+    TLG_VARIANT_TILE_128_DMA_STREAMK = 12  /* as 7, with the persistent stream-K schedule of 11 */
 } tlg_variant;
 
 typedef enum {
@@ -95,7 +99,9 @@ typedef struct {
     int64_t lds_bytes;     /* LDS bytes per workgroup                                 */
     int32_t k_tiles;       /* trips of the K loop per workgroup (at most)             */
     int32_t splits;        /* workgroups per output tile along K (1: no split)        */
-    int64_t workspace_bytes; /* device workspace the plan owns (0 unless splits > 1)   */
+    int64_t workspace_bytes; /* device workspace the plan owns (0 unless splits > 1 or stream-K) */
+    int32_t dp_tiles;      /* stream-K plans: output tiles computed whole (the first waves)  */
+    int32_t sk_tiles;      /* stream-K plans: output tiles shared out by K iterations         */
 } tlg_plan_info;
 
 /*

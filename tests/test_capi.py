@@ -57,7 +57,7 @@ def test_create_rejects_bad_arguments():
     assert _create(4, 4, 4, tA=2)[0] == INVALID
     assert _create(4, 4, 4, clear=3)[0] == INVALID
     assert _create(4, 4, 4, epi=2)[0] == INVALID
-    assert _create(4, 4, 4, variant=11)[0] == INVALID
+    assert _create(4, 4, 4, variant=13)[0] == INVALID
     assert _create(4, 4, 4, variant=9)[0] == UNSUPPORTED                # the block-scaled kernel needs FP8
     assert _create(100, 100, 777, tA=1, tB=1, variant=8)[0] == UNSUPPORTED
     # forced variants that cannot run the request

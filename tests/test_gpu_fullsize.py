@@ -38,31 +38,37 @@ def _device():
     yield
 
 
-def _check_full(case, exact=False, guard=0, want_variant=None):
+def _check_full(case, exact=False, guard=0, want_variant=None, variants=("auto",)):
+    """Run `case` with each plan variant in `variants` and compare every output with the
+    oracle (computed once).  Returns the plans."""
     log(f"[case] full-size {case.name} M={case.M} N={case.N} K={case.K} ab={case.ab} c={case.c} "
         f"tA={case.transpose_A} tB={case.transpose_B} relu={case.relu} dist={case.dist}")
     A, B, C_in = W.make_inputs(case)
-    C, plan, buf, g = run_gpu(case, A, B, C_in, guard=guard)
-    log(f"    plan: {plan.describe()}")
+    results = []
+    for v in variants:
+        C, plan, buf, g = run_gpu(case, A, B, C_in, variant=v, guard=guard)
+        log(f"    plan: {plan.describe()}")
+        if guard:
+            raw = buf.view(torch.uint8).cpu()
+            esz = 4 if case.c == "f32" else 2
+            assert bool((raw[:g * esz] == 0x5A).all()) and bool((raw[(g + case.M * case.N) * esz:] == 0x5A).all()), \
+                "store outside C"
+        results.append((plan, out_values(C)))
+        del C, buf
     if want_variant is not None:
-        assert plan.info.variant == want_variant
-    if guard:
-        raw = buf.view(torch.uint8).cpu()
-        esz = 4 if case.c == "f32" else 2
-        assert bool((raw[:g * esz] == 0x5A).all()) and bool((raw[(g + case.M * case.N) * esz:] == 0x5A).all()), \
-            "store outside C"
-    gpu = out_values(C)
-    del C, buf
+        assert results[0][0].info.variant == want_variant
     o = oracle_full(case, A, B, C_in)
-    if exact:
-        assert_exact(gpu, o, case, plan.describe())
-        log("    exact")
-    else:
-        err = assert_within_tolerance(gpu, o, case, plan.describe())
-        log(f"    max|err| = {err:.3e}")
-    if case.relu:
-        assert (gpu >= 0).all()
-    return plan
+    for plan, gpu in results:
+        if exact:
+            assert_exact(gpu, o, case, plan.describe())
+            log(f"    exact ({plan.describe().split()[0]})")
+        else:
+            err = assert_within_tolerance(gpu, o, case, plan.describe())
+            log(f"    max|err| = {err:.3e} ({plan.describe().split()[0]})")
+        if case.relu:
+            assert (gpu >= 0).all()
+    plans = [r[0] for r in results]
+    return plans[0] if len(plans) == 1 else plans
 
 
 # ------------------------------------------------------------ the target workloads, every output
@@ -91,21 +97,27 @@ def test_small_integers_exact_full_size(n, ab, c, relu):
 
 # ------------------------------------------------------------ large ragged shapes, full output
 def test_large_ragged_xcd_remap_partial_band():
-    """288 tiles of 256 x 256 (a multiple of 8: XCD remap on), 18 tile rows (four bands
-    of four, then one of two), K = 4100 (the last K tile holds 4 elements)."""
+    """With 256 x 256 tiles: 288 tiles (a multiple of 8: XCD remap on), 18 tile rows (four
+    bands of four, then one of two), K = 4100 (the last K tile holds 4 elements).  The
+    automatic plan takes 128 x 128 tiles here (5 waves of them beat 2 of 256 x 256),
+    1152 tiles with a last band of four rows and a remap; both are checked."""
     case = W.GemmCase("ragged-4600x4096x4100", 4600, 4096, 4100, relu=1, dist="normal", seed=4101)
-    plan = _check_full(case, guard=4096, want_variant=6)
-    assert plan.info.grid == 288
+    p256, pauto = _check_full(case, guard=4096, variants=("tile256dma", "auto"))
+    assert p256.info.grid == 288
+    assert pauto.info.variant == 7 and pauto.info.grid == 1152
 
 
 def test_large_ragged_no_remap_exact():
-    """306 tiles (not a multiple of 8: no XCD remap), a last tile column 254 wide, B
-    stored [N, K] with K = 4100 (both operands' last K chunk trimmed in LDS); small
-    integers, exact."""
+    """With 256 x 256 tiles: 306 tiles (not a multiple of 8: no XCD remap), a last tile
+    column 254 wide, B stored [N, K] with K = 4100 (both operands' last K chunk trimmed in
+    LDS); small integers, exact.  The automatic plan (128 x 128 tiles, 1224 of them) and
+    the persistent stream-K schedule are checked on the same inputs."""
     case = W.GemmCase("ragged-4600x4350x4100", 4600, 4350, 4100, c="f32", transpose_B=1, dist="smallint",
                       seed=4102)
-    plan = _check_full(case, exact=True, guard=4096, want_variant=6)
-    assert plan.info.grid == 306
+    p256, pauto, psk = _check_full(case, exact=True, guard=4096,
+                                   variants=("tile256dma", "auto", "tile256dma_streamk"))
+    assert p256.info.grid == 306
+    assert pauto.info.variant == 7 and pauto.info.grid == 1224
 
 
 # ------------------------------------------------------------ block-scaled and sparse at 8192^3

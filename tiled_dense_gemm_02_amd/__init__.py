@@ -25,7 +25,8 @@ F16, BF16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
 _TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
                   torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
 VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "tile256w8": 5,
-            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8, "mx256": 9, "tile64dma": 10}
+            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8, "mx256": 9, "tile64dma": 10,
+            "tile256dma_streamk": 11, "tile128dma_streamk": 12}
 EPILOGUES = {"none": 0, "relu": 1}
 
 STATUS = {0: "TLG_OK", -1: "TLG_ERR_INVALID_ARG", -2: "TLG_ERR_UNSUPPORTED", -3: "TLG_ERR_NULL",
@@ -47,7 +48,7 @@ class PlanInfo(ctypes.Structure):
                 ("block_k", ctypes.c_int32), ("stages", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("vec_a", ctypes.c_int32), ("vec_b", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int64), ("k_tiles", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64)]
+                ("workspace_bytes", ctypes.c_int64), ("dp_tiles", ctypes.c_int32), ("sk_tiles", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

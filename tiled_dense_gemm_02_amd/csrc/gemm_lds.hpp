@@ -271,12 +271,22 @@ struct LdsOperand {
     }
 };
 
-// SK: split-K.  Workgroup b handles tile b / splits and K range b % splits; the
-// fp32 partial tiles are summed, in range order, by whichever workgroup of the
-// tile finishes last (a counter per tile elects it), so the result does not
-// depend on the order in which the workgroups finish.
+// Work decomposition (MODE):
+//   kModeDP      one output tile per workgroup, whole K (the tile program's grid).
+//   kModeSplitK  workgroup b handles tile b / splits and K range b % splits.
+//   kModeStreamK persistent: a fixed grid of G workgroups (one per CU); workgroup g
+//                first computes the whole-K tiles g, g + G, ... below p.dp_tiles,
+//                then an equal share of the remaining p.sk_tiles x (K tiles)
+//                iterations, cut at tile boundaries into segments (the "persistent"
+//                schedule of the overview page: a tile scheduler that balances the
+//                tail of the grid over every CU).
+// A tile whose K range is split over several workgroups has its fp32 partial
+// tiles summed, in K order, by whichever of them finishes last (a counter per tile
+// elects it), so the result does not depend on the order in which they finish.
+enum : int { kModeDP = 0, kModeSplitK = 1, kModeStreamK = 2 };
+
 template <int BM, int BN, int S, int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC,
-          bool SK = false>
+          int MODE = kModeDP>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_lds_kernel(GemmParams p)
 {
@@ -301,29 +311,49 @@ gemm_lds_kernel(GemmParams p)
     static_assert((S - 2) * L + D < 64, "vmcnt range");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
+    __shared__ unsigned ticket;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-    int tile_id = blockIdx.x, split = 0;
-    if constexpr (SK) {
-        split = blockIdx.x % p.splits;
-        tile_id = blockIdx.x / p.splits;
-    }
-    int tm, tn;
-    tile_coords(tile_id, p.tiles_m, p.tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int lane_id = threadIdx.x & 63;
+    const int wave_id = threadIdx.x >> 6;
     const int K = p.K;
     const int TPALL = (K + BK - 1) / BK;              // K tiles (the last one zero-padded)
-    int kt0 = 0, TP = TPALL;                          // this workgroup's K tiles: kt0 .. kt0+TP-1
-    if constexpr (SK) {
-        const int per = (TPALL + p.splits - 1) / p.splits;
-        kt0 = split * per;
-        TP = min(per, TPALL - kt0);
+
+    // One segment: output tile tile_id over K tiles kt0 .. kt0+TP-1.  When the tile's
+    // K range is shared by nslots > 1 segments, their partial tiles go to workspace
+    // slots counted from slot_base: segment s (in K order) uses slot
+    // slot_base + (s == 0 ? first_off : s * stride), this one slot_base + self_off;
+    // counters[counter] elects the segment that sums them.
+    auto segment = [&](int tile_id, int kt0, int TP, int slot_base, int nslots, int self_off, int first_off,
+                       int stride, int counter) {
+    // In the persistent loop the lane and wave indices pass through empty asm
+    // statements: this keeps the compiler from hoisting the lane-dependent address
+    // arithmetic out of the loop, where it would stay live across the K loop and spill.
+    int lane = lane_id, wave = __builtin_amdgcn_readfirstlane(wave_id);
+    if constexpr (MODE == kModeStreamK) {
+        asm volatile("" : "+v"(lane));
+        asm volatile("" : "+s"(wave));
+        lane &= 63;   // the compiler's knowledge of the ranges, lost through the asm
+        wave &= 7;
+        // The segment's parameters are the same in every lane: say so, so that the
+        // K loop's counters and buffer resources stay in scalar registers.
+        tile_id = __builtin_amdgcn_readfirstlane(tile_id);
+        kt0 = __builtin_amdgcn_readfirstlane(kt0);
+        TP = __builtin_amdgcn_readfirstlane(TP);
+        slot_base = __builtin_amdgcn_readfirstlane(slot_base);
+        nslots = __builtin_amdgcn_readfirstlane(nslots);
+        self_off = __builtin_amdgcn_readfirstlane(self_off);
+        first_off = __builtin_amdgcn_readfirstlane(first_off);
+        counter = __builtin_amdgcn_readfirstlane(counter);
     }
-    // Loads stop at the end of the workgroup's K range (elements past it read as zeros).
-    const int KLIM = SK ? min(K, (kt0 + TP) * BK) : K;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    int tm, tn;
+    if constexpr (MODE == kModeStreamK)
+        band_coords(tile_id, p.tiles_m, p.tiles_n, tm, tn);   // the worker numbering groups XCDs
+    else
+        tile_coords(tile_id, p.tiles_m, p.tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    // Loads stop at the end of the segment's K range (elements past it read as zeros).
+    const int KLIM = min(K, (kt0 + TP) * BK);
 
     OpA opa;
     OpB opb;
@@ -461,10 +491,10 @@ gemm_lds_kernel(GemmParams p)
         });
         __builtin_amdgcn_s_setprio(0);
     }
-    // No direct load may still be writing LDS when the workgroup ends.
+    // No direct load may still be writing LDS when the segment ends.
     wait_vmcnt<0>();
 
-    if constexpr (SK) {
+    if constexpr (MODE != kModeDP) if (nslots > 1) {
         // Publish this range's fp32 partial tile, then take a ticket; the last
         // workgroup of the tile sums the partials in range order and goes on to the
         // epilogue, the others are done.  The XCDs have separate L2 caches, so the
@@ -474,9 +504,8 @@ gemm_lds_kernel(GemmParams p)
         // for its partial stores to complete before the barrier that precedes the
         // ticket, and the partials are read only after the ticket, so no cache
         // write-back or invalidation is needed.
-        __shared__ unsigned ticket;
         const __amdgpu_buffer_rsrc_t wsr =
-            make_rsrc(p.ws + (size_t)tile_id * p.splits * (BM * BN), (uint64_t)p.splits * BM * BN * 4u);
+            make_rsrc(p.ws + (size_t)slot_base * (BM * BN), (uint64_t)((nslots - 1) * stride + 1) * BM * BN * 4u);
         auto ws_off = [&](int s2, int i, int jj) {
             const int ml = arow + i * 16 + (lane & 15), nl = bcol + jj * 16 + 4 * (lane >> 4);
             return (uint32_t)((s2 * (BM * BN) + ml * BN + nl) * 4);
@@ -486,41 +515,50 @@ gemm_lds_kernel(GemmParams p)
 #pragma unroll
             for (int jj = 0; jj < FN; ++jj)
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][jj]), wsr,
-                                                       ws_off(split, i, jj), 0, kCoherentDevice);
+                                                       ws_off(self_off, i, jj), 0, kCoherentDevice);
         wait_vmcnt<0>();
         __syncthreads();
         if (threadIdx.x == 0)
-            ticket = __hip_atomic_fetch_add(p.counters + tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ticket = __hip_atomic_fetch_add(p.counters + counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        if (ticket != (unsigned)(p.splits - 1)) return;
-        // acc = partial 0 + partial 1 + ... in range order (this workgroup's own
-        // partial is read back from the workspace too, which keeps the code free of
-        // branches).  The loads of up to four ranges are in flight together (ranges
-        // past the last one read zeros: their offsets lie beyond the resource).
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (__builtin_amdgcn_readfirstlane(ticket) != (unsigned)(nslots - 1)) return;
+        // acc = partial 0 + partial 1 + ... in K order (this workgroup's own partial is
+        // read back from the workspace too, which keeps the code free of branches).
+        // The loads of up to four partials are in flight together (slots past the
+        // last one read zeros: their offsets lie beyond the resource), RBI row blocks
+        // of fragments at a time so that at most 128 registers hold loaded values.
         constexpr int G = 4;
-        for (int s0 = 0; s0 < p.splits; s0 += G) {
-            u32x4 part[G][FM][FN];
+        constexpr int RBI = (32 / (G * FN)) < FM ? (32 / (G * FN) > 0 ? 32 / (G * FN) : 1) : FM;
+        static_assert(FM % RBI == 0, "row blocks of the reduction");
 #pragma unroll
-            for (int g = 0; g < G; ++g)
+        for (int i0 = 0; i0 < FM; i0 += RBI) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+            for (int i = i0; i < i0 + RBI; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < FN; ++jj)
-                        part[g][i][jj] = __builtin_amdgcn_raw_buffer_load_b128(
-                            wsr, s0 + g < p.splits ? ws_off(s0 + g, i, jj) : kOOB, 0, kCoherentDevice);
+                for (int jj = 0; jj < FN; ++jj) acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < nslots; s0 += G) {
+                u32x4 part[G][RBI][FN];
 #pragma unroll
-            for (int g = 0; g < G; ++g)
+                for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
+                    for (int i = 0; i < RBI; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < FN; ++jj) acc[i][jj] += __builtin_bit_cast(f32x4, part[g][i][jj]);
+                        for (int jj = 0; jj < FN; ++jj)
+                            part[g][i][jj] = __builtin_amdgcn_raw_buffer_load_b128(
+                                wsr,
+                                s0 + g < nslots ? ws_off(s0 + g == 0 ? first_off : (s0 + g) * stride, i0 + i, jj)
+                                                : kOOB,
+                                0, kCoherentDevice);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+#pragma unroll
+                    for (int i = 0; i < RBI; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < FN; ++jj) acc[i0 + i][jj] += __builtin_bit_cast(f32x4, part[g][i][jj]);
+            }
         }
         if (threadIdx.x == 0)   // ready for the next launch
-            __hip_atomic_store(p.counters + tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.counters + counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // Epilogue.  acc[i][j][e] is C[m][n + e] with
@@ -551,27 +589,104 @@ gemm_lds_kernel(GemmParams p)
             store_c4(p.C, p.c_dtype, idx, vec_ok, v, count);
         }
     }
+    };   // segment
+
+    if constexpr (MODE == kModeDP) {
+        segment(blockIdx.x, 0, TPALL, 0, 1, 0, 0, 1, 0);
+    } else if constexpr (MODE == kModeSplitK) {
+        const int tile_id = blockIdx.x / p.splits, split = blockIdx.x % p.splits;
+        const int per = (TPALL + p.splits - 1) / p.splits;
+        const int kt0 = split * per;
+        segment(tile_id, kt0, min(per, TPALL - kt0), tile_id * p.splits, p.splits, split, 0, 1, tile_id);
+    } else {
+        // Persistent.  Workgroup g first takes the whole-K tiles g, g + G, ... below
+        // dp_tiles, then its share of the stream-K iterations [0, W) of the sk_tiles
+        // remaining tiles: [beg(g), beg(g + 1)) with beg(g) = g W / G.  Iteration i
+        // belongs to workgroup owner(i) = ((i + 1) G - 1) / W, the largest g with
+        // beg(g) <= i.  A workgroup has at most two partial segments: the one that
+        // starts at beg(g) (slot 2g) and, if its range crosses a tile boundary, the
+        // one that ends at beg(g + 1) (slot 2g + 1); the segments in between cover
+        // whole tiles.  So the partials of stream-K tile r, made by workgroups
+        // gf .. gl, sit in slots 2gf + (r starts at beg(gf) ? 0 : 1), then 2g for
+        // g = gf+1 .. gl.  The loop ends: every trip either takes one of the finitely
+        // many whole tiles or advances `it` by at least one K tile towards its end.
+        // (One call site of `segment`, so its code is instantiated once.)
+        // W = sk_tiles x (K tiles) < 2^9 x 2^16 fits 32 bits (the plan bounds both).
+        // The loop state (trip j, iteration `it`) lives in LDS and is read back with
+        // volatile loads at the top of every trip, so nothing derived from it can be
+        // hoisted out of the loop and held in registers across the K loop.
+        __shared__ int sched[2];
+        if (threadIdx.x == 0) {
+            const int G = (int)gridDim.x;
+            const int g = G % kXcds == 0 ? ((int)blockIdx.x % kXcds) * (G / kXcds) + (int)blockIdx.x / kXcds
+                                         : (int)blockIdx.x;
+            sched[0] = 0;
+            sched[1] = (int)((int64_t)g * (p.sk_tiles * TPALL) / G);
+        }
+        __syncthreads();
+        for (;;) {
+            // Worker index: workgroups are dispatched round-robin over the 8 XCDs, so
+            // numbering the workers XCD by XCD gives each XCD's workgroups consecutive
+            // whole tiles and consecutive shares of the iterations, i.e. neighbouring
+            // tiles (tile ids walk bands of tile rows, no further remap) that reuse the
+            // same A and B panels from that XCD's L2.  (A bijection on [0, G) when
+            // G % 8 == 0; the schedule below is correct for any numbering.)
+            const int G = (int)gridDim.x;
+            const int g = G % kXcds == 0 ? ((int)blockIdx.x % kXcds) * (G / kXcds) + (int)blockIdx.x / kXcds
+                                         : (int)blockIdx.x;
+            const int j = __builtin_amdgcn_readfirstlane(*(volatile int*)&sched[0]);
+            const int itv = __builtin_amdgcn_readfirstlane(*(volatile int*)&sched[1]);
+            const int ndp = g < p.dp_tiles ? (p.dp_tiles - g + G - 1) / G : 0;
+            const int W = p.sk_tiles * TPALL;
+            const int beg = (int)((int64_t)g * W / G), end = (int)((int64_t)(g + 1) * W / G);
+            int tile, k0, tp, base, ns, self, first, ctr, next = itv;
+            if (j < ndp) {
+                tile = g + j * G; k0 = 0; tp = TPALL; base = 0; ns = 1; self = 0; first = 0; ctr = 0;
+            } else {
+                if (itv >= end) break;
+                const int r = itv / TPALL;
+                k0 = itv - r * TPALL;
+                const int k1 = min(TPALL, k0 + (end - itv));
+                const int64_t tb = (int64_t)r * TPALL;
+                const int gf = (int)(((tb + 1) * G - 1) / W), gl = (int)(((tb + TPALL) * G - 1) / W);
+                tile = p.dp_tiles + r; tp = k1 - k0; ns = gl - gf + 1; ctr = r;
+                base = 2 * gf;
+                first = tb == (int64_t)gf * W / G ? 0 : 1;
+                self = 2 * (g - gf) + (itv == beg ? 0 : 1);
+                next = itv + tp;
+            }
+            segment(tile, k0, tp, base, ns, self, first, 2, ctr);
+            // Every thread read the state before the segment's barriers; the next trip
+            // reads it after the barrier below.
+            if (threadIdx.x == 0) {
+                sched[0] = j + 1;
+                sched[1] = next;
+            }
+            __syncthreads();   // every wave is done with the LDS ring before the next prologue
+        }
+    }
 }
 
-template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC, bool SK>
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC, int MODE>
 inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
-    const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * (SK ? p.splits : 1)));
+    const dim3 grid((unsigned)(MODE == kModeStreamK ? p.persistent_grid
+                                                    : p.tiles_m * p.tiles_n * (MODE == kModeSplitK ? p.splits : 1)));
     const dim3 block(64 * WM * WN);
-    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC, SK>, grid,
+    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC, MODE>, grid,
                            block, kargs, 0, stream);
 }
 
 // K-contiguous A <=> transpose_A == 0; K-contiguous B <=> transpose_B == 1.
-template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool SK = false>
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, int MODE = kModeDP>
 inline hipError_t dispatch_lds_layout(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    if (!tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, true, SK>(p, s);
-    if (!tA && !tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, false, SK>(p, s);
-    if (tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, true, SK>(p, s);
-    return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, false, SK>(p, s);
+    if (!tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, true, MODE>(p, s);
+    if (!tA && !tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, true, false, MODE>(p, s);
+    if (tA && tB) return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, true, MODE>(p, s);
+    return launch_lds_inst<BM, BN, S, SPLIT, R, WM, WN, T, false, false, MODE>(p, s);
 }
 
 // 256 x 256 tiles: 8 waves of 128 x 64, 2-slot ring, barrier after 8 of the last
@@ -598,15 +713,28 @@ template <int T>
 inline hipError_t dispatch_lds64(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
     if (tA) return hipErrorInvalidValue;
-    if (tB) return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, true, false>(p, s);
-    return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, false, false>(p, s);
+    if (tB) return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, true, kModeDP>(p, s);
+    return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, false, kModeDP>(p, s);
 }
 
 // The same 128 x 128 kernel with K split over p.splits workgroups per tile.
 template <int T>
 inline hipError_t dispatch_lds128_sk(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T, true>(p, tA, tB, s);
+    return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T, kModeSplitK>(p, tA, tB, s);
+}
+
+// Persistent stream-K schedules of the 256 x 256 and 128 x 128 kernels.
+template <int T>
+inline hipError_t dispatch_lds_streamk(const GemmParams& p, int tA, int tB, hipStream_t s)
+{
+    return dispatch_lds_layout<256, 256, 2, 8, 2, 2, 4, T, kModeStreamK>(p, tA, tB, s);
+}
+
+template <int T>
+inline hipError_t dispatch_lds128_streamk(const GemmParams& p, int tA, int tB, hipStream_t s)
+{
+    return dispatch_lds_layout<128, 128, 4, 4, 2, 2, 4, T, kModeStreamK>(p, tA, tB, s);
 }
 
 }  // namespace tlg

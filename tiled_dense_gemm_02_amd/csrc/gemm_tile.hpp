@@ -196,11 +196,10 @@ struct TileLoader<false, VEC, R, THREADS> {
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
 
-__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn)
+// Tile id -> (tile row, tile column), walking bands of kGroupM tile rows column by
+// column.
+__device__ inline void band_coords(int id, int tiles_m, int tiles_n, int& tm, int& tn)
 {
-    const int total = tiles_m * tiles_n;
-    int id = bid;
-    if (total % kXcds == 0) id = (bid % kXcds) * (total / kXcds) + bid / kXcds;
     const int band = kGroupM * tiles_n;
     const int g = id / band;
     const int first = g * kGroupM;
@@ -208,6 +207,15 @@ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, i
     const int r = id - g * band;
     tm = first + r % rows;
     tn = r / rows;
+}
+
+// Workgroup id -> tile: the XCD remap (consecutive tile ids onto one XCD), then the bands.
+__device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn)
+{
+    const int total = tiles_m * tiles_n;
+    int id = bid;
+    if (total % kXcds == 0) id = (bid % kXcds) * (total / kXcds) + bid / kXcds;
+    band_coords(id, tiles_m, tiles_n, tm, tn);
 }
 
 // ---------------------------------------------------------------------------

@@ -34,6 +34,7 @@ struct tlg_gemm_s {
     int splits = 1;
     void* ws = nullptr;
     size_t ws_partials_bytes = 0, ws_bytes = 0;
+    int64_t dp_tiles = 0, sk_tiles = 0, grid = 0;   // stream-K plans (grid: persistent workgroups)
     int device = -1;
     tlg_plan_info info;
     char desc[256];
@@ -77,6 +78,8 @@ const char* variant_name(int v)
     case TLG_VARIANT_TILE_128_DMA_SPLITK: return "tile128dma_sk";
     case TLG_VARIANT_MX_256: return "mx256";
     case TLG_VARIANT_TILE_64_DMA: return "tile64dma";
+    case TLG_VARIANT_TILE_256_DMA_STREAMK: return "tile256dma_streamk";
+    case TLG_VARIANT_TILE_128_DMA_STREAMK: return "tile128dma_streamk";
     default: return "?";
     }
 }
@@ -107,6 +110,34 @@ int choose_splits(int64_t tiles, int64_t ktiles)
     return (int)s;
 }
 
+bool is_streamk(int v) { return v == TLG_VARIANT_TILE_256_DMA_STREAMK || v == TLG_VARIANT_TILE_128_DMA_STREAMK; }
+
+// Persistent grid of the stream-K variants: one workgroup per CU of an MI355X
+// (each takes 128 KiB of LDS, so one fits a CU).
+constexpr int kPersistentGrid = 256;
+
+// Tiles computed whole vs shared out by K iterations, and the persistent grid.
+// Every wave but the last full one is data-parallel; the last full wave and the
+// remainder (G .. 2G-1 tiles) are stream-K, so every workgroup gets at least one
+// tile's worth of K iterations and a tile has at most three partial segments.
+// Fewer tiles than workgroups: all stream-K, on min(G, iterations) workgroups so
+// that no workgroup's share is empty (the workgroups sharing a tile must be
+// consecutive).  K == 0: every tile is "whole" (the epilogue alone).
+void streamk_split(int64_t tiles, int64_t ktiles, int64_t* dp, int64_t* sk, int64_t* grid)
+{
+    const int64_t G = kPersistentGrid;
+    if (ktiles == 0) {
+        *dp = tiles;
+        *sk = 0;
+        *grid = std::min(G, tiles);
+        return;
+    }
+    const int64_t waves = tiles / G;
+    *dp = waves >= 2 ? (waves - 1) * G : 0;
+    *sk = tiles - *dp;
+    *grid = *dp > 0 ? G : std::min(G, *sk * ktiles);
+}
+
 bool is_tile(int v)
 {
     return v == TLG_VARIANT_TILE_256 || v == TLG_VARIANT_TILE_128 || v == TLG_VARIANT_TILE_256_W8;
@@ -131,7 +162,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_64_DMA || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA_STREAMK || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
     if (is_mx(ab)) {
         // Block-scaled FP8: A stored [M, K], B stored [N, K], whole 128-wide K
@@ -184,7 +215,8 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
             return TLG_ERR_UNSUPPORTED;
         if ((forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA ||
-             forced == TLG_VARIANT_TILE_128_DMA_SPLITK || forced == TLG_VARIANT_TILE_64_DMA) && !dma_ok)
+             forced == TLG_VARIANT_TILE_128_DMA_SPLITK || forced == TLG_VARIANT_TILE_64_DMA ||
+             is_streamk(forced)) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
         if (forced == TLG_VARIANT_TILE_64_DMA && tA) return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyRows && skinny_ok) {
@@ -198,8 +230,18 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         // workgroups in one wave (measured on MI355X: 1024^3 12.9 -> 11.8 us,
         // 1000x1500x777 bf16 12.7 -> 10.9 us; at 2048^3, 256 tiles of 128x128,
         // they are 1.5x slower).
+        //
+        // Once 256x256 tiles fill the chip, the wave count decides between the two
+        // tile sizes: a wave of 128x128 tiles costs about 0.37 of a wave of 256x256
+        // tiles (measured on MI355X: 8192^3 82 vs 222 us per wave, 4096^3 43 vs 122,
+        // 6144^3 43 vs 107), so a grid whose last wave of 256x256 tiles is nearly
+        // empty runs faster in 128x128 tiles (4600x4350x4100: 306 tiles of 256x256,
+        // 2 waves, 293 us; 1224 of 128x128, 5 waves, 260 us).
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), kt = ceil_div(K, 64);
-        if (ceil_div(M, 256) * ceil_div(N, 256) >= 256)
+        const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
+        if (t256 >= 256 && 37 * ceil_div(t128, 256) < 97 * ceil_div(t256, 256))
+            variant = TLG_VARIANT_TILE_128_DMA;
+        else if (t256 >= 256)
             variant = TLG_VARIANT_TILE_256_DMA;
         else if (t128 < 128 && kt >= kSplitMinKTiles && choose_splits(t128, kt) >= 2)
             variant = TLG_VARIANT_TILE_128_DMA_SPLITK;
@@ -226,9 +268,9 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         }
     }
     if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
-        variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA) {
+        variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA || is_streamk(variant)) {
         const int64_t b = (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_256_W8 ||
-                           variant == TLG_VARIANT_TILE_256_DMA) ? 256 : 128;
+                           variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_256_DMA_STREAMK) ? 256 : 128;
         const int64_t bm = variant == TLG_VARIANT_TILE_64_DMA ? kLds64BM : b;
         if (ceil_div(M, bm) * ceil_div(N, b) * splits > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
@@ -239,7 +281,8 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
     p->variant = variant;
     const bool dma = variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
-                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA;
+                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA ||
+                     is_streamk(variant);
     p->vec_a = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : va;
     p->vec_b = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : vb;
     if (dma) {
@@ -251,6 +294,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     }
 
     tlg_plan_info& in = p->info;
+    in = tlg_plan_info{};
     in.variant = variant;
     in.vec_a = p->vec_a;
     in.vec_b = p->vec_b;
@@ -282,6 +326,23 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
             p->ws_partials_bytes = (size_t)tiles * splits * kLds128BM * kLds128BN * sizeof(float);
             p->ws_bytes = p->ws_partials_bytes + (size_t)((tiles * sizeof(unsigned) + 255) / 256 * 256);
         }
+    } else if (is_streamk(variant)) {
+        const bool big = variant == TLG_VARIANT_TILE_256_DMA_STREAMK;
+        const int64_t bm = big ? kLdsBM : kLds128BM, bn = big ? kLdsBN : kLds128BN;
+        const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn);
+        streamk_split(tiles, ceil_div(K, kLdsBK), &p->dp_tiles, &p->sk_tiles, &p->grid);
+        in.block_m = (int32_t)bm; in.block_n = (int32_t)bn; in.block_k = kLdsBK;
+        in.stages = big ? kLdsStages : kLds128Stages;
+        in.threads = kLdsThreads;
+        in.grid = p->grid;
+        in.lds_bytes = (int64_t)in.stages * (bm + bn) * kLdsBK * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
+        in.dp_tiles = (int32_t)p->dp_tiles;
+        in.sk_tiles = (int32_t)p->sk_tiles;
+        if (p->sk_tiles > 0) {
+            p->ws_partials_bytes = (size_t)2 * (size_t)p->grid * (size_t)(bm * bn) * sizeof(float);
+            p->ws_bytes = p->ws_partials_bytes + (size_t)((p->sk_tiles * sizeof(unsigned) + 255) / 256 * 256);
+        }
     } else if (variant == TLG_VARIANT_TILE_64_DMA) {
         in.block_m = kLds64BM; in.block_n = kLds64BN; in.block_k = kLdsBK;
         in.stages = kLds64Stages;
@@ -299,12 +360,16 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     }
     in.splits = p->splits;
     in.workspace_bytes = (int64_t)p->ws_bytes;
+    char sk_desc[64] = "";
+    if (is_streamk(variant))
+        std::snprintf(sk_desc, sizeof(sk_desc), " dp_tiles=%lld sk_tiles=%lld", (long long)p->dp_tiles,
+                      (long long)p->sk_tiles);
     std::snprintf(p->desc, sizeof(p->desc),
                   "%s M=%lld N=%lld K=%lld ab=%s c=%s tA=%d tB=%d clear=%d relu=%d block=%dx%dx%d "
-                  "stages=%d threads=%d grid=%lld lds=%lld vec=%d/%d splits=%d",
+                  "stages=%d threads=%d grid=%lld lds=%lld vec=%d/%d splits=%d%s",
                   variant_name(variant), (long long)M, (long long)N, (long long)K, dt_name(ab), dt_name(c), tA,
                   tB, clear, p->relu, in.block_m, in.block_n, in.block_k, in.stages, in.threads,
-                  (long long)in.grid, (long long)in.lds_bytes, in.vec_a, in.vec_b, in.splits);
+                  (long long)in.grid, (long long)in.lds_bytes, in.vec_a, in.vec_b, in.splits, sk_desc);
     return TLG_OK;
 }
 
@@ -433,6 +498,21 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
         gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
         err = p.ab == TLG_F16 ? launch_lds128_f16(gp, p.tA, p.tB, (hipStream_t)stream)
                               : launch_lds128_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
+    } else if (is_streamk(p.variant)) {
+        const bool big = p.variant == TLG_VARIANT_TILE_256_DMA_STREAMK;
+        gp.tiles_m = (int)ceil_div(p.M, big ? kLdsBM : kLds128BM);
+        gp.tiles_n = (int)ceil_div(p.N, big ? kLdsBN : kLds128BN);
+        gp.persistent_grid = (int)p.grid;
+        gp.dp_tiles = (int)p.dp_tiles;
+        gp.sk_tiles = (int)p.sk_tiles;
+        gp.ws = ws;
+        gp.counters = counters;
+        if (big)
+            err = p.ab == TLG_F16 ? launch_lds_sk2_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                                  : launch_lds_sk2_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
+        else
+            err = p.ab == TLG_F16 ? launch_lds128_sk2_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                                  : launch_lds128_sk2_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else if (p.variant == TLG_VARIANT_TILE_64_DMA) {
         gp.tiles_m = (int)ceil_div(p.M, kLds64BM);
         gp.tiles_n = (int)ceil_div(p.N, kLds64BN);
@@ -549,8 +629,7 @@ tlg_status tlg_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int32_t ab_dtyp
     float* ws = nullptr;
     unsigned* counters = nullptr;
     if (p.ws_bytes) {
-        const size_t tiles = (size_t)(ceil_div(M, kLds128BM) * ceil_div(N, kLds128BN));
-        if (p.ws_partials_bytes > kScratchPartialBytes || tiles * sizeof(unsigned) > kScratchCounterBytes)
+        if (p.ws_partials_bytes > kScratchPartialBytes || p.ws_bytes - p.ws_partials_bytes > kScratchCounterBytes)
             return TLG_ERR_TOO_LARGE;
         char* base = nullptr;
         st = scratch_for_current_device(stream, &base);
@@ -768,6 +847,8 @@ std::vector<TuneCandidate> tune_space(int64_t M, int64_t N)
                                     {TLG_VARIANT_TILE_64_DMA, 0},  {TLG_VARIANT_SKINNY, 0},
                                     {TLG_VARIANT_TILE_256_W8, 0},  {TLG_VARIANT_TILE_256, 0},
                                     {TLG_VARIANT_TILE_128, 0}};
+    c.push_back({TLG_VARIANT_TILE_256_DMA_STREAMK, 0});
+    c.push_back({TLG_VARIANT_TILE_128_DMA_STREAMK, 0});
     if (ceil_div(M, 128) * ceil_div(N, 128) < 256)
         for (int s = 2; s <= kMaxSplits; ++s) c.push_back({TLG_VARIANT_TILE_128_DMA_SPLITK, s});
     return c;

@@ -27,6 +27,13 @@ struct GemmParams {
     int splits;
     float* ws;
     unsigned* counters;
+    // persistent (stream-K) plans only: persistent_grid workgroups; tiles
+    // 0 .. dp_tiles-1 (in tile order) are computed whole, the sk_tiles after them
+    // in equal shares of K iterations; partial tiles go to ws slots
+    // ([persistent_grid + sk_tiles - 1][BM*BN]), counters[0 .. sk_tiles-1].
+    int persistent_grid;
+    int dp_tiles;
+    int sk_tiles;
 };
 
 // Block-tile configurations of the tiled kernel.
@@ -97,6 +104,11 @@ hipError_t launch_lds128_bf16(const GemmParams& p, int transpose_A, int transpos
 hipError_t launch_lds128sk_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128sk_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 // 64 x 128 tiles; A must be K-contiguous (transpose_A == 0).
+// Persistent stream-K schedules of the 256 x 256 and 128 x 128 kernels.
+hipError_t launch_lds_sk2_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds_sk2_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds128_sk2_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds128_sk2_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds64_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds64_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 
