@@ -252,7 +252,7 @@ class Oracle:
         return self.decode(self.encode(x, dtype), dtype)
 
 
-MX_CODES = {"e4m3": 10, "e5m2": 11, "e8m0": 12}
+MX_CODES = {"e4m3": 10, "e5m2": 11, "e8m0": 12, "e2m1": 13}
 
 
 def _row_ranges(part, m0, m1, nthreads):

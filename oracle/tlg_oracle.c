@@ -288,16 +288,20 @@ int oracle_encode(int dtype, const double *x, int64_t n, uint32_t *bits)
  *         (largest finite 1.75 * 2^8 = 448).
  *   E5M2: 1 sign, 5 exponent (bias 15), 2 fraction bits, IEEE-style:
  *         subnormal at field 0, Inf / NaN at field 31.
+ *   E2M1 (the 4-bit element of MXFP4): 1 sign, 2 exponent (bias 1), 1 fraction
+ *         bit; exponent field 0 is subnormal (frac * 2^-1); no infinity or NaN
+ *         (largest 1.5 * 2^2 = 6).  Two elements per byte: element k of a row is
+ *         the low nibble of byte k/2 when k is even, the high nibble when odd.
  *   E8M0 (scale): an 8-bit biased exponent, value 2^(e - 127); 255 is NaN.
  * Value computed (A stored [M, K], B stored [N, K], both K-contiguous, as the
- * pages' "1d1d" block-scaled example has it):
- *   a(m,k) = elem(A[m*K + k]) * 2^(SA[m*(K/32) + k/32] - 127)
- *   b(k,n) = elem(B[n*K + k]) * 2^(SB[n*(K/32) + k/32] - 127)
+ * pages' "1d1d" block-scaled example has it; E2M1 rows hold K/2 bytes):
+ *   a(m,k) = elem(A, m, k) * 2^(SA[m*(K/32) + k/32] - 127)
+ *   b(k,n) = elem(B, n, k) * 2^(SB[n*(K/32) + k/32] - 127)
  *   s(m,n) = (clear_accum ? 0 : C_in(m,n)) + sum_k a(m,k) * b(k,n)   (double)
  *   o(m,n) = relu ? max(s, +0) : s
  * K must be a multiple of 32 (whole scale blocks).  NaN inputs: parity unpinned.
  * ======================================================================== */
-enum { ORACLE_E4M3 = 10, ORACLE_E5M2 = 11, ORACLE_E8M0 = 12 };
+enum { ORACLE_E4M3 = 10, ORACLE_E5M2 = 11, ORACLE_E8M0 = 12, ORACLE_E2M1 = 13 };
 
 static double dec_e4m3(uint32_t b)
 {
@@ -312,6 +316,14 @@ static double dec_e4m3(uint32_t b)
 
 static double dec_e5m2(uint32_t b) { return dec_ieee(b & 0xffu, 2, 5); }
 
+static double dec_e2m1(uint32_t b)
+{
+    const uint32_t frac = b & 1u, e = (b >> 1) & 3u;
+    const int neg = (b >> 3) & 1u;
+    const double v = e == 0 ? ldexp((double)frac, 1 - 1 - 1) : ldexp((double)(2u + frac), (int)e - 1 - 1);
+    return neg ? -v : v;
+}
+
 static double dec_e8m0(uint32_t b)
 {
     b &= 0xffu;
@@ -323,11 +335,23 @@ static double dec_mx(int fmt, uint32_t b)
     switch (fmt) {
     case ORACLE_E4M3: return dec_e4m3(b);
     case ORACLE_E5M2: return dec_e5m2(b);
+    case ORACLE_E2M1: return dec_e2m1(b);
     default: return dec_e8m0(b);
     }
 }
 
-static int valid_elem_fmt(int f) { return f == ORACLE_E4M3 || f == ORACLE_E5M2; }
+static int valid_elem_fmt(int f) { return f == ORACLE_E4M3 || f == ORACLE_E5M2 || f == ORACLE_E2M1; }
+
+/* Element k of row r of an MX operand with K elements per row: one byte per
+ * element for the 8-bit formats, two per byte (low nibble first) for E2M1. */
+static double mx_elem(int fmt, const uint8_t *X, int64_t K, int64_t r, int64_t k)
+{
+    if (fmt == ORACLE_E2M1) {
+        const uint32_t byte = X[r * (K / 2) + k / 2];
+        return dec_e2m1((k & 1) ? byte >> 4 : byte & 15u);
+    }
+    return dec_mx(fmt, X[r * K + k]);
+}
 
 struct mxjob {
     int64_t M, N, K, m0;
@@ -347,7 +371,7 @@ static void *run_mx_rows(void *arg)
     if (!arow) return (void *)1;
     for (int64_t m = j->r_begin; m < j->r_end; ++m) {
         for (int64_t k = 0; k < j->K; ++k)
-            arow[k] = dec_mx(j->fa, j->A[m * j->K + k]) * dec_e8m0(j->SA[m * KB + k / 32]);
+            arow[k] = mx_elem(j->fa, j->A, j->K, m, k) * dec_e8m0(j->SA[m * KB + k / 32]);
         for (int64_t n = 0; n < j->N; ++n) {
             const double prior = j->clear ? 0.0 : dec(j->cd, c_bits(j->C_in, j->cd, m * j->N + n));
             const double *bc = j->bcol + n * j->K;
@@ -379,7 +403,7 @@ int oracle_mxgemm_rows(int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, in
     if (!bcol) return -2;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k)
-            bcol[n * K + k] = dec_mx(fmt_b, B[n * K + k]) * dec_e8m0(SB[n * KB + k / 32]);
+            bcol[n * K + k] = mx_elem(fmt_b, B, K, n, k) * dec_e8m0(SB[n * KB + k / 32]);
     int64_t rows = m1 - m0;
     if (nthreads > rows) nthreads = (int)rows;
     struct mxjob *jobs = (struct mxjob *)calloc((size_t)nthreads, sizeof(struct mxjob));
@@ -419,15 +443,16 @@ int oracle_mxgemm_points(int64_t M, int64_t N, int64_t K, int fmt_a, int fmt_b, 
         if (m < 0 || m >= M || n < 0 || n >= N) return -1;
         double s = clear_accum ? 0.0 : dec(c_dtype, c_bits(C_in, c_dtype, m * N + n));
         for (int64_t k = 0; k < K; ++k)
-            s += (dec_mx(fmt_a, A[m * K + k]) * dec_e8m0(SA[m * KB + k / 32])) *
-                 (dec_mx(fmt_b, B[n * K + k]) * dec_e8m0(SB[n * KB + k / 32]));
+            s += (mx_elem(fmt_a, A, K, m, k) * dec_e8m0(SA[m * KB + k / 32])) *
+                 (mx_elem(fmt_b, B, K, n, k) * dec_e8m0(SB[n * KB + k / 32]));
         if (relu) s = (s > 0.0) ? s : 0.0;
         out[i] = s;
     }
     return 0;
 }
 
-/* Decode of E4M3 / E5M2 / E8M0 bytes (for the comparisons and the pins). */
+/* Decode of E4M3 / E5M2 / E8M0 bytes, or of E2M1 codes (one code 0..15 per byte),
+ * for the comparisons and the pins. */
 int oracle_mx_decode(int fmt, const uint8_t *bytes, int64_t n, double *out)
 {
     if ((!valid_elem_fmt(fmt) && fmt != ORACLE_E8M0) || n < 0) return -1;

@@ -35,7 +35,7 @@ def test_mx_rejects_bad_arguments(O):
     with pytest.raises(ValueError):
         O.mxgemm(1, 1, 32, z, s, z, s, clear_accum=0)
     with pytest.raises(KeyError):
-        O.mxgemm(1, 1, 32, z, s, z, s, fmt_a="e2m1")
+        O.mxgemm(1, 1, 32, z, s, z, s, fmt_a="e3m2")
     with pytest.raises(ValueError):
         O.mxgemm_points(1, 1, 32, z, s, z, s, [1], [0])
 
@@ -49,6 +49,11 @@ MX_MUTANTS = {
     "b_scaled_by_a_scales": ("* dec_e8m0(SB[n * KB + k / 32]);\n    int64_t rows",
                              "* dec_e8m0(SA[n * KB + k / 32]);\n    int64_t rows"),
     "e5m2_as_e4m3": ("case ORACLE_E5M2: return dec_e5m2(b);", "case ORACLE_E5M2: return dec_e4m3(b);"),
+    "e2m1_high_nibble_first": ("return dec_e2m1((k & 1) ? byte >> 4 : byte & 15u);",
+                               "return dec_e2m1((k & 1) ? byte & 15u : byte >> 4);"),
+    "e2m1_exponent_bias": ("ldexp((double)(2u + frac), (int)e - 1 - 1);", "ldexp((double)(2u + frac), (int)e - 2 - 1);"),
+    "e2m1_subnormal": ("e == 0 ? ldexp((double)frac, 1 - 1 - 1)", "e == 0 ? ldexp((double)frac, 1 - 1)"),
+    "e2m1_row_stride_bytes": ("const uint32_t byte = X[r * (K / 2) + k / 2];", "const uint32_t byte = X[r * K + k / 2];"),
 }
 
 

@@ -159,8 +159,31 @@ def sample_points(M: int, N: int, count: int, seed: int = 7):
 #     exact multiple of 2^-4 and the fp32 sums are exact.
 # ---------------------------------------------------------------------------
 FP8_DTYPES = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
-FP8_EMAX = {"e4m3": 8, "e5m2": 15}
-FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0}
+FP8_EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}
+FP8_MAX = {"e4m3": 448.0, "e5m2": 57344.0, "e2m1": 6.0}
+# MXFP4: E2M1 elements (the magnitudes of codes 0..7), two per byte, element 2i in
+# the low nibble of byte i.  torch has no conversion to this format, so values are
+# rounded to the nearest magnitude here, ties to the even code (RNE).
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_codes(x: torch.Tensor) -> np.ndarray:
+    """Round-to-nearest-even E2M1 codes of finite values with |x| <= 6."""
+    v = np.asarray(x, dtype=np.float64)
+    a = np.abs(v)
+    d = np.abs(a[..., None] - E2M1_MAGNITUDES)                 # distance to each magnitude
+    best = d.min(axis=-1, keepdims=True)
+    tie_ok = d == best
+    # among equally near magnitudes take the even code (codes 0..7 in magnitude order)
+    even = tie_ok & ((np.arange(8) % 2) == 0)
+    code = np.where(even.any(axis=-1), even.argmax(axis=-1), tie_ok.argmax(axis=-1)).astype(np.uint8)
+    return code | (np.signbit(v) & (code > 0)).astype(np.uint8) << 3
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """[rows, K] codes 0..15 -> [rows, K/2] bytes (element 2i in the low nibble of byte i)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
 
 
 @dataclass(frozen=True)
@@ -169,7 +192,7 @@ class MxCase:
     M: int
     N: int
     K: int
-    fmt: str = "e4m3"        # element format of A and B
+    fmt: str = "e4m3"        # element format of A and B: "e4m3", "e5m2" or "e2m1" (MXFP4, packed)
     c: str = "f16"
     relu: int = 0
     clear_accum: int = 1
@@ -188,7 +211,8 @@ class MxCase:
         """One read of A, B and their scales, one write of C (plus a read when accumulating)."""
         sc = 4 if self.c == "f32" else 2
         c_reads = 0 if self.clear_accum else sc * self.M * self.N
-        return (self.M + self.N) * self.K + (self.M + self.N) * (self.K // 32) + sc * self.M * self.N + c_reads
+        elem = self.K // 2 if self.fmt == "e2m1" else self.K
+        return (self.M + self.N) * elem + (self.M + self.N) * (self.K // 32) + sc * self.M * self.N + c_reads
 
     def with_(self, **kw) -> "MxCase":
         return replace(self, **kw)
@@ -201,6 +225,12 @@ MX_CONFIGS = {
                   note="ragged 1000x1500x768 MXFP8 (E5M2), fp32 out"),
     "mx3": MxCase("mx3", 8192, 8192, 8192, seed=1103,
                   note="8192^3 MXFP8 (E4M3, E8M0 scales per 32 of K), fp16 out"),
+    "mx4": MxCase("mx4", 256, 256, 256, fmt="e2m1", relu=1, seed=1104,
+                  note="C=ReLU(A·B) 256^3 MXFP4 (E2M1, E8M0 scales per 32 of K), fp16 out"),
+    "mx5": MxCase("mx5", 1000, 1500, 768, fmt="e2m1", c="f32", dist="uniform", seed=1105,
+                  note="ragged 1000x1500x768 MXFP4 (E2M1), fp32 out"),
+    "mx6": MxCase("mx6", 8192, 8192, 8192, fmt="e2m1", seed=1106,
+                  note="8192^3 MXFP4 (E2M1, E8M0 scales per 32 of K), fp16 out"),
 }
 
 
@@ -216,13 +246,16 @@ def _mx_quantize(v: torch.Tensor, fmt: str, g: torch.Generator, case: MxCase):
         X = X.clamp(-127, 127)
         scales = (X + 127).to(torch.uint8)
         elems = (blocks / torch.exp2(X).unsqueeze(2)).clamp(-FP8_MAX[fmt], FP8_MAX[fmt]).reshape(rows, K)
-    q = elems.to(FP8_DTYPES[fmt]).view(torch.uint8).contiguous()
+    if fmt == "e2m1":
+        q = torch.from_numpy(pack_e2m1(e2m1_codes(elems.numpy()))).contiguous()
+    else:
+        q = elems.to(FP8_DTYPES[fmt]).view(torch.uint8).contiguous()
     return q, scales.contiguous()
 
 
 def make_mx_inputs(case: MxCase, with_c: bool | None = None):
-    """CPU uint8 tensors (A [M,K], SA [M,K/32], B [N,K], SB [N,K/32]) and the prior C
-    (or None when clear_accum)."""
+    """CPU uint8 tensors (A [M,K], SA [M,K/32], B [N,K], SB [N,K/32]; A [M,K/2] and
+    B [N,K/2] packed for E2M1) and the prior C (or None when clear_accum)."""
     if case.K % 32:
         raise ValueError("block-scaled operands need K % 32 == 0")
     g = torch.Generator().manual_seed(case.seed)
