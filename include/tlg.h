@@ -51,8 +51,9 @@ extern "C" {
 
 typedef struct tlg_gemm_s *tlg_gemm_t;
 
-/* TLG_E4M3 / TLG_E5M2: FP8 operands of the block-scaled GEMM (tlg_gemm_run_mx). */
-typedef enum { TLG_F16 = 1, TLG_BF16 = 2, TLG_F32 = 3, TLG_E4M3 = 4, TLG_E5M2 = 5 } tlg_dtype;
+/* TLG_E4M3 / TLG_E5M2: FP8 operands, TLG_E2M1: FP4 operands (two per byte) of the
+ * block-scaled GEMM (tlg_gemm_run_mx). */
+typedef enum { TLG_F16 = 1, TLG_BF16 = 2, TLG_F32 = 3, TLG_E4M3 = 4, TLG_E5M2 = 5, TLG_E2M1 = 6 } tlg_dtype;
 
 typedef enum { TLG_EPI_NONE = 0, TLG_EPI_RELU = 1 } tlg_epilogue;
 
@@ -67,7 +68,7 @@ typedef enum {
     TLG_VARIANT_TILE_256_DMA = 6, /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
     TLG_VARIANT_TILE_128_DMA = 7, /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
     TLG_VARIANT_TILE_128_DMA_SPLITK = 8, /* as 7, K split over several workgroups per tile (plan owns a workspace) */
-    TLG_VARIANT_MX_256 = 9,    /* block-scaled FP8: 256x256x128, 8 wave64s, scaled MFMA 16x16x128 */
+    TLG_VARIANT_MX_256 = 9,    /* block-scaled FP8 / FP4: 256x256 x 128 bytes of K, 8 wave64s, scaled MFMA 16x16x128 */
     TLG_VARIANT_TILE_64_DMA = 10, /* 64x128x64, 8 wave64s, 4-slot ring of direct loads; A stored [M,K] only
                                     (transpose_A == 0); grids of at most 128 tiles of 128x128 */
     TLG_VARIANT_TILE_256_DMA_STREAMK = 11, /* as 6, persistent: 256 workgroups (one per CU) take the tiles
@@ -224,21 +225,24 @@ tlg_status tlg_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int32_t ab_dtyp
 
 /*
  * Block-scaled ("MX") GEMM: the block-scaled MMA of the codegen chapter
- * (sections 3.4 and 4.6.3): FP8 elements in which every 32 consecutive
- * elements along K share one E8M0 scale factor, fp32 accumulation.  A plan is
- * made by tlg_gemm_create with ab_dtype TLG_E4M3 or TLG_E5M2 (both operands
- * in that format), transpose_A = 0 and transpose_B = 1, and K a multiple of
- * 128; any other combination is refused with TLG_ERR_UNSUPPORTED (a scaled
- * operand is never run without its scales).  Value computed:
+ * (sections 3.4 and 4.6.3, MXFP8 / MXFP4): FP8 or FP4 elements in which every 32
+ * consecutive elements along K share one E8M0 scale factor, fp32 accumulation.
+ * A plan is made by tlg_gemm_create with ab_dtype TLG_E4M3, TLG_E5M2 or TLG_E2M1
+ * (both operands in that format), transpose_A = 0 and transpose_B = 1, and K a
+ * multiple of 128; any other combination is refused with TLG_ERR_UNSUPPORTED (a
+ * scaled operand is never run without its scales).  Value computed:
  *   acc(m,n) = (clear_accum ? 0 : (float)C[m*N + n])
  *              + sum_k (A[m*K + k] * 2^(SA[m*(K/32) + k/32] - 127))
  *                      * (B[n*K + k] * 2^(SB[n*(K/32) + k/32] - 127))
  *   C[m*N + n] = convert_rne(epilogue == RELU ? max(acc, +0) : acc)
  * where A[.] and B[.] are decoded as E4M3 (1 sign, 4 exponent bits with bias 7,
- * 3 fraction bits, no infinity) or E5M2 (IEEE-style, 5/2 bits, bias 15).
- *   A  : device pointer, M x K bytes, row-major (16-byte aligned).
+ * 3 fraction bits, no infinity), E5M2 (IEEE-style, 5/2 bits, bias 15) or E2M1
+ * (1 sign, 2 exponent bits with bias 1, 1 fraction bit, no infinity or NaN;
+ * element k of a row in the low nibble of byte k/2 when k is even, the high
+ * nibble when odd).
+ *   A  : device pointer, M x K bytes (M x K/2 for E2M1), row-major (16-byte aligned).
  *   SA : device pointer, M x K/32 E8M0 bytes (4-byte aligned).
- *   B  : device pointer, N x K bytes, row-major (16-byte aligned).
+ *   B  : device pointer, N x K bytes (N x K/2 for E2M1), row-major (16-byte aligned).
  *   SB : device pointer, N x K/32 E8M0 bytes (4-byte aligned).
  *   C  : as for tlg_gemm_run.
  * Returns TLG_ERR_INVALID_ARG for a plan that is not block-scaled (or C

@@ -141,6 +141,25 @@ def test_mx_8192_small_integers_exact():
     assert_exact(gpu, o, case, plan.describe())
 
 
+def test_mxfp4_8192_small_integers_exact():
+    """MXFP4 (E2M1, two per byte) at 8192^3: elements in [-2, 2] and scales 2^-2..2^2 keep
+    every partial sum exact in fp32, as for MXFP8."""
+    import tiled_dense_gemm_02_amd as tlg
+    case = W.MxCase("mx6-int", 8192, 8192, 8192, fmt="e2m1", c="f32", dist="smallint", lo=-2, hi=2, seed=4105)
+    log(f"[case] full-size {case.name} exact")
+    A, SA, B, SB, _ = W.make_mx_inputs(case)
+    dev = torch.device("cuda:0")
+    C = torch.empty((case.M, case.N), dtype=torch.float32, device=dev)
+    plan = tlg.Gemm(case.M, case.N, case.K, case.fmt, torch.float32, transpose_B=True)
+    plan.run_mx(A.to(dev), SA.to(dev), B.to(dev), SB.to(dev), C)
+    torch.cuda.synchronize()
+    gpu = out_values(C)
+    del C
+    o = O.mxgemm(case.M, case.N, case.K, A.numpy(), SA.numpy(), B.numpy(), SB.numpy(), fmt_a=case.fmt,
+                 fmt_b=case.fmt, c=case.c)
+    assert_exact(gpu, o, case, plan.describe())
+
+
 def test_sparse_8192_small_integers_exact():
     """2:4 sparse GEMM at 8192^3 on integers in [-4, 4]: 4096 products per output, each
     at most 16, so every partial sum is an integer below 2^24."""

@@ -131,3 +131,52 @@ def test_mx_deterministic_and_plain_run_refused():
     Ad, Bd = A.cuda(), B.cuda()
     with pytest.raises(tlg.TlgError):
         plan.run(Ad.view(torch.float8_e4m3fn), Bd.view(torch.float8_e4m3fn), C1)   # scales are required
+
+
+# ---------------------------------------------------------------- MXFP4 (E2M1 elements, two per byte)
+def test_mxfp4_mx4_relu_256():
+    plan = _full_check(W.MX_CONFIGS["mx4"], guard=4096)
+    assert plan.info.variant == 9 and plan.info.block_k == 256 and plan.info.k_tiles == 1
+
+
+def test_mxfp4_mx5_ragged_f32out():
+    _full_check(W.MX_CONFIGS["mx5"], guard=4096)
+
+
+def test_mxfp4_mx6_8192_sampled():
+    case = W.MX_CONFIGS["mx6"]
+    log(f"[case] {case.name} sampled")
+    A, SA, B, SB, _ = W.make_mx_inputs(case)
+    C, plan = _run(case, A, SA, B, SB, None)
+    ms, ns = W.sample_points(case.M, case.N, 2048)
+    o = O.mxgemm_points(case.M, case.N, case.K, _np(A), _np(SA), _np(B), _np(SB), ms, ns, fmt_a=case.fmt,
+                        fmt_b=case.fmt, c=case.c)
+    gpu = out_values(C)
+    err = assert_within_tolerance(gpu[ms, ns], o, case, plan.describe())
+    assert np.isfinite(gpu).all()
+    log(f"    max|err| = {err:.3e}  ({plan.describe()})")
+
+
+@pytest.mark.parametrize("K", [384, 512])
+@pytest.mark.parametrize("c", ["f32", "f16"])
+def test_mxfp4_small_integers_exact(K, c):
+    """K = 384: the last K tile of 256 FP4 elements is half full (zero fill of the data
+    and of the second scale plane)."""
+    case = W.MxCase("mxfp4-smallint", 300, 264, K, fmt="e2m1", c=c, relu=1, dist="smallint", seed=78)
+    _full_check(case, exact=True, guard=1024)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 128), (17, 33, 128), (255, 257, 256), (256, 256, 0), (513, 130, 640)])
+def test_mxfp4_edges(shape):
+    M, N, K = shape
+    for it, (c, relu) in enumerate((("bf16", 1), ("f16", 0))):
+        case = W.MxCase(f"mxfp4-edge{M}x{N}x{K}", M, N, K, fmt="e2m1", c=c, relu=relu, dist="uniform", seed=610 + it)
+        if K == 0:
+            case = case.with_(clear_accum=0)
+        _full_check(case, guard=1024)
+
+
+def test_mxfp4_accumulate_onto_c():
+    for c in ("f16", "f32"):
+        case = W.MxCase(f"mxfp4-accum-{c}", 264, 200, 384, fmt="e2m1", c=c, clear_accum=0, relu=1, seed=32)
+        _full_check(case)

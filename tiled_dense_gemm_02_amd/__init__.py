@@ -16,14 +16,14 @@ import threading
 import torch
 
 __all__ = ["Gemm", "gemm", "gemm_mx", "gemm_noalloc", "select", "tune", "PlanInfo", "TuneResult", "TlgError", "lib_path", "load_library",
-           "status_name", "VARIANTS", "F16", "BF16", "F32", "E4M3", "E5M2"]
+           "status_name", "VARIANTS", "F16", "BF16", "F32", "E4M3", "E5M2", "E2M1"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtlg.so")
 
-F16, BF16, F32, E4M3, E5M2 = 1, 2, 3, 4, 5
+F16, BF16, F32, E4M3, E5M2, E2M1 = 1, 2, 3, 4, 5, 6
 _TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
-                  torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2}
+                  torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.float4_e2m1fn_x2: E2M1}
 VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "tile256w8": 5,
             "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8, "mx256": 9, "tile64dma": 10,
             "tile256dma_streamk": 11, "tile128dma_streamk": 12}
@@ -114,7 +114,7 @@ def _code(dt) -> int:
     if isinstance(dt, int):
         return dt
     if isinstance(dt, str):
-        return {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2}[dt]
+        return {"f16": F16, "bf16": BF16, "f32": F32, "e4m3": E4M3, "e5m2": E5M2, "e2m1": E2M1}[dt]
     return _TORCH_TO_CODE[dt]
 
 
@@ -207,9 +207,11 @@ class Gemm:
     def run_mx(self, A: torch.Tensor, SA: torch.Tensor, B: torch.Tensor, SB: torch.Tensor, C: torch.Tensor,
                stream=None) -> torch.Tensor:
         """Enqueue the block-scaled GEMM (tlg_gemm_run_mx).  A [M,K] and B [N,K] hold FP8 bytes
-        (uint8 or the matching float8 dtype), SA [M,K/32] and SB [N,K/32] E8M0 bytes."""
+        (uint8 or the matching float8 dtype), or for E2M1 A [M,K/2] and B [N,K/2] packed FP4
+        bytes; SA [M,K/32] and SB [N,K/32] E8M0 bytes."""
         M, N, K = self.M, self.N, self.K
-        for name, t, shape in (("A", A, (M, K)), ("SA", SA, (M, K // 32)), ("B", B, (N, K)),
+        KE = K // 2 if self.ab_code == E2M1 else K      # bytes per operand row
+        for name, t, shape in (("A", A, (M, KE)), ("SA", SA, (M, K // 32)), ("B", B, (N, KE)),
                                ("SB", SB, (N, K // 32)), ("C", C, (M, N))):
             if not isinstance(t, torch.Tensor):
                 raise TypeError(f"{name} must be a torch.Tensor")
@@ -290,8 +292,11 @@ def tune(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, transpose_A: bool
 def gemm_mx(A: torch.Tensor, SA: torch.Tensor, B: torch.Tensor, SB: torch.Tensor, C: torch.Tensor | None = None,
             *, fmt: str = "e4m3", clear_accum: bool = True, epilogue: str = "none",
             out_dtype=torch.float16) -> torch.Tensor:
-    """Block-scaled FP8 GEMM C = act(A·Bᵀ) with E8M0 scales per 32 of K (A [M,K], B [N,K])."""
+    """Block-scaled GEMM C = act(A·Bᵀ) with E8M0 scales per 32 of K: FP8 (A [M,K], B [N,K]) or,
+    with fmt="e2m1", FP4 packed two per byte (A [M,K/2], B [N,K/2])."""
     M, K = A.shape
+    if fmt == "e2m1":
+        K *= 2
     N = B.shape[0]
     if C is None:
         if not clear_accum:

@@ -34,6 +34,20 @@
 // The ring barrier sits after MFMA 20, once every read of the current slot has
 // been issued; after it the tile two ahead is loaded into the freed slot, one
 // load per MFMA.
+//
+// MXFP4 (FMT 4: E2M1 elements, two per byte).  A 128-byte K tile row then holds
+// 256 elements, so the tile program, the LDS layout and the fragment reads are
+// the FP8 kernel's byte for byte; what changes is the instruction's view of a
+// fragment.  With FP4 operands the instruction reads four registers per lane:
+// lane l holds row l % 16 and K elements 32 g .. 32 g + 31 (g = l / 16), 16
+// consecutive bytes (measured on MI355X: one wave, random codes and scales,
+// compared with the host's sums under each candidate layout).  LDS chunk g of a
+// row is therefore the operand of the tile's first 128 K elements and chunk 4 + g
+// that of the second: each fragment pair (i, j) of a tile is two MFMAs, one per
+// K half, each with its own scale byte (blocks 0..3 and 4..7 of the tile, kept in
+// two scale planes of 4 bytes per row).  Per A fragment the eight MFMAs are
+// issued as the four first halves, then the four second halves, so an
+// accumulator's two MFMAs are four instructions apart.
 #pragma once
 
 #include "gemm_lds.hpp"
@@ -56,27 +70,38 @@ __device__ inline void dma4(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
 
 __device__ inline uint32_t lds_u8(const char* p) { return *(const unsigned char*)p; }
 
-// FMT: operand format code of the scaled instruction (0 = E4M3, 1 = E5M2).
-template <int FMT>
+// FMT: operand format code of the scaled instruction (0 = E4M3, 1 = E5M2, 4 = E2M1).
+// SEL: which byte of the scale registers holds the E8M0 scales (the instruction's
+// scale byte select).
+template <int FMT, int SEL = 0>
 __device__ inline f32x4 mfma_scale16x16x128(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb)
 {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, SEL, sa, SEL, sb);
+}
+
+// FP4 operands occupy the low four registers; the upper half is not read.
+__device__ inline i32x8 fp4_operand(const u32x4& x)
+{
+    const i32x4 v = __builtin_bit_cast(i32x4, x);
+    return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
 template <int FMT>
 __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
 {
-    constexpr int BM = 256, BN = 256, BKB = 128;        // K tile: 128 FP8 elements = 128 bytes per row
+    constexpr bool FP4 = FMT == 4;
+    constexpr int BM = 256, BN = 256;                    // K tile: 128 bytes per row (128 FP8 / 256 FP4 elements)
+    constexpr int PLANES = FP4 ? 2 : 1;                  // scale planes of 4 bytes per row per tile
     constexpr int WAVES_M = 2, WAVES_N = 4, NW = 8;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
     // A K-tile row has the byte layout of a 64-element 16-bit row: the operand
     // helper works in 16-bit units (K/2 of them per row).
     using OpA = LdsOperand<BM, 64, true, NW>;
     using OpB = LdsOperand<BN, 64, true, NW>;
-    constexpr int SCB = BM * 4;                          // scale bytes per operand per tile
-    constexpr int STAGE = OpA::BYTES + OpB::BYTES + 2 * SCB;
+    constexpr int SCB = BM * 4;                          // scale bytes per operand per plane per tile
+    constexpr int STAGE = OpA::BYTES + OpB::BYTES + 2 * PLANES * SCB;
     constexpr int LD = OpA::L + OpB::L;                  // 16-byte data loads per wave per tile
-    constexpr int L = LD + 1;                            // plus one 4-byte scale load
+    constexpr int L = LD + PLANES;                       // plus one 4-byte scale load per plane
     constexpr int MI = FM * FN;                          // MFMAs per tile
     constexpr int NBUF = 4;                              // rotating A fragment buffers
     constexpr int LEAD = 3 * FN;                         // A fragment i is read before MFMA FN*i - LEAD
@@ -96,8 +121,9 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
     int tm, tn;
     tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const int K = p.K, K16 = K / 2, KB = K / 32;
-    const int TP = K / BKB;
+    const int K = p.K, KB = K / 32;
+    const int K16 = FP4 ? K / 4 : K / 2;                 // row length in 16-bit units
+    const int TP = (K16 + 63) / 64;                      // K tiles (an FP4 K of 128 mod 256: last tile half full)
 
     OpA opa;
     OpB opb;
@@ -113,24 +139,28 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
     const int sc_rows_left = sc_a ? p.M - m0 : p.N - n0;
     const uint64_t sc_bytes = (uint64_t)sc_rows_left * KB;
     const uint32_t sc_voff = sc_row < sc_rows_left ? (uint32_t)sc_row * (uint32_t)KB : kOOB;
-    const uint32_t sc_dst_off = (uint32_t)(OpA::BYTES + OpB::BYTES + (sc_a ? 0 : SCB) + (wave & 3) * 256);
+    // plane h of the tile: A's planes, then B's
+    const uint32_t sc_dst_off = (uint32_t)(OpA::BYTES + OpB::BYTES + (sc_a ? 0 : PLANES * SCB) + (wave & 3) * 256);
 
     struct TileRes {
         i32x4 ra, rb, rs;
         int k0;          // in 16-bit units
         uint32_t slot, sslot;
-        uint32_t soff;
+        uint32_t soff[PLANES];
     };
     auto tile_res = [&](int t) {
         TileRes r;
         r.k0 = t * 64;
         r.ra = opa.rsrc(r.k0);
         r.rb = opb.rsrc(r.k0);
-        const uint64_t so = (uint64_t)t * 4u;
+        const uint64_t so = (uint64_t)t * 4u * PLANES;
         r.rs = rsrc_words(sc_base + so, so < sc_bytes ? sc_bytes - so : 0);
         r.slot = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t & 1) * STAGE) + (uint32_t)wave * 1024u);
         r.sslot = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t & 1) * STAGE) + sc_dst_off);
-        r.soff = t < TP ? sc_voff : kOOB;
+        // plane h covers scale blocks 4 (PLANES t + h) .. +3; past the row's KB blocks it reads zeros
+#pragma unroll
+        for (int h = 0; h < PLANES; ++h)
+            r.soff[h] = (t < TP && (t * PLANES + h) * 4 < KB) ? sc_voff + (uint32_t)(4 * h) : kOOB;
         return r;
     };
     auto issue_one = [&](const TileRes& r, int i) {
@@ -139,7 +169,7 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
         else if (i < LD)
             dma16(r.rb, opb.voff(i - OpA::L, r.k0, K16), r.slot + (uint32_t)OpA::BYTES + (uint32_t)((i - OpA::L) * NW * 1024));
         else
-            dma4(r.rs, r.soff, r.sslot);
+            dma4(r.rs, r.soff[i - LD], r.sslot + (uint32_t)((i - LD) * SCB));
     };
 
     f32x4 acc[FM][FN];
@@ -151,17 +181,31 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
     const int arow = wm * WTM, bcol = wn * WTN;
     i32x8 fa[NBUF], fb[FN];
     int sa[NBUF], sb[FN];
-    // fragment (two 16-byte chunks: K 16g.. and 64+16g..) and its scale byte
+    // fragment (two 16-byte chunks g and 4+g of the row) and its scale byte(s): the
+    // lane's row and K block (lane >> 4); with two planes, plane h's byte goes to
+    // byte h of the register (selected per MFMA by the instruction)
     auto read_a = [&](const char* slot, int i) {
         const u32x4 lo = opa.frag(slot, arow + i * 16, 0, lane), hi = opa.frag(slot, arow + i * 16, 1, lane);
         fa[i % NBUF] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sa[i % NBUF] = (int)lds_u8(slot + OpA::BYTES + OpB::BYTES + (arow + i * 16 + (lane & 15)) * 4 + (lane >> 4));
+        const char* sp = slot + OpA::BYTES + OpB::BYTES + (arow + i * 16 + (lane & 15)) * 4 + (lane >> 4);
+        int v = (int)lds_u8(sp);
+        if constexpr (PLANES == 2) v |= (int)lds_u8(sp + SCB) << 8;
+        sa[i % NBUF] = v;
     };
     auto read_b = [&](const char* slot, int j) {
         const char* bs = slot + OpA::BYTES;
         const u32x4 lo = opb.frag(bs, bcol + j * 16, 0, lane), hi = opb.frag(bs, bcol + j * 16, 1, lane);
         fb[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        sb[j] = (int)lds_u8(slot + OpA::BYTES + OpB::BYTES + SCB + (bcol + j * 16 + (lane & 15)) * 4 + (lane >> 4));
+        const char* sp = slot + OpA::BYTES + OpB::BYTES + PLANES * SCB + (bcol + j * 16 + (lane & 15)) * 4 + (lane >> 4);
+        int v = (int)lds_u8(sp);
+        if constexpr (PLANES == 2) v |= (int)lds_u8(sp + SCB) << 8;
+        sb[j] = v;
+    };
+    // FP4: the K half (0: chunk g, 1: chunk 4+g) of a fragment as the instruction's operand
+    auto half_of = [](const i32x8& f, int h) {
+        const u32x4 x = h == 0 ? u32x4{(unsigned)f[0], (unsigned)f[1], (unsigned)f[2], (unsigned)f[3]}
+                               : u32x4{(unsigned)f[4], (unsigned)f[5], (unsigned)f[6], (unsigned)f[7]};
+        return fp4_operand(x);
     };
 
     // Prologue: tile 0 whole; tile 1 is loaded in tile 0's iteration (after its
@@ -210,12 +254,29 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
                 if constexpr (g < FM) read_a(cur, g);
                 else if (g < FM + NBUF) read_a(nxt, g - FM);
             }
-            if constexpr (m > (FM - 1) * FN) read_b(nxt, m - (FM - 1) * FN - 1);   // after the last use of B fragment
+            if constexpr (!FP4) {
+                if constexpr (m > (FM - 1) * FN) read_b(nxt, m - (FM - 1) * FN - 1);   // after the last use of B fragment
+            } else {
+                // last uses in the last row block: fragments 0, 1 at step 2 (second half),
+                // fragments 2, 3 at step 3
+                if constexpr (m == (FM - 1) * FN + 3) { read_b(nxt, 0); read_b(nxt, 1); }
+                if constexpr (m == MI) { read_b(nxt, 2); read_b(nxt, 3); }
+            }
             if constexpr (m < MI) {
-                constexpr int i = m / FN, j = m % FN;
+                constexpr int i = m / FN, q = m % FN;
                 // B fragment first: the hardware tile is C's transpose (lane l holds
                 // C[m0 + l%16][n0 + 4 (l/16) + e]).
-                acc[i][j] = mfma_scale16x16x128<FMT>(fb[j], fa[i % NBUF], acc[i][j], sb[j], sa[i % NBUF]);
+                if constexpr (!FP4) {
+                    acc[i][q] = mfma_scale16x16x128<FMT>(fb[q], fa[i % NBUF], acc[i][q], sb[q], sa[i % NBUF]);
+                } else {
+                    // steps q = 0, 1: first K half of (i, 2q), (i, 2q+1); q = 2, 3: second half of (i, 2q-4), (i, 2q-3)
+                    constexpr int h = (2 * q) / FN, j0 = (2 * q) % FN;
+                    static_assert(FN == 4, "two MFMAs per step over four B fragments");
+                    acc[i][j0] = mfma_scale16x16x128<FMT, h>(half_of(fb[j0], h), half_of(fa[i % NBUF], h), acc[i][j0],
+                                                             sb[j0], sa[i % NBUF]);
+                    acc[i][j0 + 1] = mfma_scale16x16x128<FMT, h>(half_of(fb[j0 + 1], h), half_of(fa[i % NBUF], h),
+                                                                 acc[i][j0 + 1], sb[j0 + 1], sa[i % NBUF]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         });

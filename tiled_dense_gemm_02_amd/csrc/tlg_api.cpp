@@ -49,9 +49,9 @@ namespace {
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 22;
 
-int elem_bytes(int dt) { return dt == TLG_F32 ? 4 : (dt == TLG_E4M3 || dt == TLG_E5M2) ? 1 : 2; }
+int elem_bytes(int dt) { return dt == TLG_F32 ? 4 : (dt == TLG_E4M3 || dt == TLG_E5M2 || dt == TLG_E2M1) ? 1 : 2; }
 
-bool is_mx(int dt) { return dt == TLG_E4M3 || dt == TLG_E5M2; }
+bool is_mx(int dt) { return dt == TLG_E4M3 || dt == TLG_E5M2 || dt == TLG_E2M1; }
 
 const char* dt_name(int dt)
 {
@@ -61,6 +61,7 @@ const char* dt_name(int dt)
     case TLG_F32: return "f32";
     case TLG_E4M3: return "e4m3";
     case TLG_E5M2: return "e5m2";
+    case TLG_E2M1: return "e2m1";
     default: return "?";
     }
 }
@@ -158,15 +159,16 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     if (M < 0 || N < 0 || K < 0 || M > kMaxMN || N > kMaxMN || K > kMaxK) return TLG_ERR_INVALID_ARG;
     if (!flag_ok(tA) || !flag_ok(tB) || !flag_ok(clear)) return TLG_ERR_INVALID_ARG;
     if (epi != TLG_EPI_NONE && epi != TLG_EPI_RELU) return TLG_ERR_INVALID_ARG;
-    if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32 && ab != TLG_E4M3 && ab != TLG_E5M2)
+    if (ab != TLG_F16 && ab != TLG_BF16 && ab != TLG_F32 && !is_mx(ab))
         return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
     if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA_STREAMK || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
     if (is_mx(ab)) {
-        // Block-scaled FP8: A stored [M, K], B stored [N, K], whole 128-wide K
-        // tiles; anything else is refused rather than run without its scales.
+        // Block-scaled FP8 / FP4: A stored [M, K], B stored [N, K], K a multiple of
+        // 128 (whole scale words of four blocks); anything else is refused rather
+        // than run without its scales.  An FP4 K tile is 256 elements (128 bytes).
         if (tA || !tB || K % 128 != 0) return TLG_ERR_UNSUPPORTED;
         if (forced != TLG_VARIANT_AUTO && forced != TLG_VARIANT_MX_256) return TLG_ERR_UNSUPPORTED;
         const int variant = (M == 0 || N == 0) ? TLG_VARIANT_EMPTY : TLG_VARIANT_MX_256;
@@ -181,12 +183,13 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         in.variant = variant;
         in.vec_a = in.vec_b = 16;
         if (variant == TLG_VARIANT_MX_256) {
-            in.block_m = 256; in.block_n = 256; in.block_k = 128;
+            const int planes = ab == TLG_E2M1 ? 2 : 1;
+            in.block_m = 256; in.block_n = 256; in.block_k = 128 * planes;
             in.stages = 2;
             in.threads = 512;
             in.grid = ceil_div(M, 256) * ceil_div(N, 256);
-            in.lds_bytes = 2 * (2 * 256 * 128 + 2 * 256 * 4);
-            in.k_tiles = (int32_t)(K / 128);
+            in.lds_bytes = 2 * (2 * 256 * 128 + 2 * planes * 256 * 4);
+            in.k_tiles = (int32_t)ceil_div(K, in.block_k);
         }
         in.splits = 1;
         std::snprintf(p->desc, sizeof(p->desc),
@@ -619,7 +622,7 @@ tlg_status tlg_gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int32_t ab_dtyp
                                 int32_t transpose_A, int32_t transpose_B, int32_t clear_accum, int32_t epilogue,
                                 const void* A, const void* B, void* C, void* stream)
 {
-    if (ab_dtype == TLG_E4M3 || ab_dtype == TLG_E5M2) return TLG_ERR_UNSUPPORTED;   // block-scaled: tlg_gemm_run_mx
+    if (is_mx(ab_dtype)) return TLG_ERR_UNSUPPORTED;   // block-scaled: tlg_gemm_run_mx
     tlg_gemm_s p;   // on the stack: plan_build is host work only and allocates nothing
     tlg_status st = plan_build(&p, M, N, K, ab_dtype, c_dtype, transpose_A, transpose_B, clear_accum, epilogue,
                                TLG_VARIANT_AUTO);
@@ -653,9 +656,11 @@ tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const
     const int cb = elem_bytes(p.c);
     if (c % (uintptr_t)cb) return TLG_ERR_MISALIGNED;
     if (p.K > 0 && ((a % 16) || (b % 16) || (sa % 4) || (sb % 4))) return TLG_ERR_MISALIGNED;
-    const uint64_t a_bytes = p.K > 0 ? (uint64_t)p.M * (uint64_t)p.K : 0;
-    const uint64_t b_bytes = p.K > 0 ? (uint64_t)p.N * (uint64_t)p.K : 0;
-    const uint64_t sa_bytes = a_bytes / 32, sb_bytes = b_bytes / 32;
+    const uint64_t a_elems = p.K > 0 ? (uint64_t)p.M * (uint64_t)p.K : 0;
+    const uint64_t b_elems = p.K > 0 ? (uint64_t)p.N * (uint64_t)p.K : 0;
+    const uint64_t per_byte = p.ab == TLG_E2M1 ? 2 : 1;   // FP4: two elements per byte
+    const uint64_t a_bytes = a_elems / per_byte, b_bytes = b_elems / per_byte;
+    const uint64_t sa_bytes = a_elems / 32, sb_bytes = b_elems / 32;
     const uint64_t c_bytes = (uint64_t)p.M * (uint64_t)p.N * (uint64_t)cb;
     if (ranges_overlap(c, c_bytes, a, a_bytes) || ranges_overlap(c, c_bytes, b, b_bytes) ||
         ranges_overlap(c, c_bytes, sa, sa_bytes) || ranges_overlap(c, c_bytes, sb, sb_bytes))
@@ -669,7 +674,7 @@ tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const
     mp.c_vec = (p.N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
     mp.tiles_m = (int)ceil_div(p.M, 256);
     mp.tiles_n = (int)ceil_div(p.N, 256);
-    const hipError_t err = launch_mx(mp, p.ab == TLG_E4M3 ? 0 : 1, (hipStream_t)stream);
+    const hipError_t err = launch_mx(mp, p.ab == TLG_E4M3 ? 0 : p.ab == TLG_E5M2 ? 1 : 4, (hipStream_t)stream);
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }
 
@@ -679,7 +684,7 @@ tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, in
     if (batch < 0 || seq < 0 || heads < 0 || dim <= 0) return TLG_ERR_INVALID_ARG;
     if (!flag_ok(causal) || !std::isfinite(softmax_scale)) return TLG_ERR_INVALID_ARG;
     if (dtype != TLG_F16 && dtype != TLG_BF16) {
-        if (dtype == TLG_F32 || dtype == TLG_E4M3 || dtype == TLG_E5M2) return TLG_ERR_UNSUPPORTED;
+        if (dtype == TLG_F32 || is_mx(dtype)) return TLG_ERR_UNSUPPORTED;
         return TLG_ERR_INVALID_ARG;
     }
     if (dim != 64 && dim != 128) return TLG_ERR_UNSUPPORTED;

@@ -124,7 +124,7 @@ struct MxParams {
     int relu, clear_accum, c_dtype, c_vec;
     int tiles_m, tiles_n;
 };
-hipError_t launch_mx(const MxParams& p, int fmt, hipStream_t stream);   // fmt: 0 = E4M3, 1 = E5M2
+hipError_t launch_mx(const MxParams& p, int fmt, hipStream_t stream);   // fmt: 0 = E4M3, 1 = E5M2, 4 = E2M1
 
 // Attention forward (attn_fwd.hip).  Q, K, V, O are [B, S, H, dim] (dim 64 or 128),
 // fp16 or bf16, 16-byte aligned; S >= 1; S * H * dim * 2 < 2^31.
