@@ -19,10 +19,11 @@ least 100 ms of GPU time has passed (power management and the shader clock settl
 only after tens of milliseconds of load), then exactly K launches between device
 synchronisations, with a HIP event recorded on the launch stream before every
 launch and after the last one.  The mean is the headline; min / median / p90
-come from a second pass in which each launch has its own pair of events.  The
-shader clock and socket power are sampled from a thread of this process through
-the amdsmi library (started before the first GPU call), over 300 ms of further
-launches of the same workload right after the timed ones.
+come from a second pass in which each launch has its own pair of events.  For the
+three target workloads the shader clock and socket power are sampled from a
+thread of this process through the amdsmi library (started before the first GPU
+call), over 1.5 s of further launches of the same workload right after the
+timed ones (the driver refreshes the readings about once a second).
 """
 from __future__ import annotations
 
@@ -46,10 +47,15 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6,     # 256 CU x 4096 FLOP/clk x 2.4
 FLOP_PER_CLK_CU = {"f16": 4096, "bf16": 4096, "e4m3": 8192, "e5m2": 8192, "e2m1": 16384}
 PEAK_HBM_GBS = 8000.0
 WARM_MS = 100.0
-CLOCK_MS = 300.0
+# The metrics table refreshes about once a second, so the clock window spans
+# 1.5 s of launches (one or two fresh readings); it is taken for the three target
+# workloads only.
+CLOCK_MS = 1500.0
+CLOCK_WORKLOADS = ("c5a", "c3", "c5b")
 WARM_RULE = (f"W untimed launches, then more until >= {WARM_MS:.0f} ms of GPU time, then K timed launches "
              "between two HIP events on the launch stream (the mean); then K launches each between its own "
-             f"event pair (min/median/p90); then {CLOCK_MS:.0f} ms more launches while the clock is sampled")
+             f"event pair (min/median/p90); then {CLOCK_MS:.0f} ms more launches while the clock is sampled "
+             f"(workloads {', '.join(CLOCK_WORKLOADS)})")
 # Sources of each kernel family, keyed by the plan's variant number (tlg.h).
 KERNEL_SOURCES = {
     1: ["gemm_tile.hpp", "tlg_device.hpp"],
@@ -139,13 +145,19 @@ class ClockSampler:
         clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
         clk = sum(clks) / len(clks) if clks else m.get("current_gfxclk")
         pw = m.get("current_socket_power")
-        return (clk if isinstance(clk, (int, float)) else None, pw if isinstance(pw, (int, float)) else None)
+        return (m.get("firmware_timestamp"), clk if isinstance(clk, (int, float)) else None,
+                pw if isinstance(pw, (int, float)) else None)
 
     def _run(self):
+        # The driver refreshes the metrics table about once a second (measured on
+        # MI355X): only samples with a new firmware timestamp are kept.
+        last = None
         while not self._stop.is_set():
             try:
-                clk, pw = self._one()
-                self.samples.append((time.perf_counter(), clk, pw))
+                stamp, clk, pw = self._one()
+                if stamp != last:
+                    last = stamp
+                    self.samples.append((time.perf_counter(), clk, pw))
             except Exception as e:
                 self.error = f"{type(e).__name__}: {e}"
                 return
@@ -246,7 +258,7 @@ def device_facts(sampler: ClockSampler):
 
 
 # ---------------------------------------------------------------------------- timing
-def timed_launches(launch, stream, steps, warmup, sampler=None):
+def timed_launches(launch, stream, steps, warmup, sampler=None, clock=True):
     """The one timing rule (see the module docstring).  launch(i) enqueues launch i and
     returns its status.
 
@@ -295,7 +307,7 @@ def timed_launches(launch, stream, steps, warmup, sampler=None):
     torch.cuda.synchronize()
     # clock window
     clock = None
-    if sampler is not None and sampler.error is None and CLOCK_MS > 0:
+    if clock and sampler is not None and sampler.error is None and CLOCK_MS > 0:
         n = int(math.ceil(CLOCK_MS / per))
         c0 = time.perf_counter()
         for i in range(n):
@@ -318,7 +330,8 @@ def timed_launches(launch, stream, steps, warmup, sampler=None):
     r = {"ms": mean, "wall_s": t1 - t0,
          "per_launch_ms": {"mean": mean, "min": each[0], "median": q(0.5), "p90": q(0.9), "max": each[-1]}}
     if sampler is not None:
-        r["clock"] = clock if clock is not None else {"sclk_mhz": None, "error": sampler.error}
+        r["clock"] = clock if clock is not None else {"sclk_mhz": None, "error": sampler.error,
+                                                      "note": None if sampler.error else "not sampled"}
     return r
 
 
@@ -354,7 +367,7 @@ def measure(case, steps, warmup, sampler=None, log=None, variant="auto"):
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
     r = timed_launches(lambda i: plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh), stream, steps,
-                       warmup, sampler)
+                       warmup, sampler, clock=case.name in CLOCK_WORKLOADS)
     r.update({"plan": plan, "describe": plan.describe(), "C": C, "nsets": nsets})
     return r
 
@@ -383,7 +396,7 @@ def measure_mx(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler)
+    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
     r.update({"plan": plan, "describe": plan.describe(), "C": C, "nsets": nsets})
     return r
 
@@ -412,7 +425,7 @@ def measure_attn(case, steps, warmup, sampler=None, log=None):
     if log:
         log(f"[bench] {case.name}: attention B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} "
             f"sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler)
+    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
     r.update({"C": O, "nsets": nsets,
               "describe": f"attn_fwd block=128x64 threads=256 dim={case.D} causal={case.causal} dtype={case.dtype}"})
     return r
@@ -440,7 +453,7 @@ def measure_w4(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: w4 M={case.M} N={case.N} K={case.K} G={case.G} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler)
+    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
     r.update({"C": C, "nsets": nsets,
               "describe": f"gemm_w4 block=16x64x512 threads={kernel_constant('kW4Threads')} group={case.G} "
                           f"{case.ab}->{case.c}"})
@@ -469,7 +482,7 @@ def measure_sp(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: sp M={case.M} N={case.N} K={case.K} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler)
+    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
     r.update({"C": C, "nsets": nsets, "describe": f"gemm_sp block=256x256x64 threads=512 {case.ab}->{case.c}"})
     return r
 
@@ -755,7 +768,7 @@ def main():
         WARM_RULE = WARM_RULE.replace(">= 100 ms", f">= {WARM_MS:g} ms")
     if args.no_clock:
         CLOCK_MS = 0.0
-        WARM_RULE = WARM_RULE.split("; then 300 ms")[0]
+        WARM_RULE = WARM_RULE.split("; then 1500 ms")[0]
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               f"the sharding across GPUs is not built", file=sys.stderr)

@@ -285,3 +285,25 @@ def test_zero_padding_invariant_on_gpu():
     C1, _, _, _ = run_gpu(case, A, B, None)
     C2, _, _, _ = run_gpu(case.with_(K=Kp), Ap, Bp, None)
     assert torch.equal(C1, C2)
+
+
+@pytest.mark.parametrize("shape", [(520, 392, 1000, 0, 1), (300, 264, 777, 0, 0), (1024, 1024, 1024, 0, 0),
+                                   (264, 136, 640, 1, 1)])
+def test_ring_depths_and_tilings_bit_identical(shape):
+    """The direct-load kernels with a 2-slot ring (256x256 tiles), 4-slot rings (128x128,
+    64x128) and the persistent schedule with whole tiles all form every output's fp32 sum
+    from the same MFMA 16x16x32 steps in ascending K: their results must be bit-identical
+    (a dropped, repeated or reordered K tile in any ring shows up here)."""
+    M, N, K, tA, tB = shape
+    case = W.GemmCase(f"ringsweep-{M}x{N}x{K}", M, N, K, transpose_A=tA, transpose_B=tB, relu=1, seed=4950)
+    A, B, _ = W.make_inputs(case)
+    variants = ["tile256dma", "tile128dma"] + ([] if tA else ["tile64dma"])
+    outs = {}
+    for v in variants:
+        C, plan, _, _ = run_gpu(case, A, B, None, variant=v)
+        outs[v] = C.view(torch.int16).cpu()
+        log(f"[case] {case.name} {plan.describe()}")
+    ref = outs[variants[0]]
+    for v in variants[1:]:
+        assert torch.equal(outs[v], ref), f"{v} differs from {variants[0]}"
+    assert_within_tolerance(out_values(C), oracle_full(case, A, B, None), case, "ring sweep")
