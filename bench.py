@@ -258,7 +258,7 @@ def device_facts(sampler: ClockSampler):
 
 
 # ---------------------------------------------------------------------------- timing
-def timed_launches(launch, stream, steps, warmup, sampler=None, clock=True):
+def timed_launches(launch, stream, steps, warmup, sampler=None, sample_clock=True):
     """The one timing rule (see the module docstring).  launch(i) enqueues launch i and
     returns its status.
 
@@ -307,7 +307,7 @@ def timed_launches(launch, stream, steps, warmup, sampler=None, clock=True):
     torch.cuda.synchronize()
     # clock window
     clock = None
-    if clock and sampler is not None and sampler.error is None and CLOCK_MS > 0:
+    if sample_clock and sampler is not None and sampler.error is None and CLOCK_MS > 0:
         n = int(math.ceil(CLOCK_MS / per))
         c0 = time.perf_counter()
         for i in range(n):
@@ -367,7 +367,7 @@ def measure(case, steps, warmup, sampler=None, log=None, variant="auto"):
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
     r = timed_launches(lambda i: plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh), stream, steps,
-                       warmup, sampler, clock=case.name in CLOCK_WORKLOADS)
+                       warmup, sampler, sample_clock=case.name in CLOCK_WORKLOADS)
     r.update({"plan": plan, "describe": plan.describe(), "C": C, "nsets": nsets})
     return r
 
@@ -396,7 +396,7 @@ def measure_mx(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
     r.update({"plan": plan, "describe": plan.describe(), "C": C, "nsets": nsets})
     return r
 
@@ -425,7 +425,7 @@ def measure_attn(case, steps, warmup, sampler=None, log=None):
     if log:
         log(f"[bench] {case.name}: attention B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} "
             f"sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
     r.update({"C": O, "nsets": nsets,
               "describe": f"attn_fwd block=128x64 threads=256 dim={case.D} causal={case.causal} dtype={case.dtype}"})
     return r
@@ -453,7 +453,7 @@ def measure_w4(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: w4 M={case.M} N={case.N} K={case.K} G={case.G} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
     r.update({"C": C, "nsets": nsets,
               "describe": f"gemm_w4 block=16x64x512 threads={kernel_constant('kW4Threads')} group={case.G} "
                           f"{case.ab}->{case.c}"})
@@ -482,7 +482,7 @@ def measure_sp(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: sp M={case.M} N={case.N} K={case.K} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
     r.update({"C": C, "nsets": nsets, "describe": f"gemm_sp block=256x256x64 threads=512 {case.ab}->{case.c}"})
     return r
 
