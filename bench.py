@@ -55,7 +55,8 @@ CLOCK_WORKLOADS = ("c5a", "c3", "c5b")
 WARM_RULE = (f"W untimed launches, then more until >= {WARM_MS:.0f} ms of GPU time, then K timed launches "
              "between two HIP events on the launch stream (the mean); then K launches each between its own "
              f"event pair (min/median/p90); then {CLOCK_MS:.0f} ms more launches while the clock is sampled "
-             f"(workloads {', '.join(CLOCK_WORKLOADS)})")
+             f"(workloads {', '.join(CLOCK_WORKLOADS)}); secondary workloads time max(K/2, 10) launches or "
+             "at least 20 ms of them")
 # Sources of each kernel family, keyed by the plan's variant number (tlg.h).
 KERNEL_SOURCES = {
     1: ["gemm_tile.hpp", "tlg_device.hpp"],
@@ -258,7 +259,7 @@ def device_facts(sampler: ClockSampler):
 
 
 # ---------------------------------------------------------------------------- timing
-def timed_launches(launch, stream, steps, warmup, sampler=None, sample_clock=True):
+def timed_launches(launch, stream, steps, warmup, sampler=None, sample_clock=True, min_timed_ms=0.0):
     """The one timing rule (see the module docstring).  launch(i) enqueues launch i and
     returns its status.
 
@@ -288,6 +289,8 @@ def timed_launches(launch, stream, steps, warmup, sampler=None, sample_clock=Tru
     per = max(w0.elapsed_time(w1) / 20, 1e-3)
     for i in range(int(math.ceil(max(0.0, warm_ms - 20 * per) / per))):
         status |= launch(i)
+    if min_timed_ms > 0:      # secondary workloads: at least this much timed GPU work
+        steps = max(steps, int(math.ceil(min_timed_ms / per)))
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -327,7 +330,7 @@ def timed_launches(launch, stream, steps, warmup, sampler=None, sample_clock=Tru
         return each[min(len(each) - 1, int(f * (len(each) - 1) + 0.5))]
 
     mean = start.elapsed_time(end) / steps
-    r = {"ms": mean, "wall_s": t1 - t0,
+    r = {"ms": mean, "wall_s": t1 - t0, "steps": steps,
          "per_launch_ms": {"mean": mean, "min": each[0], "median": q(0.5), "p90": q(0.9), "max": each[-1]}}
     if sampler is not None:
         r["clock"] = clock if clock is not None else {"sclk_mhz": None, "error": sampler.error,
@@ -344,7 +347,7 @@ def plan_out_dtype(case):
     return {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[case.c]
 
 
-def measure(case, steps, warmup, sampler=None, log=None, variant="auto"):
+def measure(case, steps, warmup, sampler=None, log=None, variant="auto", min_timed_ms=0.0):
     """Time the 16-bit GEMM of `case` through a plan (tlg_gemm_create / tlg_gemm_run)."""
     import torch
     import tiled_dense_gemm_02_amd as tlg
@@ -367,12 +370,13 @@ def measure(case, steps, warmup, sampler=None, log=None, variant="auto"):
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
     r = timed_launches(lambda i: plan.run_ptrs(ptrs[i % nsets][0], ptrs[i % nsets][1], c_ptr, sh), stream, steps,
-                       warmup, sampler, sample_clock=case.name in CLOCK_WORKLOADS)
+                       warmup, sampler, sample_clock=case.name in CLOCK_WORKLOADS,
+                       min_timed_ms=min_timed_ms)
     r.update({"plan": plan, "describe": plan.describe(), "C": C, "nsets": nsets})
     return r
 
 
-def measure_mx(case, steps, warmup, sampler=None, log=None):
+def measure_mx(case, steps, warmup, sampler=None, log=None, min_timed_ms=0.0):
     """Time a block-scaled workload (tlg_gemm_run_mx)."""
     import torch
     import tiled_dense_gemm_02_amd as tlg
@@ -396,12 +400,12 @@ def measure_mx(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: {plan.describe()} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False, min_timed_ms=min_timed_ms)
     r.update({"plan": plan, "describe": plan.describe(), "C": C, "nsets": nsets})
     return r
 
 
-def measure_attn(case, steps, warmup, sampler=None, log=None):
+def measure_attn(case, steps, warmup, sampler=None, log=None, min_timed_ms=0.0):
     """Time an attention-forward workload (tlg_attn_fwd)."""
     import torch
     import tiled_dense_gemm_02_amd as tlg
@@ -425,13 +429,13 @@ def measure_attn(case, steps, warmup, sampler=None, log=None):
     if log:
         log(f"[bench] {case.name}: attention B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} "
             f"sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False, min_timed_ms=min_timed_ms)
     r.update({"C": O, "nsets": nsets,
               "describe": f"attn_fwd block=128x64 threads=256 dim={case.D} causal={case.causal} dtype={case.dtype}"})
     return r
 
 
-def measure_w4(case, steps, warmup, sampler=None, log=None):
+def measure_w4(case, steps, warmup, sampler=None, log=None, min_timed_ms=0.0):
     """Time a 4-bit dequant GEMM workload (tlg_gemm_w4)."""
     import torch
     import tiled_dense_gemm_02_amd as tlg
@@ -453,14 +457,14 @@ def measure_w4(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: w4 M={case.M} N={case.N} K={case.K} G={case.G} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False, min_timed_ms=min_timed_ms)
     r.update({"C": C, "nsets": nsets,
               "describe": f"gemm_w4 block=16x64x512 threads={kernel_constant('kW4Threads')} group={case.G} "
                           f"{case.ab}->{case.c}"})
     return r
 
 
-def measure_sp(case, steps, warmup, sampler=None, log=None):
+def measure_sp(case, steps, warmup, sampler=None, log=None, min_timed_ms=0.0):
     """Time a 2:4 structured-sparse GEMM workload (tlg_gemm_sp)."""
     import torch
     import tiled_dense_gemm_02_amd as tlg
@@ -482,7 +486,7 @@ def measure_sp(case, steps, warmup, sampler=None, log=None):
 
     if log:
         log(f"[bench] {case.name}: sp M={case.M} N={case.N} K={case.K} sets={nsets}")
-    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False)
+    r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False, min_timed_ms=min_timed_ms)
     r.update({"C": C, "nsets": nsets, "describe": f"gemm_sp block=256x256x64 threads=512 {case.ab}->{case.c}"})
     return r
 
@@ -708,37 +712,41 @@ def sp_line(args, case, sampler, dev, log):
     return out
 
 
+SECONDARY_MIN_MS = 20.0   # timed GPU work per secondary workload, at least
+
+
 def secondary_entry(name, args, sampler, dev, log):
     import tlg_workloads as W
-    steps = max(10, args.steps // 2)
+    steps, mt = max(10, args.steps // 2), SECONDARY_MIN_MS
     if name in W.MX_CONFIGS:
         c = W.MX_CONFIGS[name]
-        rr, dt = measure_mx(c, steps, args.warmup, sampler, log), c.fmt
+        rr, dt = measure_mx(c, steps, args.warmup, sampler, log, min_timed_ms=mt), c.fmt
     elif name in W.ATTN_CONFIGS:
         c = W.ATTN_CONFIGS[name]
-        rr, dt = measure_attn(c, steps, args.warmup, sampler, log), c.dtype
+        rr, dt = measure_attn(c, steps, args.warmup, sampler, log, min_timed_ms=mt), c.dtype
     elif name in W.W4_CONFIGS:
         c = W.W4_CONFIGS[name]
-        rr, dt = measure_w4(c, steps, args.warmup, sampler, log), c.ab
+        rr, dt = measure_w4(c, steps, args.warmup, sampler, log, min_timed_ms=mt), c.ab
     elif name in W.SP_CONFIGS:
         c = W.SP_CONFIGS[name]
-        rr, dt = measure_sp(c, steps, args.warmup, sampler, log), c.ab
+        rr, dt = measure_sp(c, steps, args.warmup, sampler, log, min_timed_ms=mt), c.ab
     else:
         c = W.CONFIGS[name]
-        rr, dt = measure(c, steps, args.warmup, sampler, log), c.ab
+        rr, dt = measure(c, steps, args.warmup, sampler, log, min_timed_ms=mt), c.ab
     t = rr["ms"] * 1e-3
     tflops = c.flops / t / 1e12
     gbs = c.algorithmic_bytes / t / 1e9
-    entry = {"workload": name, "ms": rr["ms"], "TFLOP/s": tflops, "GB/s": gbs, "plan": rr["describe"],
+    entry = {"workload": name, "ms": rr["ms"], "timed_launches": rr["steps"], "TFLOP/s": tflops, "GB/s": gbs,
+             "plan": rr["describe"],
              "mfma_frac": tflops / PEAK_TFLOPS[dt], "hbm_frac": gbs / PEAK_HBM_GBS}
     entry.update(clock_fields(rr, dev, dt, tflops))
     return entry
 
 
-SECONDARY = ("c3", "c5b", "c2", "c4", "c1", "mx3", "fa3", "w4a", "sp3")
+SECONDARY = ("c3", "c5b", "c2", "c4", "c1", "mx3", "mx6", "fa3", "w4a", "sp3")
 # Oracle sample sizes: about 10 s of the oracle on 16 host threads.
 CPU_ROWS = {"c5a": 4096, "c3": 4096, "c2": 1024, "c1": 256, "c4": 1000, "c5b": 16, "mx1": 256, "mx2": 1000,
-            "mx3": 2048}
+            "mx3": 2048, "mx4": 256, "mx5": 1000, "mx6": 2048}
 
 
 def parse():
