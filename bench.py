@@ -321,7 +321,8 @@ def timed_launches(launch, stream, steps, warmup, sampler=None, sample_clock=Tru
         c1 = time.perf_counter()
         clock = sampler.window(c0, c1)
         clock["window_ms"] = (c1 - c0) * 1e3
-        clock["timed_run"] = sampler.window(t0, t1)
+        # The timed run itself is not sampled: it is shorter than the ~1 s refresh of the
+        # driver's metrics, so a reading taken during it describes the time before it.
     if status != 0:
         raise RuntimeError(f"a launch failed during the timed run (status {status})")
     each = sorted(a.elapsed_time(b) for a, b in evs)
