@@ -306,6 +306,7 @@ gemm_lds_kernel(GemmParams p)
     constexpr int D = D0 < L ? D0 : L;
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
     static_assert(KS == 2, "fragment buffering assumes two K steps per tile");
+    static_assert(FM >= 2, "B fragments of the next K step are read at MFMAs jj * FM + 1 of a step");
     static_assert(SPLIT >= 1 && SPLIT < MPS, "barrier inside the last K step");
     static_assert(L - D == 0 || (L - D - 1) * R < BPOS, "early loads precede the barrier");
     static_assert((S - 2) * L + D < 64, "vmcnt range");
@@ -706,15 +707,20 @@ inline hipError_t dispatch_lds128(const GemmParams& p, int tA, int tB, hipStream
 }
 
 // 64 x 128 tiles (grids of at most 128 tiles of 128 x 128: twice the workgroups
-// in one wave): 8 waves of 32 x 32, 4-slot ring, barrier after 2 of the last K
-// step's 4 MFMAs, one direct load per MFMA.  The LDS layout takes M/N-contiguous
-// rows of 128..512 elements only, so A must be K-contiguous (transpose_A == 0).
+// in one wave): 8 waves of 32 x 32, 4-slot ring, barrier after 1 of the last K
+// step's 4 MFMAs, one direct load per MFMA.  With only 8 MFMAs per wave and K
+// tile, the K loop of these small grids is bound by each step's barrier and LDS
+// round trip, not by the loads (a 5- or 6-slot ring is slower); three MFMAs after
+// the barrier hide the next tile's fragment reads better than two (measured on
+// MI355X: 1024^3 11.9 -> 10.7 us, 64 x 128 x 4096 34.6 -> 29.0 us).  The LDS
+// layout takes M/N-contiguous rows of 128..512 elements only, so A must be
+// K-contiguous (transpose_A == 0).
 template <int T>
 inline hipError_t dispatch_lds64(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
     if (tA) return hipErrorInvalidValue;
-    if (tB) return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, true, kModeDP>(p, s);
-    return launch_lds_inst<64, 128, 4, 2, 1, 2, 4, T, true, false, kModeDP>(p, s);
+    if (tB) return launch_lds_inst<64, 128, 4, 1, 1, 2, 4, T, true, true, kModeDP>(p, s);
+    return launch_lds_inst<64, 128, 4, 1, 1, 2, 4, T, true, false, kModeDP>(p, s);
 }
 
 // The same 128 x 128 kernel with K split over p.splits workgroups per tile.

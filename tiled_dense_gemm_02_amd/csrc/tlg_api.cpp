@@ -230,8 +230,8 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         // partial tiles costs ~5-10 us per launch (measured on MI355X), which a
         // split repays only from about 48 K tiles (K >= 3072) on.  Otherwise, at
         // most 128 tiles of 128x128 and A stored [M,K]: 64x128 tiles, twice the
-        // workgroups in one wave (measured on MI355X: 1024^3 12.9 -> 11.8 us,
-        // 1000x1500x777 bf16 12.7 -> 10.9 us; at 2048^3, 256 tiles of 128x128,
+        // workgroups in one wave (measured on MI355X: 1024^3 13.5 -> 10.6 us,
+        // 1000x1500x777 bf16 13.5 -> 10.8 us; at 2048^3, 256 tiles of 128x128,
         // they are 1.5x slower).
         //
         // Once 256x256 tiles fill the chip, the wave count decides between the two
