@@ -89,11 +89,11 @@ def test_variant_choice_and_geometry_for_the_workloads():
 
     # at most 128 tiles of 128x128 with A stored [M,K]: 64x128 tiles
     i = info(C["c1"])
-    assert (i.variant, i.block_m, i.block_n, i.grid, i.k_tiles, i.splits) == (10, 64, 128, 8, 4, 1)
-    # 1024^3: 64 tiles of 128x128 (too short a K to split) -> 128 tiles of 64x128, 16 K tiles each
+    assert (i.variant, i.block_m, i.block_n, i.grid, i.k_tiles, i.splits) == (10, 64, 128, 8, 2, 1)
+    # 1024^3: 64 tiles of 128x128 (too short a K to split) -> 128 tiles of 64x128, 8 K tiles of 128 each
     i = info(C["c2"])
-    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (10, 64, 128, 64, 128, 16)
-    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (4, 512, 4 * (64 + 128) * 64 * 2, 1, 0)
+    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (10, 64, 128, 128, 128, 8)
+    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (3, 512, 3 * (64 + 128) * 128 * 2, 1, 0)
     i = info(C["c2"], "tile128dma")
     assert (i.variant, i.block_m, i.grid, i.lds_bytes) == (7, 128, 64, 4 * 2 * 128 * 64 * 2)
     # A stored [K,M]: 64-row tiles of an M-contiguous operand do not exist
@@ -109,7 +109,7 @@ def test_variant_choice_and_geometry_for_the_workloads():
     i = info(C["c3"])
     assert (i.variant, i.block_m, i.grid, i.k_tiles, i.lds_bytes, i.threads) == (6, 256, 256, 64, 131072, 512)
     i = info(C["c4"])
-    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (10, 8, 8, 16 * 12, 13, 1)
+    assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (10, 8, 8, 16 * 12, 7, 1)
     # forced split of 1000x1500x777: 8 x 12 = 96 tiles, 13 K tiles -> 2 ranges (7 + 6 K tiles)
     i = info(C["c4"], "tile128dma_sk")
     assert (i.variant, i.vec_a, i.vec_b, i.grid, i.k_tiles, i.splits) == (8, 8, 8, 8 * 12 * 2, 7, 2)

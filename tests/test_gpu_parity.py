@@ -53,6 +53,8 @@ def test_config1_relu_256():
 
 def test_config2_1024():
     plan = _full_check(W.CONFIGS["c2"])
+    assert plan.info.block_k == 128 and plan.info.k_tiles == 8     # 64x128 tiles take K in tiles of 128
+    plan = _full_check(W.CONFIGS["c2"], variant="tile128dma")
     assert plan.info.k_tiles == 16          # 1024 / 64, the pages' K trip count
     plan = _full_check(W.CONFIGS["c2"], variant="tile128dma_sk")
     assert plan.info.splits == 4 and plan.info.k_tiles == 4   # K split in 4 ranges of 4 K tiles
@@ -290,10 +292,11 @@ def test_zero_padding_invariant_on_gpu():
 @pytest.mark.parametrize("shape", [(520, 392, 1000, 0, 1), (300, 264, 777, 0, 0), (1024, 1024, 1024, 0, 0),
                                    (264, 136, 640, 1, 1)])
 def test_ring_depths_and_tilings_bit_identical(shape):
-    """The direct-load kernels with a 2-slot ring (256x256 tiles), 4-slot rings (128x128,
-    64x128) and the persistent schedule with whole tiles all form every output's fp32 sum
-    from the same MFMA 16x16x32 steps in ascending K: their results must be bit-identical
-    (a dropped, repeated or reordered K tile in any ring shows up here)."""
+    """The direct-load kernels with a 2-slot ring of 64-wide K tiles (256x256 tiles), a
+    4-slot ring of 64-wide K tiles (128x128), a 3-slot ring of 128-wide K tiles (64x128)
+    and the persistent schedule with whole tiles all form every output's fp32 sum from
+    the same MFMA 16x16x32 steps in ascending K: their results must be bit-identical (a
+    dropped, repeated or reordered K tile in any ring shows up here)."""
     M, N, K, tA, tB = shape
     case = W.GemmCase(f"ringsweep-{M}x{N}x{K}", M, N, K, transpose_A=tA, transpose_B=tB, relu=1, seed=4950)
     A, B, _ = W.make_inputs(case)

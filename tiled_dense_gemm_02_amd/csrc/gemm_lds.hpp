@@ -286,11 +286,11 @@ struct LdsOperand {
 enum : int { kModeDP = 0, kModeSplitK = 1, kModeStreamK = 2 };
 
 template <int BM, int BN, int S, int SPLIT, int R, int WAVES_M, int WAVES_N, int T_IN, bool A_KC, bool B_KC,
-          int MODE = kModeDP>
+          int MODE = kModeDP, int BK = 64>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 gemm_lds_kernel(GemmParams p)
 {
-    constexpr int BK = 64, NW = WAVES_M * WAVES_N;
+    constexpr int NW = WAVES_M * WAVES_N;
     constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N, FM = WTM / 16, FN = WTN / 16;
     using OpA = LdsOperand<BM, BK, A_KC, NW>;
     using OpB = LdsOperand<BN, BK, B_KC, NW>;
@@ -305,7 +305,7 @@ gemm_lds_kernel(GemmParams p)
     constexpr int D0 = (MI - 1 - BPOS) / R + 1;
     constexpr int D = D0 < L ? D0 : L;
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
-    static_assert(KS == 2, "fragment buffering assumes two K steps per tile");
+    static_assert(KS == 2 || (KS == 4 && MODE == kModeDP), "K tiles of 64, or of 128 without a split K");
     static_assert(FM >= 2, "B fragments of the next K step are read at MFMAs jj * FM + 1 of a step");
     static_assert(SPLIT >= 1 && SPLIT < MPS, "barrier inside the last K step");
     static_assert(L - D == 0 || (L - D - 1) * R < BPOS, "early loads precede the barrier");
@@ -668,7 +668,7 @@ gemm_lds_kernel(GemmParams p)
     }
 }
 
-template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC, int MODE>
+template <int BM, int BN, int S, int SPLIT, int R, int WM, int WN, int T, bool AKC, bool BKC, int MODE, int BK = 64>
 inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
@@ -676,7 +676,7 @@ inline hipError_t launch_lds_inst(const GemmParams& p, hipStream_t stream)
     const dim3 grid((unsigned)(MODE == kModeStreamK ? p.persistent_grid
                                                     : p.tiles_m * p.tiles_n * (MODE == kModeSplitK ? p.splits : 1)));
     const dim3 block(64 * WM * WN);
-    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC, MODE>, grid,
+    return hipLaunchKernel((const void*)&gemm_lds_kernel<BM, BN, S, SPLIT, R, WM, WN, T, AKC, BKC, MODE, BK>, grid,
                            block, kargs, 0, stream);
 }
 
@@ -707,20 +707,21 @@ inline hipError_t dispatch_lds128(const GemmParams& p, int tA, int tB, hipStream
 }
 
 // 64 x 128 tiles (grids of at most 128 tiles of 128 x 128: twice the workgroups
-// in one wave): 8 waves of 32 x 32, 4-slot ring, barrier after 1 of the last K
-// step's 4 MFMAs, one direct load per MFMA.  With only 8 MFMAs per wave and K
-// tile, the K loop of these small grids is bound by each step's barrier and LDS
-// round trip, not by the loads (a 5- or 6-slot ring is slower); three MFMAs after
-// the barrier hide the next tile's fragment reads better than two (measured on
-// MI355X: 1024^3 11.9 -> 10.7 us, 64 x 128 x 4096 34.6 -> 29.0 us).  The LDS
-// layout takes M/N-contiguous rows of 128..512 elements only, so A must be
-// K-contiguous (transpose_A == 0).
+// in one wave): 8 waves of 32 x 32, K tiles of 128 in a 3-slot ring (144 KiB),
+// barrier after 1 of the last K step's 4 MFMAs, one direct load every 2 MFMAs.
+// These small grids are bound by each K step's barrier and LDS round trip, not by
+// the loads: with K tiles of 64 a wave has only 8 MFMAs per barrier (deeper rings
+// of 5 or 6 slots are slower).  K tiles of 128 halve the barriers, and three
+// MFMAs after the barrier hide the next tile's fragment reads better than two
+// (measured on MI355X: 1024^3 11.9 -> 10.0 us, 64 x 128 x 4096 34.6 -> 25.3 us).
+// The LDS layout takes M/N-contiguous rows of 128..512 elements only, so A must
+// be K-contiguous (transpose_A == 0).
 template <int T>
 inline hipError_t dispatch_lds64(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
     if (tA) return hipErrorInvalidValue;
-    if (tB) return launch_lds_inst<64, 128, 4, 1, 1, 2, 4, T, true, true, kModeDP>(p, s);
-    return launch_lds_inst<64, 128, 4, 1, 1, 2, 4, T, true, false, kModeDP>(p, s);
+    if (tB) return launch_lds_inst<64, 128, 3, 1, 2, 2, 4, T, true, true, kModeDP, 128>(p, s);
+    return launch_lds_inst<64, 128, 3, 1, 2, 2, 4, T, true, false, kModeDP, 128>(p, s);
 }
 
 // The same 128 x 128 kernel with K split over p.splits workgroups per tile.

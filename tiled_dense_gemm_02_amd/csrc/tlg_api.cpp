@@ -230,7 +230,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         // partial tiles costs ~5-10 us per launch (measured on MI355X), which a
         // split repays only from about 48 K tiles (K >= 3072) on.  Otherwise, at
         // most 128 tiles of 128x128 and A stored [M,K]: 64x128 tiles, twice the
-        // workgroups in one wave (measured on MI355X: 1024^3 13.5 -> 10.6 us,
+        // workgroups in one wave (measured on MI355X: 1024^3 13.5 -> 10.0 us,
         // 1000x1500x777 bf16 13.5 -> 10.8 us; at 2048^3, 256 tiles of 128x128,
         // they are 1.5x slower).
         //
@@ -347,12 +347,12 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
             p->ws_bytes = p->ws_partials_bytes + (size_t)((p->sk_tiles * sizeof(unsigned) + 255) / 256 * 256);
         }
     } else if (variant == TLG_VARIANT_TILE_64_DMA) {
-        in.block_m = kLds64BM; in.block_n = kLds64BN; in.block_k = kLdsBK;
+        in.block_m = kLds64BM; in.block_n = kLds64BN; in.block_k = kLds64BK;
         in.stages = kLds64Stages;
         in.threads = kLdsThreads;
         in.grid = ceil_div(M, kLds64BM) * ceil_div(N, kLds64BN);
-        in.lds_bytes = (int64_t)kLds64Stages * (kLds64BM + kLds64BN) * kLdsBK * 2;
-        in.k_tiles = (int32_t)ceil_div(K, kLdsBK);
+        in.lds_bytes = (int64_t)kLds64Stages * (kLds64BM + kLds64BN) * kLds64BK * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kLds64BK);
     } else if (variant == TLG_VARIANT_SKINNY) {
         in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
         in.stages = kSkinnyStages;

@@ -96,7 +96,7 @@ hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
 // fill the chip with 256x256 tiles.
 constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64, kLdsStages = 2, kLdsThreads = 512;
 constexpr int kLds128BM = 128, kLds128BN = 128, kLds128Stages = 4;
-constexpr int kLds64BM = 64, kLds64BN = 128, kLds64Stages = 4;
+constexpr int kLds64BM = 64, kLds64BN = 128, kLds64BK = 128, kLds64Stages = 3;
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
