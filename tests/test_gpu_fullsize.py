@@ -95,6 +95,18 @@ def test_small_integers_exact_full_size(n, ab, c, relu):
     assert plan.info.k_tiles == n // 64
 
 
+# ------------------------------------------------------------ the skinny kernel's rotated K order
+@pytest.mark.parametrize("M,N,K", [(16, 16384, 8192), (16, 16384, 4096), (13, 4000, 8200)])
+def test_skinny_small_integers_exact_full_size(M, N, K):
+    """The skinny kernel's workgroups stream their K stages in rotated orders (each
+    starts at its own stage and wraps around): on small integers every output is the
+    exact sum, so a stage read twice or skipped in any rotation fails.  16 x 16384 x
+    8192 is the decode workload; 8200 leaves a last stage of 8 elements."""
+    case = W.GemmCase(f"skinny-int-{M}x{N}x{K}", M, N, K, c="f32", transpose_B=1, dist="smallint",
+                      relu=M % 2, seed=4300 + K)
+    _check_full(case, exact=True, guard=1024, want_variant=3)
+
+
 # ------------------------------------------------------------ large ragged shapes, full output
 def test_large_ragged_xcd_remap_partial_band():
     """With 256 x 256 tiles: 288 tiles (a multiple of 8: XCD remap on), 18 tile rows (four

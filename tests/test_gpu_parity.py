@@ -190,6 +190,8 @@ def test_empty_k_and_empty_output():
     _full_check(case)
     case = W.GemmCase("k0relu", 70, 90, 0, c="f16", relu=1, seed=6)
     _full_check(case)
+    case = W.GemmCase("k0skinny", 16, 96, 0, c="f32", transpose_B=1, clear_accum=0, relu=1, seed=7)
+    assert _full_check(case).info.variant == 3
     import tiled_dense_gemm_02_amd as tlg
     plan = tlg.Gemm(0, 5, 7)
     assert plan.info.variant == 4

@@ -20,9 +20,10 @@
 // as zero through the buffer resource's range check ("core primitives"
 // chapter, section 4.2).
 //
-// Measured on MI355X for 16 x 16384 x 8192 fp16: ~5.0 TB/s; the previous
-// design that loaded MFMA operands straight from HBM into registers (16 rows
-// x 64 bytes per load instruction) reached ~4.8 TB/s with 8 waves.
+// Measured on MI355X for 16 x 16384 x 8192 fp16: ~6.1 TB/s with the K stage
+// order rotated per workgroup (below), ~5.0 TB/s without; the previous design
+// that loaded MFMA operands straight from HBM into registers (16 rows x 64
+// bytes per load instruction) reached ~4.8 TB/s with 8 waves.
 
 #include "gemm_lds.hpp"
 
@@ -64,12 +65,23 @@ gemm_skinny_kernel(GemmParams p)
     const uint64_t b_bytes = (uint64_t)(p.N - n0) * ld;
     const uint64_t a_bytes = (uint64_t)(p.M - m0) * ld;
 
+    // The workgroups that one XCD holds at a time (dispatch sends workgroup b to XCD
+    // b % 8) start at different K stages and wrap around: in step j a workgroup
+    // streams stage (j + rot) mod NST.  When every workgroup reads the same K range
+    // of its rows at once, a row pitch of a power of two (K = 4096, 8192, 16384)
+    // puts those reads on few HBM channels (measured on MI355X, 16 x 16384 x 8192:
+    // 5.0 TB/s in step, 6.1 TB/s rotated, as fast as with K = 8320).  Each output
+    // still sums every stage once, in an order fixed by its workgroup.
+    const int rot = NST > 0 ? (int)((blockIdx.x / 8u) % (unsigned)NST) : 0;
+    auto stage_of = [&](int j) { const int x = j + rot; return x >= NST ? x - NST : x; };
+
     // Load i of this wave fills LDS rows q*LPI .. q*LPI + LPI - 1 of the stage
     // (q = i * WAVES + wave); lane -> row q*LPI + lane / CHUNKS, position lane % CHUNKS.
-    auto issue = [&](int st) {
-        const int k0 = st * KST;
+    // Step j of the loop fills ring slot j % S with K stage stage_of(j).
+    auto issue = [&](int j) {
+        const int k0 = stage_of(j) * KST;
         const uint64_t o = (uint64_t)k0 * 2u;
-        const uint32_t slot = lds0 + (uint32_t)((st % S) * STAGE);
+        const uint32_t slot = lds0 + (uint32_t)((j % S) * STAGE);
         const i32x4 rb = rsrc_words(b_base + o, b_bytes > o ? b_bytes - o : 0);
         const i32x4 ra = rsrc_words(a_base + o, a_bytes > o ? a_bytes - o : 0);
 #pragma unroll
