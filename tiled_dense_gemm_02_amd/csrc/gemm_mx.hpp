@@ -286,32 +286,8 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
     // iterations load zero-filled tiles past K into free slots).
     wait_vmcnt<0>();
 
-    const bool vec_cols = p.c_vec != 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + arow + i * 16 + (lane & 15);
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int jj = 0; jj < FN; ++jj) {
-            const int n = n0 + bcol + jj * 16 + 4 * (lane >> 4);
-            if (n >= p.N) continue;
-            const int count = min(4, p.N - n);
-            const bool vec_ok = vec_cols && count == 4;
-            const int64_t idx = (int64_t)m * p.N + n;
-            float v[4] = {acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
-            if (!p.clear_accum) {
-                float c[4] = {0.f, 0.f, 0.f, 0.f};
-                load_c4(p.C, p.c_dtype, idx, vec_ok, c, count);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = c[e] + v[e];
-            }
-            if (p.relu) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = relu(v[e]);
-            }
-            store_c4(p.C, p.c_dtype, idx, vec_ok, v, count);
-        }
-    }
+    store_blocks<FM, FN>(p.C, p.M, p.N, p.c_dtype, p.c_vec != 0, p.c_vec8 != 0, p.relu != 0, p.clear_accum != 0, acc,
+                         m0 + arow, n0 + bcol, lane);
 }
 
 }  // namespace tlg

@@ -219,25 +219,8 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
     }
     wait_vmcnt<0>();
 
-    const bool vec_cols = p.c_vec != 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + arow + i * 16 + r16;
-        if (m >= p.M) continue;
-#pragma unroll
-        for (int jj = 0; jj < FN; ++jj) {
-            const int n = n0 + bcol + jj * 16 + 4 * g;
-            if (n >= p.N) continue;
-            const int count = min(4, p.N - n);
-            const bool vec_ok = vec_cols && count == 4;
-            float v[4] = {acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
-            if (p.relu) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = relu(v[e]);
-            }
-            store_c4(p.C, p.c_dtype, (int64_t)m * p.N + n, vec_ok, v, count);
-        }
-    }
+    store_blocks<FM, FN>(p.C, p.M, p.N, p.c_dtype, p.c_vec != 0, p.c_vec8 != 0, p.relu != 0, true, acc, m0 + arow,
+                         n0 + bcol, lane);
 }
 
 hipError_t launch_sp(const SpParams& p, int ab_dtype, hipStream_t stream)

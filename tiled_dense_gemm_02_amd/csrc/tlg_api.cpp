@@ -485,6 +485,7 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
     gp.clear_accum = p.clear;
     gp.c_dtype = p.c;
     gp.c_vec = (p.N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    gp.c_vec8 = (p.N % 8 == 0) && (c % 16u == 0);
 
     hipError_t err;
     if (p.variant == TLG_VARIANT_SKINNY) {
@@ -672,6 +673,7 @@ tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const
     mp.clear_accum = p.clear;
     mp.c_dtype = p.c;
     mp.c_vec = (p.N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    mp.c_vec8 = (p.N % 8 == 0) && (c % 16u == 0);
     mp.tiles_m = (int)ceil_div(p.M, 256);
     mp.tiles_n = (int)ceil_div(p.N, 256);
     const hipError_t err = launch_mx(mp, p.ab == TLG_E4M3 ? 0 : p.ab == TLG_E5M2 ? 1 : 4, (hipStream_t)stream);
@@ -769,6 +771,7 @@ tlg_status tlg_gemm_sp(const void* A, const void* Wv, const void* Wm, void* C, i
     sp.relu = epilogue == TLG_EPI_RELU;
     sp.c_dtype = c_dtype;
     sp.c_vec = (N % 4 == 0) && (c % (uintptr_t)(4 * cb) == 0);
+    sp.c_vec8 = (N % 8 == 0) && (c % 16u == 0);
     sp.tiles_m = (int)ceil_div(M, 256);
     sp.tiles_n = (int)ceil_div(N, 256);
     const hipError_t err = launch_sp(sp, ab_dtype == TLG_F16 ? DT_F16 : DT_BF16, (hipStream_t)stream);

@@ -147,4 +147,91 @@ __device__ inline void store_c4(void* C, int c_dtype, int64_t idx, bool vec_ok, 
     }
 }
 
+// Two adjacent 16 x 16 output blocks of an MFMA 16x16 result, written with one
+// 16-byte store per lane.  In the result layout lane l holds four consecutive
+// columns 4 (l / 16) .. +3 of row l % 16 in each block (p: the left block, q: the
+// right one), so a plain store writes 8 bytes per lane and 32-byte pieces of each
+// row.  gfx950's v_permlane16_swap exchanges the odd 16-lane rows of its first
+// operand with the even rows of its second; applied to (q, p) it leaves lanes
+// 0-15 with columns 0-7 of q, lanes 16-31 with columns 0-7 of p, lanes 32-47 with
+// columns 8-15 of q and lanes 48-63 with columns 8-15 of p.  Each lane then
+// stores 8 consecutive 16-bit outputs, and every row receives 64 contiguous
+// bytes from one instruction.  16-bit outputs written 8 bytes per lane reach
+// about half the bandwidth of fp32 outputs written 16 bytes per lane (measured
+// on MI355X: 8192^2 outputs with K = 0, 2.5-3.1 against 5.1-5.4 TB/s).
+// c16: the first of the pair's 32 columns in row m (16-byte aligned).  All four
+// lanes sharing a row must be active together.
+__device__ inline void store_pair16(uint16_t* c16, int c_dtype, int lane, const float* p, const float* q)
+{
+    uint32_t ph[4], qh[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        ph[e] = c_dtype == DT_F16 ? f32_to_f16_bits(p[e]) : f32_to_bf16_bits(p[e]);
+        qh[e] = c_dtype == DT_F16 ? f32_to_f16_bits(q[e]) : f32_to_bf16_bits(q[e]);
+    }
+    const u32x2 s01 = __builtin_amdgcn_permlane16_swap(qh[0] | (qh[1] << 16), ph[0] | (ph[1] << 16), false, false);
+    const u32x2 s23 = __builtin_amdgcn_permlane16_swap(qh[2] | (qh[3] << 16), ph[2] | (ph[3] << 16), false, false);
+    const int g = lane >> 4;
+    const int col = ((g & 1) ? 0 : 16) + (g >> 1) * 8;
+    *(u32x4*)(c16 + col) = u32x4{s01[0], s23[0], s01[1], s23[1]};
+}
+
+// Epilogue of a wave's FM x FN blocks of 16 x 16 outputs in the MFMA 16x16 result
+// layout: acc[i][j][e] is C[m][n + e] with m = m_base + 16 i + lane % 16 and
+// n = n_base + 16 j + 4 (lane / 16).  Adds C's prior value (clear_accum == 0),
+// applies ReLU on the fp32 sum, rounds to C's type and stores what lies inside
+// M x N.  16-bit outputs of a fresh sum go out through store_pair16 where a pair of
+// blocks lies wholly inside N (c_vec8: N % 8 == 0 and C 16-byte aligned).
+template <int FM, int FN>
+__device__ inline void store_blocks(void* C, int M, int N, int c_dtype, bool c_vec, bool c_vec8, bool relu_on,
+                                    bool clear_accum, const f32x4 (&acc)[FM][FN], int m_base, int n_base, int lane)
+{
+    const bool pairs = (FN % 2 == 0) && c_vec8 && clear_accum && c_dtype != DT_F32;
+    auto store_block = [&](int i, int jj, int m) {
+        const int n = n_base + jj * 16 + 4 * (lane >> 4);
+        if (n >= N) return;
+        const int count = min(4, N - n);
+        const bool vec_ok = c_vec && count == 4;
+        const int64_t idx = (int64_t)m * N + n;
+        float v[4] = {acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]};
+        if (!clear_accum) {
+            float c[4] = {0.f, 0.f, 0.f, 0.f};
+            load_c4(C, c_dtype, idx, vec_ok, c, count);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = c[e] + v[e];
+        }
+        if (relu_on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = relu(v[e]);
+        }
+        store_c4(C, c_dtype, idx, vec_ok, v, count);
+    };
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m_base + i * 16 + (lane & 15);
+        if (m >= M) continue;
+        if (pairs) {
+#pragma unroll
+            for (int jp = 0; jp < FN / 2; ++jp) {
+                const int nb = n_base + jp * 32;
+                if (nb + 32 <= N) {
+                    float v[4], w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[e] = relu_on ? relu(acc[i][2 * jp][e]) : acc[i][2 * jp][e];
+                        w[e] = relu_on ? relu(acc[i][2 * jp + 1][e]) : acc[i][2 * jp + 1][e];
+                    }
+                    store_pair16((uint16_t*)C + (int64_t)m * N + nb, c_dtype, lane, v, w);
+                } else {
+                    store_block(i, 2 * jp, m);
+                    store_block(i, 2 * jp + 1, m);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) store_block(i, jj, m);
+        }
+    }
+}
+
 }  // namespace tlg

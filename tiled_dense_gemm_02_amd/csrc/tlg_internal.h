@@ -19,6 +19,7 @@ struct GemmParams {
     int clear_accum;  // 0: add onto C's prior contents
     int c_dtype;      // DT_F16 / DT_BF16 / DT_F32
     int c_vec;        // 1: N % 4 == 0 and C aligned to 4 elements (vector stores allowed)
+    int c_vec8;       // 1: N % 8 == 0 and C aligned to 16 bytes (16-byte stores of 8 16-bit outputs)
     int tiles_m;      // output tiles along M (tile kernels) / row blocks (skinny)
     int tiles_n;      // output tiles along N
     // split-K plans only: K is cut into `splits` ranges of whole K tiles, one
@@ -122,6 +123,7 @@ struct MxParams {
     void* C;
     int M, N, K;
     int relu, clear_accum, c_dtype, c_vec;
+    int c_vec8;       // N % 8 == 0 and C aligned to 16 bytes
     int tiles_m, tiles_n;
 };
 hipError_t launch_mx(const MxParams& p, int fmt, hipStream_t stream);   // fmt: 0 = E4M3, 1 = E5M2, 4 = E2M1
@@ -167,6 +169,7 @@ struct SpParams {
     void* C;
     int M, N, K;
     int relu, c_dtype, c_vec;
+    int c_vec8;       // N % 8 == 0 and C aligned to 16 bytes
     int tiles_m, tiles_n;
 };
 hipError_t launch_sp(const SpParams& p, int ab_dtype, hipStream_t stream);
