@@ -363,19 +363,27 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
         __syncthreads();
     }
 
-    // Epilogue: O / l, rounded to the operand type; lane holds four consecutive dims.
+    // Epilogue: O / l, rounded to the operand type.  A lane holds four consecutive
+    // dims of each 16-dim block; pairs of blocks go out as one 16-byte store per
+    // lane (store_pair16: 64 contiguous bytes of each row per instruction).  O and
+    // its rows are 16-byte aligned (the entry point checks O; a row is 128 or 256
+    // bytes of a head).
+    static_assert(DT % 2 == 0, "pairs of 16-dim blocks");
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const int q = wq0 + rt * 16 + r16;
         const float inv = 1.0f / lacc[rt][0];
         if (q >= S) continue;
-        char* orow = (char*)p.O + head_off + (uint64_t)q * stride;
+        uint16_t* orow = (uint16_t*)((char*)p.O + head_off + (uint64_t)q * stride);
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            uint32_t hb[4];
+        for (int dp = 0; dp < DT / 2; ++dp) {
+            float v[4], w[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) round_op<T>(oacc[rt][dt][e] * inv, hb[e]);
-            *(u32x2*)(orow + (dt * 16 + 4 * g) * 2) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+            for (int e = 0; e < 4; ++e) {
+                v[e] = oacc[rt][2 * dp][e] * inv;
+                w[e] = oacc[rt][2 * dp + 1][e] * inv;
+            }
+            store_pair16(orow + dp * 32, T, lane, v, w);
         }
     }
 }
