@@ -667,11 +667,13 @@ inline hipError_t dispatch_lds_layout(const GemmParams& p, int tA, int tB, hipSt
 }
 
 // 256 x 256 tiles: 8 waves of 128 x 64, 2-slot ring, barrier after 8 of the last
-// K step's 32 MFMAs, one direct load every 2 MFMAs.
+// K step's 32 MFMAs, then the next tile's eight direct loads one every 3 MFMAs
+// (measured on MI355X against one every 2: 8192^3 -2%, 4096^3 -3%; every 1, 4 or 5
+// MFMAs and barriers after 2-24 MFMAs were slower).
 template <int T>
 inline hipError_t dispatch_lds(const GemmParams& p, int tA, int tB, hipStream_t s)
 {
-    return dispatch_lds_layout<256, 256, 2, 8, 2, 2, 4, T>(p, tA, tB, s);
+    return dispatch_lds_layout<256, 256, 2, 8, 3, 2, 4, T>(p, tA, tB, s);
 }
 
 // 128 x 128 tiles (grids too small for 256 x 256): 8 waves of 64 x 32, 4-slot ring,
