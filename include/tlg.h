@@ -135,11 +135,13 @@ typedef struct {
  * block-scaled request other than the one tlg_gemm_run_mx describes),
  * TLG_ERR_NOMEM if the plan cannot be allocated.  Plans with K split over
  * several workgroups per tile (tlg_plan_info.splits > 1, chosen for output grids
- * of fewer than 128 tiles of 128x128 with at least 48 K tiles of 64) allocate a
- * device workspace here (tlg_plan_info.workspace_bytes: fp32 partial tiles plus
- * one counter per tile), on the device current at the call, zero its counters
- * and wait for that to finish (TLG_ERR_HIP if any of it fails); other plans do
- * no device work.  On failure *out is set to NULL.
+ * of fewer than 128 tiles of 128x128 with at least 48 K tiles of 64, and for the
+ * skinny kernel when it has fewer than 256 blocks of 16 x 64 outputs and at least
+ * 8 K stages of 256) allocate a device workspace here
+ * (tlg_plan_info.workspace_bytes: fp32 partial tiles plus one counter per tile),
+ * on the device current at the call, zero its counters and wait for that to
+ * finish (TLG_ERR_HIP if any of it fails); other plans do no device work.  On
+ * failure *out is set to NULL.
  */
 tlg_status tlg_gemm_create(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
                            int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
@@ -203,8 +205,9 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, 
  * in a static device buffer of the library instead of a plan workspace: 16 MiB of
  * partial tiles plus 4 KiB of counters, one copy per GPU, held until the process
  * ends.  The automatic choice always fits (it splits only grids of fewer than 128
- * tiles of 128 x 128, into at most 256 partial tiles); a request that would need
- * more is refused with TLG_ERR_TOO_LARGE.  The first call on a device looks up
+ * tiles of 128 x 128, into at most 256 partial tiles, and skinny grids of fewer
+ * than 256 blocks, into at most 256 partial blocks of 4 KiB); a request that would
+ * need more is refused with TLG_ERR_TOO_LARGE.  The first call on a device looks up
  * the buffer's device address and enqueues a small kernel on `stream` that zeroes
  * the counters; every split-K launch returns the counters it uses to zero.
  *
@@ -257,7 +260,7 @@ tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void *A, const void *SA, const
 /* One timed candidate of tlg_gemm_tune. */
 typedef struct {
     int32_t variant;   /* tlg_variant */
-    int32_t splits;    /* K ranges per output tile (split-K variant), else 1 */
+    int32_t splits;    /* K ranges per output tile (split-K variant, split skinny plans), else 1 */
     float ms;          /* average time of one run, milliseconds */
 } tlg_tune_result;
 

@@ -53,6 +53,18 @@ def test_noalloc_split_k_twice_second_smaller():
     _pair(first)
 
 
+def test_noalloc_skinny_split_twice_second_smaller():
+    """The skinny kernel's K ranges keep their partial tiles and counters in the same
+    static scratch."""
+    first = W.GemmCase("noalloc-16x4096x8192", 16, 4096, 8192, transpose_B=1, seed=4303)
+    second = W.GemmCase("noalloc-9x2048x4096", 9, 2048, 4096, c="f32", transpose_B=1, relu=1, seed=4304)
+    p1 = _pair(first)
+    assert p1.info.variant == 3 and p1.info.splits == 4
+    p2 = _pair(second)
+    assert p2.info.variant == 3 and p2.info.splits > 1 and p2.info.workspace_bytes < p1.info.workspace_bytes
+    _pair(first)
+
+
 def test_noalloc_without_scratch():
     for case in (W.CONFIGS["c1"], W.CONFIGS["c4"], W.CONFIGS["c5b"].with_(N=2048, K=1024)):
         plan = _pair(case)

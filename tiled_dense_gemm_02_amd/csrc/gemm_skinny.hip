@@ -57,7 +57,14 @@ gemm_skinny_kernel(GemmParams p)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m0 = blockIdx.y * MR, n0 = blockIdx.x * NB;
     const int K = p.K;
-    const int NST = (K + KST - 1) / KST;
+    // K stages of the whole K, and this workgroup's range of them: with p.splits > 1
+    // (grids of few column blocks) workgroup z of the splits takes stages
+    // [z * per, z * per + NST), and the partial tiles are summed below.
+    const int NST_ALL = (K + KST - 1) / KST;
+    const int splits = p.splits > 1 ? p.splits : 1;
+    const int per = (NST_ALL + splits - 1) / splits;
+    const int st0 = (int)blockIdx.z * per;
+    const int NST = max(0, min(per, NST_ALL - st0));
     const uint32_t ld = (uint32_t)K * 2u;
     const uint32_t lds0 = lds_addr_of(smem);
     const char* b_base = (const char*)p.B + (uint64_t)n0 * ld;
@@ -72,8 +79,9 @@ gemm_skinny_kernel(GemmParams p)
     // puts those reads on few HBM channels (measured on MI355X, 16 x 16384 x 8192:
     // 5.0 TB/s in step, 6.1 TB/s rotated, as fast as with K = 8320).  Each output
     // still sums every stage once, in an order fixed by its workgroup.
-    const int rot = NST > 0 ? (int)((blockIdx.x / 8u) % (unsigned)NST) : 0;
-    auto stage_of = [&](int j) { const int x = j + rot; return x >= NST ? x - NST : x; };
+    const unsigned lid = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int rot = NST > 0 ? (int)((lid / 8u) % (unsigned)NST) : 0;
+    auto stage_of = [&](int j) { const int x = j + rot; return st0 + (x >= NST ? x - NST : x); };
 
     // Load i of this wave fills LDS rows q*LPI .. q*LPI + LPI - 1 of the stage
     // (q = i * WAVES + wave); lane -> row q*LPI + lane / CHUNKS, position lane % CHUNKS.
@@ -142,8 +150,10 @@ gemm_skinny_kernel(GemmParams p)
 
     const int m = m0 + (lane & 15);
     const bool vec_cols = p.c_vec != 0;
-    for (int j = wave; j < NS; j += WAVES) {
-        float v[4];
+    static_assert(NS <= WAVES, "one wave per 16-column block in the epilogue");
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (wave < NS) {
+        const int j = wave;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float s = red[(j * 4 + e) * 64 + lane];
@@ -151,8 +161,46 @@ gemm_skinny_kernel(GemmParams p)
             for (int w = 1; w < WAVES; ++w) s += red[((w * NS + j) * 4 + e) * 64 + lane];
             v[e] = s;
         }
-        const int n = n0 + j * 16 + 4 * (lane >> 4);
-        if (m >= p.M || n >= p.N) continue;
+    }
+    if (splits > 1) {
+        // Publish this K range's 16 x NB partial tile (fp32), take a ticket; the last
+        // workgroup of the tile sums the partials in K-range order, then runs the
+        // epilogue.  The XCDs' L2 caches are separate, so partials are written and
+        // read with device-scope (sc1) buffer accesses; each wave waits for its
+        // stores before the barrier that precedes the ticket.
+        __shared__ unsigned ticket;
+        const int tile = (int)(blockIdx.y * gridDim.x + blockIdx.x);
+        constexpr int PART = NS * 64 * 4;                 // floats per partial tile
+        const __amdgpu_buffer_rsrc_t wsr = make_rsrc(p.ws + (size_t)tile * splits * PART,
+                                                     (uint64_t)splits * PART * 4u);
+        if (wave < NS)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), wsr,
+                                                   (uint32_t)((blockIdx.z * PART + (wave * 64 + lane) * 4) * 4), 0,
+                                                   kCoherentDevice);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            ticket = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(ticket) != (unsigned)(splits - 1)) return;
+        if (wave < NS) {
+            constexpr int MAXS = kSkinnyMaxSplits;
+            u32x4 part[MAXS];
+#pragma unroll
+            for (int z = 0; z < MAXS; ++z)
+                part[z] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wsr, z < splits ? (uint32_t)((z * PART + (wave * 64 + lane) * 4) * 4) : kOOB, 0, kCoherentDevice);
+            f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int z = 0; z < MAXS; ++z) t += __builtin_bit_cast(f32x4, part[z]);   // zeros past the last range
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = t[e];
+        }
+        if (threadIdx.x == 0)   // ready for the next launch
+            __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const int n = n0 + wave * 16 + 4 * (lane >> 4);
+    if (wave < NS && m < p.M && n < p.N) {
         const int count = min(4, p.N - n);
         const bool vec_ok = vec_cols && count == 4;
         const int64_t idx = (int64_t)m * p.N + n;
@@ -175,7 +223,7 @@ static hipError_t launch_skinny_t(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
-    const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m);
+    const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)(p.splits > 1 ? p.splits : 1));
     const dim3 block(kSkinnyThreads);
     return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, kSkinnyNB, kSkinnyKST, kSkinnyStages>, grid,
                            block, kargs, 0, stream);

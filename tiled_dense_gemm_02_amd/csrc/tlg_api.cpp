@@ -29,8 +29,9 @@ struct tlg_gemm_s {
     int variant;
     int vec_a, vec_b;
     int align_a, align_b;  // byte alignment run() requires of A and B
-    // split-K plans: workspace = [tiles][splits][128*128] fp32 partials, then one
-    // counter per tile (zero between launches); allocated on `device` at create
+    // split-K plans: workspace = [tiles][splits][128*128] (skinny: [16*64]) fp32
+    // partials, then one counter per tile (zero between launches); allocated on
+    // `device` at create
     int splits = 1;
     void* ws = nullptr;
     size_t ws_partials_bytes = 0, ws_bytes = 0;
@@ -108,6 +109,21 @@ int choose_splits(int64_t tiles, int64_t ktiles)
     int64_t s = std::min<int64_t>(8, std::max<int64_t>(1, 256 / std::max<int64_t>(tiles, 1)));
     s = std::min<int64_t>(s, std::max<int64_t>(1, ktiles / 2));
     while (s > 1 && (s - 1) * ((ktiles + s - 1) / s) >= ktiles) --s;
+    return (int)s;
+}
+
+// K ranges of the skinny kernel for `tiles` blocks of 16 x 64 outputs and `nst`
+// 256-wide K stages.  A block streams its 64 rows of B with at most two stages in
+// flight, so a grid of few blocks cannot keep HBM busy (16 x 4096 x 8192, 64
+// blocks: 2.7 TB/s).  Grids of fewer than 256 blocks split K over up to 8
+// workgroups per block (about 256 in all), at least 4 stages each, no empty range.
+constexpr int64_t kSkinnyMinStagesPerSplit = 4;
+int choose_skinny_splits(int64_t tiles, int64_t nst)
+{
+    if (tiles >= 256) return 1;
+    int64_t s = std::min<int64_t>(kSkinnyMaxSplits, std::max<int64_t>(1, 256 / std::max<int64_t>(tiles, 1)));
+    s = std::min<int64_t>(s, std::max<int64_t>(1, nst / kSkinnyMinStagesPerSplit));
+    while (s > 1 && (s - 1) * ((nst + s - 1) / s) >= nst) --s;
     return (int)s;
 }
 
@@ -354,12 +370,20 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         in.lds_bytes = (int64_t)kLds64Stages * (kLds64BM + kLds64BN) * kLds64BK * 2;
         in.k_tiles = (int32_t)ceil_div(K, kLds64BK);
     } else if (variant == TLG_VARIANT_SKINNY) {
+        const int64_t tiles = ceil_div(M, kSkinnyRows) * ceil_div(N, kSkinnyNB);
+        const int64_t nst = ceil_div(K, kSkinnyKST);
+        const int sp = choose_skinny_splits(tiles, nst);
         in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
         in.stages = kSkinnyStages;
         in.threads = kSkinnyThreads;
-        in.grid = ceil_div(M, kSkinnyRows) * ceil_div(N, kSkinnyNB);
+        in.grid = tiles * sp;
         in.lds_bytes = (int64_t)kSkinnyStages * (kSkinnyNB + kSkinnyRows) * kSkinnyKST * 2;
-        in.k_tiles = (int32_t)ceil_div(K, kSkinnyKST);
+        in.k_tiles = (int32_t)ceil_div(nst, sp);
+        if (sp > 1) {
+            p->splits = sp;
+            p->ws_partials_bytes = (size_t)tiles * sp * kSkinnyRows * kSkinnyNB * sizeof(float);
+            p->ws_bytes = p->ws_partials_bytes + (size_t)((tiles * sizeof(unsigned) + 255) / 256 * 256);
+        }
     }
     in.splits = p->splits;
     in.workspace_bytes = (int64_t)p->ws_bytes;
@@ -491,6 +515,9 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
     if (p.variant == TLG_VARIANT_SKINNY) {
         gp.tiles_m = (int)ceil_div(p.M, kSkinnyRows);
         gp.tiles_n = (int)ceil_div(p.N, kSkinnyNB);
+        gp.splits = p.splits;
+        gp.ws = ws;
+        gp.counters = counters;
         err = launch_skinny(gp, p.ab, (hipStream_t)stream);
     } else if (p.variant == TLG_VARIANT_TILE_256_DMA) {
         gp.tiles_m = (int)ceil_div(p.M, kLdsBM);
@@ -552,7 +579,8 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
 //   [kScratchPartialBytes, + kScratchCounterBytes)  one counter per output tile
 // The automatic plan never needs more: it splits K only for fewer than 128 tiles
 // of 128 x 128, into at most 256 / tiles ranges (tiles x ranges <= 256 partial
-// tiles of 64 KiB).
+// tiles of 64 KiB), and in the skinny kernel for fewer than 256 blocks (at most
+// 256 partial blocks of 4 KiB).
 // ---------------------------------------------------------------------------
 constexpr size_t kScratchPartialBytes = size_t(256) * kLds128BM * kLds128BN * sizeof(float);   // 16 MiB
 constexpr size_t kScratchCounterBytes = 4096;                                                 // 1024 counters

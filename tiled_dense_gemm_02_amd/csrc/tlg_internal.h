@@ -59,6 +59,7 @@ constexpr int kSkinnyNB = 64;
 constexpr int kSkinnyThreads = 512;  // 8 waves split the K steps of each stage
 constexpr int kSkinnyKST = 256;      // K elements per LDS stage (512-byte row segments)
 constexpr int kSkinnyStages = 3;     // LDS ring depth
+constexpr int kSkinnyMaxSplits = 8;  // K ranges per column block (grids of few column blocks)
 
 // Launchers (defined in the kernel translation units).  vec_a / vec_b: 8 for
 // 128-bit global loads, 1 for 16-bit loads.
