@@ -148,6 +148,19 @@ def test_split_k_choice():
     assert lib.tlg_gemm_select(ctypes.byref(tlg.PlanInfo()), -1, 1, 1, 1, 1, 0, 0, 1, 0, 0) == INVALID
 
 
+def test_wave_count_rule_between_tile_sizes():
+    """From 128 tiles of 256x256 up, the wave count picks the tile size: 0.37 x (waves of
+    128x128 tiles) against 0.97 x (waves of 256x256 tiles)."""
+    want = {(8192, 1536, 8192): 6,     # 192 tiles of 256^2 (one partial wave) vs 3 waves of 128^2
+            (3000, 3000, 3000): 6,     # 144 vs 576 (3 waves)
+            (8192, 1024, 8192): 7,     # 128 tiles of 256^2 vs 512 of 128^2 (2 waves)
+            (2816, 2816, 1024): 7,     # 121 tiles of 256^2: below half the chip
+            (4600, 4350, 4100): 7,     # 306 (2 waves, the second nearly empty) vs 1224 (5 waves)
+            (4096, 4096, 4096): 6, (8192, 8192, 8192): 6}
+    for (M, N, K), v in want.items():
+        assert tlg.select(M, N, K, transpose_B=(M, N, K) == (4600, 4350, 4100)).variant == v, (M, N, K)
+
+
 def test_plan_geometry_matches_the_pages_worked_figures():
     """LDS bytes and K trips of the 128x128x64 fp16 tile against the handbook's exercise answers."""
     rows = [l.split() for l in open(os.path.join(GOLDEN, "page_geometry.txt")) if l.strip() and l[0] != "#"]

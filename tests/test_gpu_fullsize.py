@@ -95,6 +95,16 @@ def test_small_integers_exact_full_size(n, ab, c, relu):
     assert plan.info.k_tiles == n // 64
 
 
+# ------------------------------------------------------------ one partial wave of 256x256 tiles
+def test_partial_wave_of_large_tiles_exact():
+    """3000^3: 144 tiles of 256 x 256 in one partial wave (XCD remap on: 144 = 8 x 18;
+    12 x 12 tiles in three bands of four rows, the last tile row and column 184 wide),
+    every output exact on small integers."""
+    case = W.GemmCase("int-3000", 3000, 3000, 3000, c="f32", relu=1, dist="smallint", seed=4310)
+    plan = _check_full(case, exact=True, guard=4096, want_variant=6)
+    assert plan.info.grid == 144
+
+
 # ------------------------------------------------------------ the skinny kernel's rotated K order
 @pytest.mark.parametrize("M,N,K", [(16, 16384, 8192), (16, 16384, 4096), (13, 4000, 8200)])
 def test_skinny_small_integers_exact_full_size(M, N, K):

@@ -250,17 +250,20 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         // 1000x1500x777 bf16 13.5 -> 10.8 us; at 2048^3, 256 tiles of 128x128,
         // they are 1.5x slower).
         //
-        // Once 256x256 tiles fill the chip, the wave count decides between the two
-        // tile sizes: a wave of 128x128 tiles costs about 0.37 of a wave of 256x256
-        // tiles (measured on MI355X: 8192^3 82 vs 222 us per wave, 4096^3 43 vs 122,
-        // 6144^3 43 vs 107), so a grid whose last wave of 256x256 tiles is nearly
-        // empty runs faster in 128x128 tiles (4600x4350x4100: 306 tiles of 256x256,
-        // 2 waves, 293 us; 1224 of 128x128, 5 waves, 260 us).
+        // Once 256x256 tiles fill at least half the chip, the wave count decides
+        // between the two tile sizes: a wave of 128x128 tiles costs about 0.37 of a
+        // wave of 256x256 tiles (measured on MI355X: 8192^3 82 vs 222 us per wave,
+        // 4096^3 43 vs 122, 6144^3 43 vs 107), so a grid whose last wave of 256x256
+        // tiles is nearly empty runs faster in 128x128 tiles (4600x4350x4100: 306
+        // tiles of 256x256, 2 waves, 293 us; 1224 of 128x128, 5 waves, 260 us), and
+        // one partial wave of more than 128 tiles of 256x256 beats three waves of
+        // 128x128 (8192x1536x8192: 194 against 246 us), while 128 of them lose to
+        // two waves of 128x128 (8192x1024x8192: 184 against 168 us).
         const int64_t t128 = ceil_div(M, 128) * ceil_div(N, 128), kt = ceil_div(K, 64);
         const int64_t t256 = ceil_div(M, 256) * ceil_div(N, 256);
-        if (t256 >= 256 && 37 * ceil_div(t128, 256) < 97 * ceil_div(t256, 256))
+        if (t256 >= 128 && 37 * ceil_div(t128, 256) < 97 * ceil_div(t256, 256))
             variant = TLG_VARIANT_TILE_128_DMA;
-        else if (t256 >= 256)
+        else if (t256 >= 128)
             variant = TLG_VARIANT_TILE_256_DMA;
         else if (t128 < 128 && kt >= kSplitMinKTiles && choose_splits(t128, kt) >= 2)
             variant = TLG_VARIANT_TILE_128_DMA_SPLITK;
