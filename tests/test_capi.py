@@ -161,6 +161,20 @@ def test_wave_count_rule_between_tile_sizes():
         assert tlg.select(M, N, K, transpose_B=(M, N, K) == (4600, 4350, 4100)).variant == v, (M, N, K)
 
 
+def test_skinny_rule_for_up_to_64_rows():
+    """A stored [M,K], B stored [N,K]: the skinny kernel for M <= 16 always; for 16 < M <= 32
+    (32 x 64 blocks) from K = 1024 on; for 32 < M <= 64 (64 x 32 blocks) while its blocks
+    fit about 1.5 rounds of the CUs, or two with K >= 4096."""
+    want = {(16, 16384, 256): (3, 16), (24, 16384, 8192): (3, 32), (32, 16384, 1024): (3, 32),
+            (24, 4096, 512): (10, 64), (64, 8192, 2048): (3, 64), (64, 16384, 8192): (3, 64),
+            (64, 16384, 2048): (10, 64), (48, 28672, 8192): (7, 128)}
+    for (M, N, K), (v, bm) in want.items():
+        i = tlg.select(M, N, K, transpose_B=True)
+        assert (i.variant, i.block_m) == (v, bm), (M, N, K, i.variant, i.block_m)
+    # B stored [K,N]: no skinny kernel
+    assert tlg.select(32, 16384, 8192).variant != 3
+
+
 def test_plan_geometry_matches_the_pages_worked_figures():
     """LDS bytes and K trips of the 128x128x64 fp16 tile against the handbook's exercise answers."""
     rows = [l.split() for l in open(os.path.join(GOLDEN, "page_geometry.txt")) if l.strip() and l[0] != "#"]

@@ -1,4 +1,5 @@
-"""GPU parity of the skinny kernel with K split over several workgroups per column block
+"""GPU parity of the skinny kernel's wider instances (32 x 64 and 64 x 32 outputs per
+workgroup for 16 < M <= 64) and of its K split over several workgroups per column block
 (grids of fewer than 256 blocks of 16 x 64 outputs: each workgroup streams a range of K
 stages and the last one of a block to finish sums the fp32 partial tiles in K-range
 order).  Every output is compared with the oracle: within the tolerance on N(0,1)/sqrt(K)
@@ -79,8 +80,8 @@ def test_accumulate_onto_c(c):
 
 
 def test_two_row_blocks_forced():
-    """M = 32 through the forced skinny variant: two row blocks, each with its own ranges."""
-    case = W.GemmCase("rows32", 32, 1024, 4096, transpose_B=1, dist="normal", seed=5400)
+    """M = 80 through the forced skinny variant: two row blocks of 64, each with its own ranges."""
+    case = W.GemmCase("rows80", 80, 1024, 4096, transpose_B=1, dist="normal", seed=5400)
     plan = _check(case, variant="skinny")
     assert plan.info.splits > 1
 
@@ -105,3 +106,30 @@ def test_plan_reused_counters_return_to_zero():
         A, B, _ = inputs[i]
         assert_within_tolerance(out_values(outs[i].view(torch.float16)), oracle_full(case, A, B, None), case,
                                 "plan reuse")
+
+
+# ---------------------------------------------------------------- 17 <= M <= 64 (and more rows forced)
+@pytest.mark.parametrize("M,N,K", [(17, 1000, 1040), (24, 16384, 8192), (32, 4000, 8200), (48, 2048, 4096),
+                                   (64, 16384, 8192), (64, 999, 3000)])
+def test_wider_row_blocks_exact(M, N, K):
+    """32 rows (M <= 32) and 64 rows (M <= 64, 32 columns per block) of A per workgroup:
+    exact on small integers, ragged rows, columns and K, split and unsplit plans."""
+    case = W.GemmCase(f"rows-{M}x{N}x{K}", M, N, K, c="f32", transpose_B=1, relu=M % 2, dist="smallint",
+                      seed=5600 + M)
+    plan = _check(case, exact=True)
+    assert plan.info.block_m == (32 if M <= 32 else 64)
+
+
+@pytest.mark.parametrize("M,c", [(40, "f16"), (100, "bf16")])
+def test_wider_row_blocks_tolerance(M, c):
+    """M = 100 through the forced skinny variant: two row blocks of 64."""
+    case = W.GemmCase(f"rows-{M}-{c}", M, 3000, 4096, ab="bf16" if c == "bf16" else "f16", c=c, transpose_B=1,
+                      dist="normal", seed=5700 + M)
+    _check(case, variant="skinny")
+
+
+def test_wider_row_blocks_accumulate():
+    case = W.GemmCase("rows-accum", 56, 2048, 8192, c="f16", transpose_B=1, clear_accum=0, relu=1, dist="normal",
+                      seed=5800)
+    plan = _check(case)
+    assert plan.info.block_m == 64 and plan.info.splits > 1

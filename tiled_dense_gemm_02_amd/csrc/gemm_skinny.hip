@@ -1,18 +1,19 @@
-// Skinny GEMM  C[M x N] = act(A·B)  for M <= 16 rows per workgroup, B stored
-// [N, K] (transpose_B = 1), A stored [M, K].  This shape is bound by the HBM
-// stream of B (one read of each element), not by MFMA: the roofline bound
-// P <= min(P_peak, I * B_mem) of the overview page's "performance model"
-// section puts its arithmetic intensity near 16 FLOP/byte.
+// Skinny GEMM  C[M x N] = act(A·B)  for MR = 16, 32 or 64 rows of A per
+// workgroup, B stored [N, K] (transpose_B = 1), A stored [M, K].  This shape is
+// bound by the HBM stream of B (one read of each element), not by MFMA: the
+// roofline bound P <= min(P_peak, I * B_mem) of the overview page's "performance
+// model" section puts its arithmetic intensity near 16 FLOP/byte per row of A.
 //
-// Each workgroup owns 16 rows x kSkinnyNB columns of C, i.e. kSkinnyNB
-// consecutive rows of B, and streams them exactly once through an S-stage LDS
-// ring.  One stage holds KST elements of K of every B row of the workgroup and
-// of the 16 A rows.  Stages are filled with global->LDS direct loads in which
-// each instruction reads 1 KiB of B (or A) rows contiguously, so HBM sees long
-// row segments rather than 64-byte pieces of many rows.  The eight waves take
-// different 32-wide K steps of a stage and multiply with MFMA 16x16x32; their
-// partial 16 x NB tiles are summed in LDS in a fixed order (deterministic),
-// then the epilogue applies (+ prior C) -> ReLU -> rounding -> guarded stores.
+// Each workgroup owns MR rows x NB columns of C (16 x 64, 32 x 64 or 64 x 32),
+// i.e. NB consecutive rows of B, and streams them exactly once through an
+// S-stage LDS ring.  One stage holds KST elements of K of every B row of the
+// workgroup and of the MR A rows.  Stages are filled with global->LDS direct
+// loads in which each instruction reads 1 KiB of B (or A) rows contiguously, so
+// HBM sees long row segments rather than 64-byte pieces of many rows.  The eight
+// waves take different 32-wide K steps of a stage and multiply with MFMA
+// 16x16x32 (each B fragment against the MR / 16 A fragments); their partial
+// MR x NB tiles are summed in LDS in a fixed order (deterministic), then the
+// epilogue applies (+ prior C) -> ReLU -> rounding -> guarded stores.
 //
 // Row layout in a stage: 16-byte chunk c of row r sits at c ^ (r & 15), so the
 // sixteen lanes that read sixteen consecutive rows of one chunk for an MFMA
@@ -29,11 +30,12 @@
 
 namespace tlg {
 
-template <int T_IN, int NB, int KST, int S>
+template <int T_IN, int NB, int KST, int S, int MR>
 __global__ void __launch_bounds__(kSkinnyThreads)
 gemm_skinny_kernel(GemmParams p)
 {
-    constexpr int WAVES = kSkinnyThreads / 64, MR = kSkinnyRows;
+    constexpr int WAVES = kSkinnyThreads / 64;
+    constexpr int MT = MR / 16;                      // 16-row MFMA tiles of A
     constexpr int RB = KST * 2;                      // bytes per row segment of a stage
     constexpr int ROWS = NB + MR;                    // B rows, then A rows
     constexpr int STAGE = ROWS * RB;
@@ -50,7 +52,9 @@ gemm_skinny_kernel(GemmParams p)
     static_assert(CHUNKS >= 16 && 1024 % RB == 0, "row segment of 256 B .. 1 KiB");
     static_assert(S >= 2 && S * STAGE <= 160 * 1024, "LDS ring must fit in 160 KiB");
     static_assert((S - 2) * LPW < 64, "vmcnt range");
-    static_assert(WAVES * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
+    static_assert(MR % 16 == 0 && MR % LPI == 0, "MR");
+    static_assert(WAVES * MT * NS * 4 * 64 * 4 <= S * STAGE, "reduction area reuses the ring");
+    static_assert(MT * NS <= WAVES, "one wave per 16 x 16 output block in the epilogue");
 
     __shared__ __attribute__((aligned(1024))) char smem[S * STAGE];
 
@@ -111,9 +115,11 @@ gemm_skinny_kernel(GemmParams p)
         return *(const u32x4*)(slot + row * RB + ((c ^ (row & 15)) << 4));
     };
 
-    f32x4 acc[NS];
+    f32x4 acc[MT][NS];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NS; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
     for (int st = 0; st < S - 1; ++st)
@@ -131,49 +137,60 @@ gemm_skinny_kernel(GemmParams p)
 #pragma unroll
         for (int u = 0; u < SPW; ++u) {
             const int c = (wave * SPW + u) * 4 + (lane >> 4);
-            const u32x4 af = frag(slot, NB + (lane & 15), c);
-            // B fragment first: the hardware tile is C's transpose, so acc[j][e]
-            // is C[m0 + lane%16][n0 + 16j + 4*(lane/16) + e].
+            u32x4 af[MT];
 #pragma unroll
-            for (int j = 0; j < NS; ++j) acc[j] = mfma16x16x32<T_IN>(frag(slot, j * 16 + (lane & 15), c), af, acc[j]);
+            for (int mt = 0; mt < MT; ++mt) af[mt] = frag(slot, NB + mt * 16 + (lane & 15), c);
+            // B fragment first: the hardware tile is C's transpose, so acc[mt][j][e]
+            // is C[m0 + 16mt + lane%16][n0 + 16j + 4*(lane/16) + e].
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const u32x4 bf = frag(slot, j * 16 + (lane & 15), c);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt][j] = mfma16x16x32<T_IN>(bf, af[mt], acc[mt][j]);
+            }
         }
     }
     wait_vmcnt<0>();
     __syncthreads();
 
-    float* red = (float*)smem;   // [WAVES][NS][4][64]
+    // The waves' partial sums meet in LDS; wave w then owns output block
+    // (w / NS, w % NS) of the MT x NS blocks of 16 x 16 and sums it in wave order.
+    constexpr int NBLK = MT * NS;
+    float* red = (float*)smem;   // [WAVES][NBLK][4][64]
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[((wave * NS + j) * 4 + e) * 64 + lane] = acc[j][e];
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((wave * NBLK + mt * NS + j) * 4 + e) * 64 + lane] = acc[mt][j][e];
     __syncthreads();
 
-    const int m = m0 + (lane & 15);
+    const bool owner = wave < NBLK;
+    const int mt_o = wave / NS, j_o = wave % NS;
+    const int m = m0 + mt_o * 16 + (lane & 15);
     const bool vec_cols = p.c_vec != 0;
-    static_assert(NS <= WAVES, "one wave per 16-column block in the epilogue");
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (wave < NS) {
-        const int j = wave;
+    if (owner) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float s = red[(j * 4 + e) * 64 + lane];
+            float s = red[(wave * 4 + e) * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < WAVES; ++w) s += red[((w * NS + j) * 4 + e) * 64 + lane];
+            for (int w = 1; w < WAVES; ++w) s += red[((w * NBLK + wave) * 4 + e) * 64 + lane];
             v[e] = s;
         }
     }
     if (splits > 1) {
-        // Publish this K range's 16 x NB partial tile (fp32), take a ticket; the last
+        // Publish this K range's MR x NB partial tile (fp32), take a ticket; the last
         // workgroup of the tile sums the partials in K-range order, then runs the
         // epilogue.  The XCDs' L2 caches are separate, so partials are written and
         // read with device-scope (sc1) buffer accesses; each wave waits for its
         // stores before the barrier that precedes the ticket.
         __shared__ unsigned ticket;
         const int tile = (int)(blockIdx.y * gridDim.x + blockIdx.x);
-        constexpr int PART = NS * 64 * 4;                 // floats per partial tile
+        constexpr int PART = NBLK * 64 * 4;               // floats per partial tile
         const __amdgpu_buffer_rsrc_t wsr = make_rsrc(p.ws + (size_t)tile * splits * PART,
                                                      (uint64_t)splits * PART * 4u);
-        if (wave < NS)
+        if (owner)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), wsr,
                                                    (uint32_t)((blockIdx.z * PART + (wave * 64 + lane) * 4) * 4), 0,
                                                    kCoherentDevice);
@@ -183,7 +200,7 @@ gemm_skinny_kernel(GemmParams p)
             ticket = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(ticket) != (unsigned)(splits - 1)) return;
-        if (wave < NS) {
+        if (owner) {
             constexpr int MAXS = kSkinnyMaxSplits;
             u32x4 part[MAXS];
 #pragma unroll
@@ -199,8 +216,8 @@ gemm_skinny_kernel(GemmParams p)
         if (threadIdx.x == 0)   // ready for the next launch
             __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int n = n0 + wave * 16 + 4 * (lane >> 4);
-    if (wave < NS && m < p.M && n < p.N) {
+    const int n = n0 + j_o * 16 + 4 * (lane >> 4);
+    if (owner && m < p.M && n < p.N) {
         const int count = min(4, p.N - n);
         const bool vec_ok = vec_cols && count == 4;
         const int64_t idx = (int64_t)m * p.N + n;
@@ -218,21 +235,30 @@ gemm_skinny_kernel(GemmParams p)
     }
 }
 
-template <int T>
+template <int T, int MR, int NB>
 static hipError_t launch_skinny_t(const GemmParams& p, hipStream_t stream)
 {
     GemmParams args = p;
     void* kargs[] = {&args};
     const dim3 grid((unsigned)p.tiles_n, (unsigned)p.tiles_m, (unsigned)(p.splits > 1 ? p.splits : 1));
     const dim3 block(kSkinnyThreads);
-    return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, kSkinnyNB, kSkinnyKST, kSkinnyStages>, grid,
-                           block, kargs, 0, stream);
+    return hipLaunchKernel((const void*)&gemm_skinny_kernel<T, NB, kSkinnyKST, kSkinnyStages, MR>, grid, block,
+                           kargs, 0, stream);
 }
 
+// Rows of A per block (skinny_rows) and columns per block (skinny_cols) follow M,
+// as the plan computed them.
 hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream)
 {
-    if (ab_dtype == DT_F16) return launch_skinny_t<DT_F16>(p, stream);
-    return launch_skinny_t<DT_BF16>(p, stream);
+    const int mr = skinny_rows(p.M);
+    if (ab_dtype == DT_F16) {
+        if (mr == 16) return launch_skinny_t<DT_F16, 16, skinny_cols(16)>(p, stream);
+        if (mr == 32) return launch_skinny_t<DT_F16, 32, skinny_cols(32)>(p, stream);
+        return launch_skinny_t<DT_F16, 64, skinny_cols(64)>(p, stream);
+    }
+    if (mr == 16) return launch_skinny_t<DT_BF16, 16, skinny_cols(16)>(p, stream);
+    if (mr == 32) return launch_skinny_t<DT_BF16, 32, skinny_cols(32)>(p, stream);
+    return launch_skinny_t<DT_BF16, 64, skinny_cols(64)>(p, stream);
 }
 
 }  // namespace tlg

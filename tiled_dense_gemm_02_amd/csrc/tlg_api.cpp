@@ -127,6 +127,24 @@ int choose_skinny_splits(int64_t tiles, int64_t nst)
     return (int)s;
 }
 
+// Whether the automatic plan takes the skinny kernel for M <= 64 (A stored [M,K],
+// B stored [N,K]).  Measured on MI355X against the 64 x 128 tile kernel: with 16 <
+// M <= 32 (32 x 64 blocks) it wins from K = 1024 on (32 x 16384 x 1024: 8.4 against
+// 9.5 us; 32 x 16384 x 8192: 44.6 against 62.8 us) and loses at K = 512; with
+// 32 < M <= 64 (64 x 32 blocks) it wins while the blocks fit about 1.5 rounds of
+// the CUs (64 x 8192 x 8192: 30.2 against 54.5 us; 64 x 12288 x 4096: 30.8 against
+// 32.3 us), or two rounds with a long K (64 x 16384 x 8192: 58 against 66 us), and
+// loses beyond (64 x 16384 x 2048: 20.8 against 19.8 us; 48 x 28672 x 8192: 102
+// against 85 us).
+bool skinny_pays(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= kSkinnyRows) return true;
+    if (K < 1024) return false;
+    if (M <= 32) return true;
+    const int64_t blocks = ceil_div(N, skinny_cols(skinny_rows(M)));
+    return blocks <= 384 || (blocks <= 512 && K >= 4096);
+}
+
 bool is_streamk(int v) { return v == TLG_VARIANT_TILE_256_DMA_STREAMK || v == TLG_VARIANT_TILE_128_DMA_STREAMK; }
 
 // Persistent grid of the stream-K variants: one workgroup per CU of an MI355X
@@ -238,7 +256,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
              is_streamk(forced)) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
         if (forced == TLG_VARIANT_TILE_64_DMA && tA) return TLG_ERR_UNSUPPORTED;
-    } else if (M <= kSkinnyRows && skinny_ok) {
+    } else if (M <= kSkinnyMaxRows && skinny_ok && skinny_pays(M, N, K)) {
         variant = TLG_VARIANT_SKINNY;
     } else if (dma_ok) {
         // 256x256 tiles once they fill every CU, else 128x128 tiles (4x the workgroups);
@@ -296,7 +314,8 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         const int64_t bm = variant == TLG_VARIANT_TILE_64_DMA ? kLds64BM : b;
         if (ceil_div(M, bm) * ceil_div(N, b) * splits > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
-        if (ceil_div(M, kSkinnyRows) > 65535 || ceil_div(N, kSkinnyNB) > INT32_MAX) return TLG_ERR_INVALID_ARG;
+        const int mr = skinny_rows(M);
+        if (ceil_div(M, mr) > 65535 || ceil_div(N, skinny_cols(mr)) > INT32_MAX) return TLG_ERR_INVALID_ARG;
     }
 
     p->M = M; p->N = N; p->K = K;
@@ -373,18 +392,19 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         in.lds_bytes = (int64_t)kLds64Stages * (kLds64BM + kLds64BN) * kLds64BK * 2;
         in.k_tiles = (int32_t)ceil_div(K, kLds64BK);
     } else if (variant == TLG_VARIANT_SKINNY) {
-        const int64_t tiles = ceil_div(M, kSkinnyRows) * ceil_div(N, kSkinnyNB);
+        const int mr = skinny_rows(M), nb = skinny_cols(mr);
+        const int64_t tiles = ceil_div(M, mr) * ceil_div(N, nb);
         const int64_t nst = ceil_div(K, kSkinnyKST);
         const int sp = choose_skinny_splits(tiles, nst);
-        in.block_m = kSkinnyRows; in.block_n = kSkinnyNB; in.block_k = kSkinnyKST;
+        in.block_m = mr; in.block_n = nb; in.block_k = kSkinnyKST;
         in.stages = kSkinnyStages;
         in.threads = kSkinnyThreads;
         in.grid = tiles * sp;
-        in.lds_bytes = (int64_t)kSkinnyStages * (kSkinnyNB + kSkinnyRows) * kSkinnyKST * 2;
+        in.lds_bytes = (int64_t)kSkinnyStages * (nb + mr) * kSkinnyKST * 2;
         in.k_tiles = (int32_t)ceil_div(nst, sp);
         if (sp > 1) {
             p->splits = sp;
-            p->ws_partials_bytes = (size_t)tiles * sp * kSkinnyRows * kSkinnyNB * sizeof(float);
+            p->ws_partials_bytes = (size_t)tiles * sp * mr * nb * sizeof(float);
             p->ws_bytes = p->ws_partials_bytes + (size_t)((tiles * sizeof(unsigned) + 255) / 256 * 256);
         }
     }
@@ -516,8 +536,8 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
 
     hipError_t err;
     if (p.variant == TLG_VARIANT_SKINNY) {
-        gp.tiles_m = (int)ceil_div(p.M, kSkinnyRows);
-        gp.tiles_n = (int)ceil_div(p.N, kSkinnyNB);
+        gp.tiles_m = (int)ceil_div(p.M, skinny_rows(p.M));
+        gp.tiles_n = (int)ceil_div(p.N, skinny_cols(skinny_rows(p.M)));
         gp.splits = p.splits;
         gp.ws = ws;
         gp.counters = counters;

@@ -52,10 +52,15 @@ inline TileShape tile_shape(int cfg)
     return TileShape{128, 128, 64, 2, 1, 2};
 }
 
-// Skinny kernel geometry: 16 rows x kSkinnyNB columns per workgroup, operands
-// staged through a kSkinnyStages-deep LDS ring of kSkinnyKST-wide K stages.
-constexpr int kSkinnyRows = 16;
-constexpr int kSkinnyNB = 64;
+// Skinny kernel geometry: skinny_rows(M) rows x skinny_cols(rows) columns per
+// workgroup (16 x 64, 32 x 64 or 64 x 32: a stage of A and B rows is 40 or 48
+// KiB), operands staged through a kSkinnyStages-deep LDS ring of kSkinnyKST-wide
+// K stages.
+constexpr int kSkinnyRows = 16;       // rows of the M <= 16 instance
+constexpr int kSkinnyMaxRows = 64;    // the automatic plan uses the skinny kernel for M <= 64
+constexpr int kSkinnyNB = 64;         // columns of the 16- and 32-row instances
+__host__ __device__ constexpr int skinny_rows(int64_t M) { return M <= 16 ? 16 : M <= 32 ? 32 : 64; }
+__host__ __device__ constexpr int skinny_cols(int rows) { return rows == 64 ? 32 : kSkinnyNB; }
 constexpr int kSkinnyThreads = 512;  // 8 waves split the K steps of each stage
 constexpr int kSkinnyKST = 256;      // K elements per LDS stage (512-byte row segments)
 constexpr int kSkinnyStages = 3;     // LDS ring depth
