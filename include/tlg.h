@@ -62,7 +62,7 @@ typedef enum {
     TLG_VARIANT_AUTO = 0,
     TLG_VARIANT_TILE_256 = 1,  /* 256x256x64 block tile, 4 wave64s, 2-stage LDS ring */
     TLG_VARIANT_TILE_128 = 2,  /* 128x128x64 block tile, 2 wave64s, 2-stage LDS ring */
-    TLG_VARIANT_SKINNY = 3,    /* M <= 16 rows per block, B stored [N,K], streaming  */
+    TLG_VARIANT_SKINNY = 3,    /* 16/32/64 rows of A per block, B stored [N,K], streaming */
     TLG_VARIANT_EMPTY = 4,     /* M == 0 or N == 0: nothing to launch (chosen by create) */
     TLG_VARIANT_TILE_256_W8 = 5, /* 256x256x64 block tile, 8 wave64s (2 per SIMD), 2-stage ring */
     TLG_VARIANT_TILE_256_DMA = 6, /* 256x256x64, 8 wave64s, LDS ring filled by global->LDS direct loads */
@@ -136,7 +136,7 @@ typedef struct {
  * TLG_ERR_NOMEM if the plan cannot be allocated.  Plans with K split over
  * several workgroups per tile (tlg_plan_info.splits > 1, chosen for output grids
  * of fewer than 128 tiles of 128x128 with at least 48 K tiles of 64, and for the
- * skinny kernel when it has fewer than 256 blocks of 16 x 64 outputs and at least
+ * skinny kernel when it has fewer than 256 blocks of outputs and at least
  * 8 K stages of 256) allocate a device workspace here
  * (tlg_plan_info.workspace_bytes: fp32 partial tiles plus one counter per tile),
  * on the device current at the call, zero its counters and wait for that to
@@ -206,7 +206,7 @@ tlg_status tlg_gemm_run(tlg_gemm_t plan, const void *A, const void *B, void *C, 
  * partial tiles plus 4 KiB of counters, one copy per GPU, held until the process
  * ends.  The automatic choice always fits (it splits only grids of fewer than 128
  * tiles of 128 x 128, into at most 256 partial tiles, and skinny grids of fewer
- * than 256 blocks, into at most 256 partial blocks of 4 KiB); a request that would
+ * than 256 blocks, into at most 256 partial blocks of 4 or 8 KiB); a request that would
  * need more is refused with TLG_ERR_TOO_LARGE.  The first call on a device looks up
  * the buffer's device address and enqueues a small kernel on `stream` that zeroes
  * the counters; every split-K launch returns the counters it uses to zero.

@@ -603,7 +603,7 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
 // The automatic plan never needs more: it splits K only for fewer than 128 tiles
 // of 128 x 128, into at most 256 / tiles ranges (tiles x ranges <= 256 partial
 // tiles of 64 KiB), and in the skinny kernel for fewer than 256 blocks (at most
-// 256 partial blocks of 4 KiB).
+// 256 partial blocks of 4 or 8 KiB).
 // ---------------------------------------------------------------------------
 constexpr size_t kScratchPartialBytes = size_t(256) * kLds128BM * kLds128BN * sizeof(float);   // 16 MiB
 constexpr size_t kScratchCounterBytes = 4096;                                                 // 1024 counters
