@@ -29,9 +29,9 @@ struct tlg_gemm_s {
     int variant;
     int vec_a, vec_b;
     int align_a, align_b;  // byte alignment run() requires of A and B
-    // split-K plans: workspace = [tiles][splits][128*128] (skinny: [16*64]) fp32
-    // partials, then one counter per tile (zero between launches); allocated on
-    // `device` at create
+    // split-K plans: workspace = [tiles][splits][128*128] (skinny: [rows*cols of a
+    // block]) fp32 partials, then one counter per tile (zero between launches);
+    // allocated on `device` at create
     int splits = 1;
     void* ws = nullptr;
     size_t ws_partials_bytes = 0, ws_bytes = 0;
@@ -112,10 +112,10 @@ int choose_splits(int64_t tiles, int64_t ktiles)
     return (int)s;
 }
 
-// K ranges of the skinny kernel for `tiles` blocks of 16 x 64 outputs and `nst`
-// 256-wide K stages.  A block streams its 64 rows of B with at most two stages in
-// flight, so a grid of few blocks cannot keep HBM busy (16 x 4096 x 8192, 64
-// blocks: 2.7 TB/s).  Grids of fewer than 256 blocks split K over up to 8
+// K ranges of the skinny kernel for `tiles` blocks of outputs (16 x 64, 32 x 64 or
+// 64 x 32) and `nst` 256-wide K stages.  A block streams its rows of B with at most
+// two stages in flight, so a grid of few blocks cannot keep HBM busy (16 x 4096 x
+// 8192, 64 blocks: 2.7 TB/s).  Grids of fewer than 256 blocks split K over up to 8
 // workgroups per block (about 256 in all), at least 4 stages each, no empty range.
 constexpr int64_t kSkinnyMinStagesPerSplit = 4;
 int choose_skinny_splits(int64_t tiles, int64_t nst)
