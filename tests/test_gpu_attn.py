@@ -1,6 +1,8 @@
 """GPU parity of the attention forward (tlg_attn_fwd) against the CPU attention oracle on
 the same seeded fp16/bf16 bits.  Tolerance per element (derived in the oracle):
-|gpu - o| <= 2u (|o| + max|V|) + 1e-5, u = 2^-11 (fp16) or 2^-8 (bf16)."""
+|gpu - o| <= 2u (|o| + max|V|) + 1e-5, u = 2^-11 (fp16) or 2^-8 (bf16).  At full size,
+flat scores with integer values are checked at every output against the exact mean of
+V over the allowed keys, within (u + 2^-20) |o|."""
 from __future__ import annotations
 
 import numpy as np
@@ -82,6 +84,59 @@ def test_full_size_sampled(name):
     err = _check(case, out[pb, pi, ph], o, float(v.float().abs().max()))
     assert np.isfinite(out).all()
     log(f"    max|err| = {err:.3e}")
+
+
+def _check_prefix_mean(case: W.AttnCase):
+    """Every output of a flat-score case against the exact mean of V's integers.
+
+    With K = 0 every score is exactly zero, so every allowed key gets probability
+    2^0 = 1 in the operand type; the row sum is the exact key count and the weighted
+    sum of integers in [-4, 4] is exact in fp32.  O is then the exact mean o rounded
+    twice in fp32 (the reciprocal of the count, the product) and once to the operand
+    type: |gpu - o| <= (u + 2^-20) |o| with u = 2^-11 (fp16) or 2^-8 (bf16), where
+    |o| >= 1/S whenever o != 0 keeps o in the normal range.  A key block dropped,
+    repeated or taken from the wrong rows moves some output of the last rows by at
+    least 1/S, far outside this bound."""
+    log(f"[case] {case.name} B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} {case.dtype} "
+        f"flat scores, integer values, every output")
+    q, k, v = W.make_attn_inputs(case)
+    out = _run(case, q, k, v)
+    vi = v.float().numpy().astype(np.int64)
+    del q, k, v
+    u = 2.0 ** -11 if case.dtype == "f16" else 2.0 ** -8
+    count = np.arange(1, case.S + 1, dtype=np.float64)[:, None, None]
+    worst = 0.0
+    for b in range(case.B):
+        if case.causal:
+            o = np.cumsum(vi[b], axis=0) / count
+        else:
+            o = np.broadcast_to(vi[b].sum(axis=0) / case.S, vi[b].shape)
+        got = out_values(out[b])
+        err = np.abs(got - o)
+        bad = ~(err <= (u + 2.0 ** -20) * np.abs(o))
+        if bad.any():
+            idx = np.argwhere(bad)[:5]
+            raise AssertionError(f"{case.name} batch {b}: {int(bad.sum())} of {bad.size} outputs off the exact "
+                                 f"mean; first (i, h, d) {idx.tolist()} gpu={got[bad][:5]} exact={o[bad][:5]}")
+        nz = o != 0
+        if nz.any():
+            worst = max(worst, float((err[nz] / np.abs(o[nz])).max()))
+    log(f"    max relative error {worst:.3e} (bound {u + 2.0 ** -20:.3e})")
+
+
+@pytest.mark.parametrize("name", ["fa3", "fa4"])
+def test_full_size_flat_scores_every_output(name):
+    """The two large causal workloads at full size, every output checked: the causal
+    mask and every key block of every (batch, head) enter each row exactly once."""
+    _check_prefix_mean(W.ATTN_CONFIGS[name].with_(name=f"{name}-flat-int", dist="flat_int_values", seed=1450))
+
+
+@pytest.mark.parametrize("shape", [(2, 4000, 8, 128, 0), (1, 4000, 4, 64, 1)], ids=lambda s: "x".join(map(str, s)))
+def test_ragged_flat_scores_every_output_bf16(shape):
+    """A partial last key block (4000 = 62.5 blocks of 64), with and without the mask."""
+    B, S, H, D, causal = shape
+    _check_prefix_mean(W.AttnCase(f"flat-int-{B}x{S}x{H}x{D}-c{causal}", B, S, H, D, causal=causal, dtype="bf16",
+                                  dist="flat_int_values", seed=1460 + causal))
 
 
 SWEEP = [(1, 1, 1, 64, 1), (1, 2, 3, 128, 0), (2, 63, 2, 64, 1), (1, 64, 2, 128, 1), (1, 65, 1, 64, 0),

@@ -102,6 +102,22 @@ def test_small_integers_exact(ab, c):
           guard=512, exact=True)
 
 
+@pytest.mark.parametrize("ab", ["f16", "bf16"])
+def test_w4a_small_integers_exact_full_size(ab):
+    """The decode shape 16 x 16384 x 8192 in full, exactly, with a scale 2^-1..2^2 and a
+    zero point 0..15 of its own for every row and group of 128: each weight is a multiple
+    of 1/2 of magnitude at most 60 and A holds integers in [-4, 4], so every partial sum
+    is a multiple of 1/2 below 2^21 (exact in fp32), and a scale or zero point read from
+    the wrong row or group changes the result."""
+    case = W.W4Case(f"w4a-int-groups-{ab}", 16, 16384, 8192, G=128, ab=ab, c="f32", dist="smallint_groups",
+                    seed=7300 + (ab == "bf16"))
+    log(f"[case] full-size {case.name} exact")
+    A, Wq, S, Z, _ = W.make_w4_inputs(case)
+    gpu = out_values(_run(case, A, Wq, S, Z))
+    o = O.w4gemm(case.M, case.N, case.K, case.G, W.bits16(A), Wq.numpy(), W.bits16(S), Z.numpy(), dtype=case.ab)
+    _check(case, gpu, o, A, 0.0, exact=True)
+
+
 EDGES = [(1, 1, 32, 32), (1, 64, 32, 32), (16, 65, 64, 64), (17, 130, 544, 32), (3, 257, 1536, 256),
          (2, 129, 8160, 32), (4, 100, 0, 32)]
 

@@ -299,7 +299,7 @@ class AttnCase:
     D: int
     causal: int = 1
     dtype: str = "f16"
-    dist: str = "normal"     # "normal" | "uniform_keys" | "ramp_up" | "ramp_down"
+    dist: str = "normal"     # "normal" | "uniform_keys" | "flat_int_values" | "ramp_up" | "ramp_down"
     scale: float | None = None   # None: 1/sqrt(D), the page's choice
     seed: int = 0
     note: str = field(default="", compare=False)
@@ -347,6 +347,12 @@ def make_attn_inputs(case: AttnCase):
     v = torch.randn(case.shape, generator=g)
     if case.dist == "uniform_keys":
         k = torch.zeros(case.shape)
+    elif case.dist == "flat_int_values":
+        # Every score is zero and V holds small integers: each allowed key gets
+        # probability 1 exactly, so O is the exact mean of V's integers over the
+        # allowed keys, rounded once to the operand type.
+        k = torch.zeros(case.shape)
+        v = torch.randint(-4, 5, case.shape, generator=g).to(torch.float32)
     elif case.dist in ("ramp_up", "ramp_down"):
         # Scores that rise (fall) by about 0.2 in log2 units per key position: every
         # query is close to the first axis and key j's first coordinate is j steps.
@@ -405,7 +411,7 @@ class W4Case:
     ab: str = "f16"
     c: str = "f16"
     relu: int = 0
-    dist: str = "normal"     # "normal" | "smallint"
+    dist: str = "normal"     # "normal" | "smallint" | "smallint_groups"
     seed: int = 0
     lo: int = -4
     hi: int = 4
@@ -463,6 +469,15 @@ def make_w4_inputs(case: W4Case):
         q = torch.randint(0, 16, (N, K), generator=g).to(torch.uint8)
         S = torch.ones((N, K // G), dtype=dt)
         Z = torch.full((N, K // G), 8, dtype=torch.uint8)
+    elif case.dist == "smallint_groups":
+        # Integers, with a power-of-two scale in {1/2, 1, 2, 4} and a zero point in
+        # 0..15 drawn per row and group: every weight (q - z) s is a multiple of 1/2
+        # of magnitude at most 60, exact in fp16 and bf16, so sums stay exact while
+        # every group's own scale and zero point matter.
+        A = torch.randint(case.lo, case.hi + 1, (case.M, K), generator=g).to(dt)
+        q = torch.randint(0, 16, (N, K), generator=g).to(torch.uint8)
+        S = torch.pow(2.0, torch.randint(-1, 3, (N, K // G), generator=g).to(torch.float32)).to(dt)
+        Z = torch.randint(0, 16, (N, K // G), generator=g).to(torch.uint8)
     elif case.dist == "normal":
         A = (torch.rand((case.M, K), generator=g) * 2.0 - 1.0).to(dt)
         w = torch.randn((N, K), generator=g).reshape(N, K // G, G)
