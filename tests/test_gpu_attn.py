@@ -1,9 +1,11 @@
 """GPU parity of the attention forward (tlg_attn_fwd) against the CPU attention oracle on
 the same seeded fp16/bf16 bits.  Tolerance per element (derived in the oracle):
 |gpu - o| <= 2u (|o| + max|V|) + 1e-5, u = 2^-11 (fp16) or 2^-8 (bf16).  At full size,
-flat scores with integer values are checked at every output against the exact mean of
-V over the allowed keys, within (u + 2^-20) |o|."""
+flat scores and integer scores (exact power-of-two probabilities) with integer values
+are checked at every output against exact values, within (u + 2^-20) |o|."""
 from __future__ import annotations
+
+import math
 
 import numpy as np
 import pytest
@@ -137,6 +139,81 @@ def test_ragged_flat_scores_every_output_bf16(shape):
     B, S, H, D, causal = shape
     _check_prefix_mean(W.AttnCase(f"flat-int-{B}x{S}x{H}x{D}-c{causal}", B, S, H, D, causal=causal, dtype="bf16",
                                   dist="flat_int_values", seed=1460 + causal))
+
+
+def _dyadic_expected(case: W.AttnCase, q, k, v, b: int) -> np.ndarray:
+    """Softmax-weighted means of the dyadic-score recipe for batch b, [S, H, D], exactly:
+    query i's weights are 2^(k[j,0] + q[i,1] k[j,1]) (the row maximum is 0 at key 0), so
+    with two query classes the weighted sums over the allowed keys are prefix sums of
+    dyadic numbers, exact in float64, and one division gives each output."""
+    kb = k[b].float().numpy().astype(np.float64)
+    vb = v[b].float().numpy().astype(np.float64)
+    cls = q[b, :, :, 1].float().numpy()
+    out = np.empty(vb.shape)
+    for c in (0.0, 1.0):
+        w = np.exp2(kb[:, :, 0] + c * kb[:, :, 1])
+        if case.causal:
+            o = np.cumsum(w[:, :, None] * vb, axis=0) / np.cumsum(w, axis=0)[:, :, None]
+        else:
+            o = np.broadcast_to((w[:, :, None] * vb).sum(axis=0) / w.sum(axis=0)[:, None], vb.shape)
+        sel = cls == c
+        out[sel] = o[sel]
+    return out
+
+
+def _check_dyadic(case: W.AttnCase):
+    """Every output of a dyadic-score case against its exact value.
+
+    With the scale ln 2 the kernel's folded factor scale*log2(e) is exactly 1, every
+    score is an integer in [-6, 0] and every row's first key block holds its maximum 0,
+    so each probability is an exact power of two in [2^-6, 1] in the operand type and
+    the row sums and P V sums (multiples of 2^-6 below 2^14) are exact in fp32.  The
+    result differs from the exact value only by the two fp32 roundings of the division
+    and the rounding to the operand type: |gpu - o| <= (u + 2^-20) |o|, plus half the
+    fp16 subnormal spacing (2^-25) since |o| can be as small as 2^-6 / S.  The expected
+    values are pinned to the oracle on sampled rows."""
+    log(f"[case] {case.name} B={case.B} S={case.S} H={case.H} D={case.D} causal={case.causal} {case.dtype} "
+        f"dyadic scores, every output")
+    q, k, v = W.make_attn_inputs(case)
+    out = _run(case, q, k, v)
+    pb, pi, ph = W.sample_attn_rows(case, 64)
+    o_pts = O.attn_points(case.B, case.S, case.H, case.D, W.bits16(q), W.bits16(k), W.bits16(v), pb, pi, ph,
+                          dtype=case.dtype, causal=case.causal, scale=case.softmax_scale)
+    u = 2.0 ** -11 if case.dtype == "f16" else 2.0 ** -8
+    floor = 2.0 ** -25 if case.dtype == "f16" else 0.0
+    worst = 0.0
+    for b in range(case.B):
+        o = _dyadic_expected(case, q, k, v, b)
+        sel = pb == b
+        if sel.any():
+            ref = o[pi[sel], ph[sel]]
+            assert np.allclose(ref, o_pts[sel], rtol=1e-12, atol=1e-15), "closed form disagrees with the oracle"
+        got = out_values(out[b])
+        err = np.abs(got - o)
+        bad = ~(err <= (u + 2.0 ** -20) * np.abs(o) + floor)
+        if bad.any():
+            idx = np.argwhere(bad)[:5]
+            raise AssertionError(f"{case.name} batch {b}: {int(bad.sum())} of {bad.size} outputs off the exact "
+                                 f"value; first (i, h, d) {idx.tolist()} gpu={got[bad][:5]} exact={o[bad][:5]}")
+        nz = np.abs(o) > 2.0 ** -14
+        if nz.any():
+            worst = max(worst, float((err[nz] / np.abs(o[nz])).max()))
+    log(f"    max relative error (|o| > 2^-14) {worst:.3e} (bound {u + 2.0 ** -20:.3e})")
+
+
+@pytest.mark.parametrize("name", ["fa3", "fa4"])
+def test_full_size_dyadic_scores_every_output(name):
+    """The two large causal workloads at full size through the exponentials, row sums and
+    P V products with query-dependent scores, every output checked."""
+    _check_dyadic(W.ATTN_CONFIGS[name].with_(name=f"{name}-dyadic", dist="dyadic_scores", scale=math.log(2.0),
+                                             seed=1470))
+
+
+@pytest.mark.parametrize("shape", [(2, 4000, 8, 128, 0), (1, 4000, 4, 64, 1)], ids=lambda s: "x".join(map(str, s)))
+def test_ragged_dyadic_scores_every_output_bf16(shape):
+    B, S, H, D, causal = shape
+    _check_dyadic(W.AttnCase(f"dyadic-{B}x{S}x{H}x{D}-c{causal}", B, S, H, D, causal=causal, dtype="bf16",
+                             dist="dyadic_scores", scale=math.log(2.0), seed=1480 + causal))
 
 
 SWEEP = [(1, 1, 1, 64, 1), (1, 2, 3, 128, 0), (2, 63, 2, 64, 1), (1, 64, 2, 128, 1), (1, 65, 1, 64, 0),

@@ -299,7 +299,7 @@ class AttnCase:
     D: int
     causal: int = 1
     dtype: str = "f16"
-    dist: str = "normal"     # "normal" | "uniform_keys" | "flat_int_values" | "ramp_up" | "ramp_down"
+    dist: str = "normal"     # "normal" | "uniform_keys" | "flat_int_values" | "dyadic_scores" | "ramp_up" | "ramp_down"
     scale: float | None = None   # None: 1/sqrt(D), the page's choice
     seed: int = 0
     note: str = field(default="", compare=False)
@@ -352,6 +352,21 @@ def make_attn_inputs(case: AttnCase):
         # probability 1 exactly, so O is the exact mean of V's integers over the
         # allowed keys, rounded once to the operand type.
         k = torch.zeros(case.shape)
+        v = torch.randint(-4, 5, case.shape, generator=g).to(torch.float32)
+    elif case.dist == "dyadic_scores":
+        # Integer scores in [-6, 0] with every row's maximum 0 at key 0: query i's
+        # score for key j is k[j,0] + q[i,1] k[j,1] with q[i,0] = 1, q[i,1] in {0, 1},
+        # k[j,0] in [-4, 0], k[j,1] in [-2, 0] and key 0 all zero (the other
+        # coordinates of Q are arbitrary, those of K zero).  With the scale ln 2 the
+        # probabilities are exact powers of two in [2^-6, 1]; V holds integers in
+        # [-4, 4], so every sum over keys is exact in fp32.
+        q = torch.randint(-3, 4, case.shape, generator=g).to(torch.float32)
+        q[..., 0] = 1.0
+        q[..., 1] = torch.randint(0, 2, case.shape[:3], generator=g).to(torch.float32)
+        k = torch.zeros(case.shape)
+        k[..., 0] = torch.randint(-4, 1, case.shape[:3], generator=g).to(torch.float32)
+        k[..., 1] = torch.randint(-2, 1, case.shape[:3], generator=g).to(torch.float32)
+        k[:, 0] = 0.0
         v = torch.randint(-4, 5, case.shape, generator=g).to(torch.float32)
     elif case.dist in ("ramp_up", "ramp_down"):
         # Scores that rise (fall) by about 0.2 in log2 units per key position: every
