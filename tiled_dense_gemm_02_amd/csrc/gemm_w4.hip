@@ -183,15 +183,41 @@ __global__ void __launch_bounds__(kW4Threads) gemm_w4_kernel(W4Params p)
     for (int st = 0; st < S - 2; ++st)
         if (st < NST) issue(st);
     // Scale / zero table of this workgroup's rows (rows past N: zero weights).
-    for (int i = threadIdx.x; i < NB * KG; i += WAVES * 64) {
-        const int r = i / KG, gi = i - r * KG;
-        uint32_t e = 0;
-        if (n0 + r < p.N) {
-            const int64_t idx = (int64_t)(n0 + r) * KG + gi;
-            const uint32_t z = ((const uint8_t*)p.Z)[idx];
-            e = (T_IN == DT_F16 ? 0x6400u + z : z) | ((uint32_t)((const uint16_t*)p.S)[idx] << 16);
+    // Every gather is issued before the first is waited for: entry i of the table
+    // is thread i % 1024's gather number i / 1024 (at most GMAX of them), read
+    // through range-checked resources (entries past the rows' end read zeros).
+    {
+        constexpr int GMAX = (NB * kW4MaxGroups + WAVES * 64 - 1) / (WAVES * 64);
+        const int nent = NB * KG;
+        const int rows = min(NB, p.N - n0);
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc((const uint8_t*)p.Z + (uint64_t)n0 * KG, (uint64_t)rows * KG);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc((const uint16_t*)p.S + (uint64_t)n0 * KG, (uint64_t)rows * KG * 2u);
+        uint32_t zv[GMAX], sv[GMAX];
+#pragma unroll
+        for (int it = 0; it < GMAX; ++it) {
+            const int i = (int)threadIdx.x + it * WAVES * 64;
+            zv[it] = sv[it] = 0u;
+            if (it * WAVES * 64 < nent) {
+                // i = r * KG + gi is the entry's offset in both arrays (row-major [N, K/G]).
+                const uint32_t off = i < nent ? (uint32_t)i : kOOB;
+                zv[it] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, off, 0, 0);
+                sv[it] = buf_load2(rs, off == kOOB ? kOOB : off * 2u);
+            }
         }
-        tab[gi * NB + (r ^ (gi & 15))] = e;
+#pragma unroll
+        for (int it = 0; it < GMAX; ++it) {
+            const int i = (int)threadIdx.x + it * WAVES * 64;
+            if (it * WAVES * 64 < nent) {
+                // Keeps the use of the loaded values here, after every gather has gone out.
+                asm volatile("" : "+v"(zv[it]), "+v"(sv[it]));
+                if (i < nent) {
+                    const int r = i / KG, gi = i - r * KG;
+                    const uint32_t e =
+                        n0 + r < p.N ? ((T_IN == DT_F16 ? 0x6400u + zv[it] : zv[it]) | (sv[it] << 16)) : 0u;
+                    tab[gi * NB + (r ^ (gi & 15))] = e;
+                }
+            }
+        }
     }
     // The gathers above overlap the first stages' direct loads.  They are waited
     // for here, together with everything issued before them: the ring's vmcnt
