@@ -3,7 +3,8 @@ C-ABI, against the plan + run pair of tlg_gemm_create / tlg_gemm_run on the same
 which runs the same kernel, so the outputs must be bit-identical; and against the oracle
 within the tolerance |gpu - o| <= 2^-10 |o| + 1e-4 sqrt(K).  Two calls in a row, the second
 smaller, both with a split-K choice (the calls share the library's static scratch), then
-shapes whose automatic plan needs no scratch."""
+shapes whose automatic plan needs no scratch; and the same calls captured into a graph and
+replayed."""
 from __future__ import annotations
 
 import ctypes
@@ -69,3 +70,50 @@ def test_noalloc_without_scratch():
     for case in (W.CONFIGS["c1"], W.CONFIGS["c4"], W.CONFIGS["c5b"].with_(N=2048, K=1024)):
         plan = _pair(case)
         assert plan.info.splits == 1
+
+
+def test_noalloc_under_graph_capture():
+    """Callers under HIP graph capture: a split-K and a skinny-split call captured once
+    into a graph (after one eager call on the device, which sets up the static scratch),
+    replayed four times with C cleared, and other eager calls that use the same scratch,
+    between the replays.  Every replay must equal the eager result bit for bit."""
+    import tiled_dense_gemm_02_amd as tlg
+    dev = torch.device("cuda:0")
+    T = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    cases = [W.GemmCase("graph-1024x1024x4096", 1024, 1024, 4096, relu=1, seed=4311),
+             W.GemmCase("graph-16x4096x8192", 16, 4096, 8192, c="f32", transpose_B=1, seed=4312)]
+    runs = []
+    for case in cases:
+        A, B, _ = W.make_inputs(case)
+        Ad, Bd = A.to(dev), B.to(dev)
+        kw = dict(transpose_B=bool(case.transpose_B), epilogue="relu" if case.relu else "none")
+        ref = torch.empty((case.M, case.N), dtype=T[case.c], device=dev)
+        tlg.gemm_noalloc(Ad, Bd, ref, **kw)
+        torch.cuda.synchronize()
+        runs.append((case, Ad, Bd, kw, ref, torch.empty_like(ref)))
+    side = torch.cuda.Stream(dev)
+    graph = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for case, Ad, Bd, kw, ref, out in runs:       # warm-up on the capture stream
+            tlg.gemm_noalloc(Ad, Bd, out, **kw)
+    torch.cuda.synchronize()
+    log("[case] noalloc graph: capturing " + ", ".join(r[0].name for r in runs))
+    with torch.cuda.graph(graph, stream=side):
+        for case, Ad, Bd, kw, ref, out in runs:
+            tlg.gemm_noalloc(Ad, Bd, out, **kw)
+    for rep in range(4):
+        for _, _, _, _, _, out in runs:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for case, _, _, _, ref, out in runs:
+            assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), f"replay {rep} of {case.name} differs"
+        # eager calls between the replays, on the same scratch (the other shape's plan)
+        for case, Ad, Bd, kw, ref, out in runs[::-1]:
+            scratch_user = torch.empty_like(ref)
+            tlg.gemm_noalloc(Ad, Bd, scratch_user, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(scratch_user.view(torch.uint8), ref.view(torch.uint8))
+        log(f"    replay {rep}: bit-identical to the eager result")
