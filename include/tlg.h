@@ -69,7 +69,7 @@ typedef enum {
     TLG_VARIANT_TILE_128_DMA = 7, /* 128x128x64, 8 wave64s, 4-slot ring of direct loads (grids too small for 256x256) */
     TLG_VARIANT_TILE_128_DMA_SPLITK = 8, /* as 7, K split over several workgroups per tile (plan owns a workspace) */
     TLG_VARIANT_MX_256 = 9,    /* block-scaled FP8 / FP4: 256x256 x 128 bytes of K, 8 wave64s, scaled MFMA 16x16x128 */
-    TLG_VARIANT_TILE_64_DMA = 10, /* 64x128x64, 8 wave64s, 4-slot ring of direct loads; A stored [M,K] only
+    TLG_VARIANT_TILE_64_DMA = 10, /* 64x128x128, 8 wave64s, 3-slot ring of direct loads; A stored [M,K] only
                                     (transpose_A == 0); grids of at most 128 tiles of 128x128 */
     TLG_VARIANT_TILE_256_DMA_STREAMK = 11, /* as 6, persistent: 256 workgroups (one per CU) take the tiles
                                     of all but the last wave whole, then equal shares of the remaining
