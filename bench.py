@@ -77,11 +77,21 @@ W4_VARIANT = "w4"
 SP_VARIANT = "sp"
 
 
+def _code_only(text: str) -> str:
+    """A C/C++ source without its comments and blank lines, so that the hash below
+    follows the code and not the wording of its comments (no kernel source has a
+    comment marker inside a string literal)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_hash(variant) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[variant]:
-        with open(os.path.join(ROOT, "tiled_dense_gemm_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "tiled_dense_gemm_02_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,0 +1,33 @@
+"""Host-side pieces of bench.py (no GPU): the kernel-source hash that ties the stored
+rocprofv3 traffic figures to the code they were measured on, and the stored figures'
+validity for the current sources."""
+from __future__ import annotations
+
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_code_only_drops_comments_and_blank_lines_only():
+    src = "int a = 1; // one\n\n/* a\n   block */ int b = 2;\n  return a + b;  \n"
+    assert bench._code_only(src) == "int a = 1;\n int b = 2;\n  return a + b;"
+    # a change of code changes the text, a change of comment does not
+    assert bench._code_only(src.replace("// one", "// uno")) == bench._code_only(src)
+    assert bench._code_only(src.replace("a + b", "a - b")) != bench._code_only(src)
+
+
+def test_stored_traffic_matches_current_kernel_code():
+    """Every committed FETCH/WRITE summary was taken on the current kernel code."""
+    variants = {"c3": 6, "c5a": 6, "c5b": 3, "fa3": "attn", "fa4": "attn", "mx3": 9, "mx6": 9, "sp3": "sp",
+                "w4a": "w4"}
+    for w, v in variants.items():
+        path = os.path.join(ROOT, "profiles", f"pmc_{w}.json")
+        rec = json.load(open(path))
+        assert rec["kernel_hash"] == bench.kernel_hash(v), f"{w}: profile taken on other kernel code"
+        assert bench.stored_traffic(w, v) == rec["traffic_bytes_per_launch"]

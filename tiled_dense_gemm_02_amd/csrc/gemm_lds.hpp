@@ -1,10 +1,12 @@
-// Tiled GEMM with a two-slot LDS ring fed by global->LDS direct loads.
+// Tiled GEMM with an LDS ring fed by global->LDS direct loads.
 //
-// The tile program of the overview page's GEMM example (one 256 x 256 output
-// tile per workgroup, a K loop over 64-wide tiles, fp32 register fragments,
-// fused epilogue), with the software pipeline of T.Pipelined realised as a
-// ring: while tile j is multiplied, tile j+1 is in flight ("software
-// pipelining" section of the overview page).
+// The tile program of the overview page's GEMM example (one output tile per
+// workgroup, a K loop over K tiles, fp32 register fragments, fused epilogue),
+// with the software pipeline of T.Pipelined realised as a ring of S slots: while
+// tile j is multiplied, tiles j+1 .. j+S-1 are in flight ("software pipelining"
+// section of the overview page).  Instances: 256 x 256 tiles with 64-wide K
+// tiles and 2 slots (the large-shape default, described below), 128 x 128 with
+// 64-wide K tiles and 4 slots, 64 x 128 with 128-wide K tiles and 3 slots.
 //
 // Global->LDS copies use buffer_load_dwordx4 ... lds: each lane's 16 bytes go
 // straight to LDS at (1 KiB block + 16 * lane), with no VGPR staging and no LDS
@@ -18,7 +20,8 @@
 // matrix's last row, whose chunk runs past the buffer, it is refetched).
 // M/N-contiguous rows must hold a multiple of 8 elements.
 //
-// Operand layouts in LDS (one ring slot; "rows" are the operand's M or N index):
+// Operand layouts in LDS (one ring slot of a 256 x 256 tile; "rows" are the
+// operand's M or N index; LdsOperand below gives the general rule):
 //   K-contiguous operand (A stored [M,K], B stored [N,K]): 256 rows of 64
 //     elements (128 bytes); 16-byte chunk c of row r sits at c ^ ((r / 2) % 8).
 //     A fragment (16 consecutive rows, one chunk) is one ds_read_b128 per lane
@@ -50,9 +53,9 @@
 //     the remaining MFMAs cover the latency of the next tile's first fragment
 //     reads, so no wave starts a tile waiting on LDS;
 //   - right after that barrier the tile's slot is free and the loads of the
-//     tile two ahead are issued, one every R MFMAs, so each load has a full
-//     K tile of MFMA work to land and the vector-memory queue never blocks
-//     the MFMA stream.
+//     tile S ahead (two ahead with 2 slots) are issued, one every R MFMAs, so
+//     each load has at least a full K tile of MFMA work to land and the
+//     vector-memory queue never blocks the MFMA stream.
 #pragma once
 
 #include <utility>
