@@ -100,6 +100,11 @@ def test_variant_choice_and_geometry_for_the_workloads():
     assert tlg.select(1024, 1024, 1024, transpose_A=True).variant == 7
     with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
         tlg.select(1024, 1024, 1024, transpose_A=True, variant="tile64dma")
+    # B stored [K, N]: 127 rows of k apart must stay inside a 31-bit lane offset
+    assert tlg.select(64, 8454656, 128, variant="tile64dma").variant == 10
+    with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
+        tlg.select(64, 8454664, 128, variant="tile64dma")
+    assert tlg.select(64, 8454664, 128, transpose_B=True, variant="tile64dma").variant == 10
     # B stored [N, K] is fine: 1000x1500x777 forced
     assert tlg.select(1000, 1500, 777, "bf16", "f32", transpose_B=True, variant="tile64dma").grid == 16 * 12
     # forced split: 4 ranges of 4 K tiles (256 workgroups)

@@ -256,6 +256,12 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
              is_streamk(forced)) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
         if (forced == TLG_VARIANT_TILE_64_DMA && tA) return TLG_ERR_UNSUPPORTED;
+        // Its K tiles are 128 rows of k: with B stored [K,N] a lane's direct-load
+        // offset reaches 127 rows of 2N bytes (plus a chunk), which must stay below
+        // 2^31 (offsets from 2^31 up read as out of range).  The automatic choice
+        // takes this variant only for N <= 128 * 128.
+        if (forced == TLG_VARIANT_TILE_64_DMA && !tB && 127 * 2 * N + 256 > (int64_t)INT32_MAX)
+            return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyMaxRows && skinny_ok && skinny_pays(M, N, K)) {
         variant = TLG_VARIANT_SKINNY;
     } else if (dma_ok) {
