@@ -67,6 +67,7 @@ KERNEL_SOURCES = {
     7: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     8: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
     10: ["gemm_lds.hpp", "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "tlg_device.hpp"],
+    13: ["gemm_lds.hpp", "gemm_lds32.hip", "tlg_device.hpp"],
     9: ["gemm_mx.hpp", "gemm_mx.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     "attn": ["attn_fwd.hpp", "attn_fwd.hip", "gemm_lds.hpp", "tlg_device.hpp"],
     "w4": ["gemm_w4.hip", "gemm_lds.hpp", "tlg_device.hpp"],

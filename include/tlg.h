@@ -74,7 +74,9 @@ typedef enum {
     TLG_VARIANT_TILE_256_DMA_STREAMK = 11, /* as 6, persistent: 256 workgroups (one per CU) take the tiles
                                     of all but the last wave whole, then equal shares of the remaining
                                     tiles' K iterations (stream-K); the plan owns a workspace */
-    TLG_VARIANT_TILE_128_DMA_STREAMK = 12  /* as 7, with the persistent stream-K schedule of 11 */
+    TLG_VARIANT_TILE_128_DMA_STREAMK = 12, /* as 7, with the persistent stream-K schedule of 11 */
+    TLG_VARIANT_TILE_32_DMA = 13  /* 32x128x128, 4 wave64s, 3-slot ring of direct loads; A stored [M,K] only
+                                    (transpose_A == 0); grids whose 32x128 tiles fit one wave (256) */
 } tlg_variant;
 
 typedef enum {
@@ -164,7 +166,9 @@ tlg_status tlg_gemm_select(tlg_plan_info *info, int64_t M, int64_t N, int64_t K,
  * As tlg_gemm_create, but forces a kernel variant (tlg_variant).  Returns
  * TLG_ERR_UNSUPPORTED when the forced variant cannot run the request (the
  * skinny variant needs transpose_A == 0, transpose_B == 1 and K % 8 == 0;
- * TILE_64_DMA needs transpose_A == 0).
+ * TILE_64_DMA and TILE_32_DMA need transpose_A == 0, and with transpose_B == 0
+ * N <= 8454656, so that a direct load's lane offset, up to 127 rows of B apart,
+ * stays below 2^31).
  */
 tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_t K,
                                    int32_t ab_dtype, int32_t c_dtype, int32_t transpose_A,
@@ -180,7 +184,8 @@ tlg_status tlg_gemm_create_variant(tlg_gemm_t *out, int64_t M, int64_t N, int64_
  *   C    : device pointer to the packed M x N output (read when clear_accum == 0).
  * A and B must be aligned to their element size, and to 16 bytes when the plan
  * uses 128-bit loads for them (tlg_plan_info.vec_a / vec_b == 8), except that
- * the direct-load variants (TILE_256_DMA, TILE_128_DMA, TILE_128_DMA_SPLITK, TILE_64_DMA) take K-contiguous
+ * the direct-load variants (TILE_256_DMA, TILE_128_DMA, TILE_128_DMA_SPLITK, TILE_64_DMA, TILE_32_DMA and
+ * the stream-K variants) take K-contiguous
  * operands (A with transpose_A == 0, B with transpose_B == 1) at element
  * alignment and any K; C to its element size.  C must not overlap A or B.
  * Returns TLG_ERR_NULL, TLG_ERR_MISALIGNED, TLG_ERR_INVALID_ARG (overlap) or
@@ -270,7 +275,8 @@ typedef struct {
  * and for the split-K variant the number of K ranges, by timing every
  * candidate that can serve the request on the caller's buffers.  Candidates:
  * the fp16/bf16 variants of tlg_variant (TILE_256_DMA, TILE_128_DMA, TILE_64_DMA,
- * SKINNY, TILE_256_W8, TILE_256, TILE_128), and the split-K variant with 2..8
+ * TILE_32_DMA, SKINNY, TILE_256_W8, TILE_256, TILE_128, TILE_256_DMA_STREAMK,
+ * TILE_128_DMA_STREAMK), and the split-K variant with 2..8
  * ranges when the output has fewer than 256 tiles of 128 x 128 (block-scaled
  * requests are refused, see tlg_gemm_run_mx).  A candidate
  * that refuses the request (TLG_ERR_UNSUPPORTED) or the buffers' alignment

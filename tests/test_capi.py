@@ -57,7 +57,7 @@ def test_create_rejects_bad_arguments():
     assert _create(4, 4, 4, tA=2)[0] == INVALID
     assert _create(4, 4, 4, clear=3)[0] == INVALID
     assert _create(4, 4, 4, epi=2)[0] == INVALID
-    assert _create(4, 4, 4, variant=13)[0] == INVALID
+    assert _create(4, 4, 4, variant=14)[0] == INVALID
     assert _create(4, 4, 4, variant=9)[0] == UNSUPPORTED                # the block-scaled kernel needs FP8
     assert _create(100, 100, 777, tA=1, tB=1, variant=8)[0] == UNSUPPORTED
     # forced variants that cannot run the request
@@ -87,24 +87,36 @@ def test_variant_choice_and_geometry_for_the_workloads():
                           transpose_B=case.transpose_B, epilogue="relu" if case.relu else "none",
                           variant=variant)
 
-    # at most 128 tiles of 128x128 with A stored [M,K]: 64x128 tiles
+    # at most 128 tiles of 128x128 with A stored [M,K]: 32x128 tiles while they fit one wave of 256
+    # workgroups, else 64x128 tiles
     i = info(C["c1"])
-    assert (i.variant, i.block_m, i.block_n, i.grid, i.k_tiles, i.splits) == (10, 64, 128, 8, 2, 1)
-    # 1024^3: 64 tiles of 128x128 (too short a K to split) -> 128 tiles of 64x128, 8 K tiles of 128 each
+    assert (i.variant, i.block_m, i.block_n, i.grid, i.k_tiles, i.splits) == (13, 32, 128, 16, 2, 1)
+    # 1024^3: 64 tiles of 128x128 (too short a K to split) -> 256 tiles of 32x128, 8 K tiles of 128 each
     i = info(C["c2"])
+    assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (13, 32, 128, 128, 256, 8)
+    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (3, 256, 3 * (32 + 128) * 128 * 2, 1, 0)
+    i = info(C["c2"], "tile64dma")
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (10, 64, 128, 128, 128, 8)
     assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (3, 512, 3 * (64 + 128) * 128 * 2, 1, 0)
+    # the boundary: 256 tiles of 32x128 take them, 257 (or 384) fall back to 64x128
+    assert tlg.select(1024, 1024, 512).variant == 13
+    assert tlg.select(1056, 1024, 512).variant == 10
+    assert tlg.select(1024, 1536, 1024, transpose_B=True).variant == 10
     i = info(C["c2"], "tile128dma")
     assert (i.variant, i.block_m, i.grid, i.lds_bytes) == (7, 128, 64, 4 * 2 * 128 * 64 * 2)
     # A stored [K,M]: 64-row tiles of an M-contiguous operand do not exist
     assert tlg.select(1024, 1024, 1024, transpose_A=True).variant == 7
-    with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
-        tlg.select(1024, 1024, 1024, transpose_A=True, variant="tile64dma")
+    for v in ("tile64dma", "tile32dma"):
+        with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
+            tlg.select(1024, 1024, 1024, transpose_A=True, variant=v)
     # B stored [K, N]: 127 rows of k apart must stay inside a 31-bit lane offset
     assert tlg.select(64, 8454656, 128, variant="tile64dma").variant == 10
     with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
         tlg.select(64, 8454664, 128, variant="tile64dma")
     assert tlg.select(64, 8454664, 128, transpose_B=True, variant="tile64dma").variant == 10
+    assert tlg.select(32, 8454656, 128, variant="tile32dma").variant == 13
+    with pytest.raises(tlg.TlgError, match="UNSUPPORTED"):
+        tlg.select(32, 8454664, 128, variant="tile32dma")
     # B stored [N, K] is fine: 1000x1500x777 forced
     assert tlg.select(1000, 1500, 777, "bf16", "f32", transpose_B=True, variant="tile64dma").grid == 16 * 12
     # forced split: 4 ranges of 4 K tiles (256 workgroups)
@@ -171,8 +183,8 @@ def test_skinny_rule_for_up_to_64_rows():
     (32 x 64 blocks) from K = 1024 on; for 32 < M <= 64 (64 x 32 blocks) while its blocks
     fit about 1.5 rounds of the CUs, or two with K >= 4096."""
     want = {(16, 16384, 256): (3, 16), (24, 16384, 8192): (3, 32), (32, 16384, 1024): (3, 32),
-            (24, 4096, 512): (10, 64), (64, 8192, 2048): (3, 64), (64, 16384, 8192): (3, 64),
-            (64, 16384, 2048): (10, 64), (48, 28672, 8192): (7, 128)}
+            (24, 4096, 512): (13, 32), (64, 8192, 2048): (3, 64), (64, 16384, 8192): (3, 64),
+            (64, 16384, 2048): (13, 32), (48, 28672, 8192): (7, 128)}
     for (M, N, K), (v, bm) in want.items():
         i = tlg.select(M, N, K, transpose_B=True)
         assert (i.variant, i.block_m) == (v, bm), (M, N, K, i.variant, i.block_m)
@@ -207,7 +219,7 @@ def test_run_validation_happens_before_any_launch():
     assert g.run_ptrs(4096, 8192, 0) == NULL
     # (every pointer set below fails validation: nothing is ever launched on them)
     # direct loads: K-contiguous A at element alignment, B stored [K, N] at 16 bytes
-    assert g.info.variant == 10
+    assert g.info.variant == 13
     assert g.run_ptrs(4096 + 1, 1 << 20, 1 << 21) == MISALIGNED     # A not element-aligned
     assert g.run_ptrs(4096, (1 << 20) + 2, 1 << 21) == MISALIGNED   # B not 16-byte aligned
     assert g.run_ptrs(4096, (1 << 20) + 8, 1 << 21) == MISALIGNED

@@ -100,14 +100,14 @@ def test_config5b_skinny_full():
 
 # ---------------------------------------------------------------- exactness
 # The skinny kernel takes A stored [M,K] and B stored [N,K] only (tA=0, tB=1).
-# The 64x128 direct-load kernel takes A stored [M,K] only (tA=0).
+# The 64x128 and 32x128 direct-load kernels take A stored [M,K] only (tA=0).
 def _layouts_of(v, layouts=((0, 0), (0, 1), (1, 0), (1, 1))):
     return [(tA, tB) for tA, tB in layouts
-            if (v != "skinny" or (tA, tB) == (0, 1)) and (v != "tile64dma" or tA == 0)]
+            if (v != "skinny" or (tA, tB) == (0, 1)) and (v not in ("tile64dma", "tile32dma") or tA == 0)]
 
 
 _EXACT_CASES = [(v, tA, tB) for v in ["tile256", "tile256w8", "tile256dma", "tile128dma", "tile128dma_sk", "tile64dma",
-                                      "tile128", "skinny"]
+                                      "tile32dma", "tile128", "skinny"]
                 for tA, tB in _layouts_of(v)]
 
 
@@ -117,7 +117,7 @@ def test_small_integers_exact(variant, ab, tA, tB):
     # 300 rows: ragged for the 128 tile; the 256 tile needs 128-bit loads, so with A
     # stored [K, M] its M must be a multiple of 8 (304)
     M = {"skinny": 16, "tile128": 300, "tile256": 304, "tile256w8": 304, "tile256dma": 304, "tile128dma": 304,
-         "tile128dma_sk": 304, "tile64dma": 300}[variant]
+         "tile128dma_sk": 304, "tile64dma": 300, "tile32dma": 300}[variant]
     case = W.GemmCase("smallint", M, 264, 200, ab=ab, c="f32", transpose_A=tA, transpose_B=tB,
                       dist="smallint", seed=77, relu=1)
     _full_check(case, variant=variant, exact=True)
@@ -128,18 +128,19 @@ RAGGED = [1, 15, 17, 31, 33, 64, 65, 127, 129, 257]
 
 
 @pytest.mark.parametrize("variant,tA,tB", [(v, tA, tB) for v in ["tile128", "tile256", "tile256w8", "tile256dma",
-                                                                   "tile128dma", "tile128dma_sk", "tile64dma"]
+                                                                   "tile128dma", "tile128dma_sk", "tile64dma",
+                                                                   "tile32dma"]
                                            for tA, tB in _layouts_of(v)])
 def test_ragged_sweep(variant, tA, tB):
     rng = np.random.default_rng(1000 + 10 * tA + tB + {"tile128": 0, "tile256": 100, "tile256w8": 200, "tile256dma": 300,
                                                        "tile128dma": 400, "tile128dma_sk": 500,
-                                                       "tile64dma": 600}[variant])
+                                                       "tile64dma": 600, "tile32dma": 700}[variant])
     for it in range(6):
         M, N, K = (int(x) for x in rng.choice(RAGGED, 3))
         r8 = lambda x: (x + 7) // 8 * 8
         if variant in ("tile256", "tile256w8"):     # 128-bit register-staged loads: every extent % 8 == 0
             M, N, K = r8(M), r8(N), r8(K)
-        elif variant in ("tile256dma", "tile128dma", "tile128dma_sk", "tile64dma"):   # only M/N-contiguous rows need % 8 == 0
+        elif variant in ("tile256dma", "tile128dma", "tile128dma_sk", "tile64dma", "tile32dma"):   # only M/N-contiguous rows need % 8 == 0
             M = r8(M) if tA else M
             N = N if tB else r8(N)
         ab = "f16" if it % 2 == 0 else "bf16"
@@ -149,7 +150,8 @@ def test_ragged_sweep(variant, tA, tB):
         _full_check(case, variant=variant, guard=1024)
 
 
-@pytest.mark.parametrize("variant,tA,tB", [(v, tA, tB) for v in ["tile256dma", "tile128dma", "tile128dma_sk", "tile64dma"]
+@pytest.mark.parametrize("variant,tA,tB", [(v, tA, tB) for v in ["tile256dma", "tile128dma", "tile128dma_sk", "tile64dma",
+                                                                   "tile32dma"]
                                            for tA, tB in _layouts_of(v, ((0, 0), (0, 1), (1, 1)))])
 def test_direct_loads_unaligned_k_and_base(variant, tA, tB):
     """K-contiguous operands at any K and at a base address 2 bytes off 16-byte alignment:
@@ -177,7 +179,7 @@ def test_skinny_rows(M):
 def test_accumulate_onto_c():
     for variant, tB in (("tile128", 0), ("tile256", 0), ("tile256w8", 0), ("tile256dma", 0), ("tile256dma", 1),
                         ("tile128dma", 0), ("tile128dma", 1), ("tile128dma_sk", 0), ("tile128dma_sk", 1),
-                        ("tile64dma", 0), ("tile64dma", 1),
+                        ("tile64dma", 0), ("tile64dma", 1), ("tile32dma", 0), ("tile32dma", 1),
                         ("skinny", 1)):
         for c in ("f16", "f32"):
             case = W.GemmCase(f"accum-{variant}-{c}", 16 if variant == "skinny" else 264, 200, 136,
@@ -295,14 +297,14 @@ def test_zero_padding_invariant_on_gpu():
                                    (264, 136, 640, 1, 1)])
 def test_ring_depths_and_tilings_bit_identical(shape):
     """The direct-load kernels with a 2-slot ring of 64-wide K tiles (256x256 tiles), a
-    4-slot ring of 64-wide K tiles (128x128), a 3-slot ring of 128-wide K tiles (64x128)
-    and the persistent schedule with whole tiles all form every output's fp32 sum from
-    the same MFMA 16x16x32 steps in ascending K: their results must be bit-identical (a
-    dropped, repeated or reordered K tile in any ring shows up here)."""
+    4-slot ring of 64-wide K tiles (128x128) and 3-slot rings of 128-wide K tiles (64x128
+    with 8 waves, 32x128 with 4) all form every output's fp32 sum from the same MFMA
+    16x16x32 steps in ascending K: their results must be bit-identical (a dropped,
+    repeated or reordered K tile in any ring shows up here)."""
     M, N, K, tA, tB = shape
     case = W.GemmCase(f"ringsweep-{M}x{N}x{K}", M, N, K, transpose_A=tA, transpose_B=tB, relu=1, seed=4950)
     A, B, _ = W.make_inputs(case)
-    variants = ["tile256dma", "tile128dma"] + ([] if tA else ["tile64dma"])
+    variants = ["tile256dma", "tile128dma"] + ([] if tA else ["tile64dma", "tile32dma"])
     outs = {}
     for v in variants:
         C, plan, _, _ = run_gpu(case, A, B, None, variant=v)

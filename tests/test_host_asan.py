@@ -41,6 +41,7 @@ namespace tlg {
 #define STUB(name) hipError_t name(const GemmParams&, int, int, hipStream_t) { return hipErrorInvalidValue; }
 STUB(launch_lds_f16) STUB(launch_lds_bf16) STUB(launch_lds128_f16) STUB(launch_lds128_bf16)
 STUB(launch_lds128sk_f16) STUB(launch_lds128sk_bf16) STUB(launch_lds64_f16) STUB(launch_lds64_bf16)
+STUB(launch_lds32_f16) STUB(launch_lds32_bf16)
 STUB(launch_lds_sk2_f16) STUB(launch_lds_sk2_bf16) STUB(launch_lds128_sk2_f16) STUB(launch_lds128_sk2_bf16)
 #define STUB6(name) hipError_t name(const GemmParams&, int, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
 STUB6(launch_tile_256_f16) STUB6(launch_tile_256_bf16) STUB6(launch_tile_256w8_f16) STUB6(launch_tile_256w8_bf16)

@@ -25,7 +25,7 @@ F16, BF16, F32, E4M3, E5M2, E2M1 = 1, 2, 3, 4, 5, 6
 _TORCH_TO_CODE = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32,
                   torch.float8_e4m3fn: E4M3, torch.float8_e5m2: E5M2, torch.float4_e2m1fn_x2: E2M1}
 VARIANTS = {"auto": 0, "tile256": 1, "tile128": 2, "skinny": 3, "empty": 4, "tile256w8": 5,
-            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8, "mx256": 9, "tile64dma": 10,
+            "tile256dma": 6, "tile128dma": 7, "tile128dma_sk": 8, "mx256": 9, "tile64dma": 10, "tile32dma": 13,
             "tile256dma_streamk": 11, "tile128dma_streamk": 12}
 EPILOGUES = {"none": 0, "relu": 1}
 

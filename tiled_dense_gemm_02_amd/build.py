@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libtlg.so")
 
 SOURCES = ["gemm_tile_256_f16.hip", "gemm_tile_256_bf16.hip", "gemm_tile_256w8_f16.hip",
            "gemm_tile_256w8_bf16.hip", "gemm_tile_128_f16.hip", "gemm_tile_128_bf16.hip",
-           "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "gemm_lds_sk2_f16.hip", "gemm_lds_sk2_bf16.hip", "gemm_mx.hip", "attn_fwd.hip", "gemm_w4.hip", "gemm_sp.hip", "gemm_skinny.hip", "tlg_api.cpp"]
+           "gemm_lds_f16.hip", "gemm_lds_bf16.hip", "gemm_lds_sk2_f16.hip", "gemm_lds_sk2_bf16.hip", "gemm_lds32.hip", "gemm_mx.hip", "attn_fwd.hip", "gemm_w4.hip", "gemm_sp.hip", "gemm_skinny.hip", "tlg_api.cpp"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function"]

@@ -82,6 +82,7 @@ const char* variant_name(int v)
     case TLG_VARIANT_TILE_64_DMA: return "tile64dma";
     case TLG_VARIANT_TILE_256_DMA_STREAMK: return "tile256dma_streamk";
     case TLG_VARIANT_TILE_128_DMA_STREAMK: return "tile128dma_streamk";
+    case TLG_VARIANT_TILE_32_DMA: return "tile32dma";
     default: return "?";
     }
 }
@@ -147,6 +148,9 @@ bool skinny_pays(int64_t M, int64_t N, int64_t K)
 
 bool is_streamk(int v) { return v == TLG_VARIANT_TILE_256_DMA_STREAMK || v == TLG_VARIANT_TILE_128_DMA_STREAMK; }
 
+// The direct-load variants with K tiles of 128 and 128-column tiles (64 x 128, 32 x 128).
+bool is_narrow_dma(int v) { return v == TLG_VARIANT_TILE_64_DMA || v == TLG_VARIANT_TILE_32_DMA; }
+
 // Persistent grid of the stream-K variants: one workgroup per CU of an MI355X
 // (each takes 128 KiB of LDS, so one fits a CU).
 constexpr int kPersistentGrid = 256;
@@ -197,7 +201,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         return TLG_ERR_INVALID_ARG;
     if (c != TLG_F16 && c != TLG_BF16 && c != TLG_F32) return TLG_ERR_INVALID_ARG;
     if (ab == TLG_F32) return TLG_ERR_UNSUPPORTED;
-    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_128_DMA_STREAMK || forced == TLG_VARIANT_EMPTY)
+    if (forced < TLG_VARIANT_AUTO || forced > TLG_VARIANT_TILE_32_DMA || forced == TLG_VARIANT_EMPTY)
         return TLG_ERR_INVALID_ARG;
     if (is_mx(ab)) {
         // Block-scaled FP8 / FP4: A stored [M, K], B stored [N, K], K a multiple of
@@ -252,15 +256,14 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         if ((forced == TLG_VARIANT_TILE_256 || forced == TLG_VARIANT_TILE_256_W8) && (va != 8 || vb != 8))
             return TLG_ERR_UNSUPPORTED;
         if ((forced == TLG_VARIANT_TILE_256_DMA || forced == TLG_VARIANT_TILE_128_DMA ||
-             forced == TLG_VARIANT_TILE_128_DMA_SPLITK || forced == TLG_VARIANT_TILE_64_DMA ||
-             is_streamk(forced)) && !dma_ok)
+             forced == TLG_VARIANT_TILE_128_DMA_SPLITK || is_narrow_dma(forced) || is_streamk(forced)) && !dma_ok)
             return TLG_ERR_UNSUPPORTED;
-        if (forced == TLG_VARIANT_TILE_64_DMA && tA) return TLG_ERR_UNSUPPORTED;
-        // Its K tiles are 128 rows of k: with B stored [K,N] a lane's direct-load
+        if (is_narrow_dma(forced) && tA) return TLG_ERR_UNSUPPORTED;
+        // Their K tiles are 128 rows of k: with B stored [K,N] a lane's direct-load
         // offset reaches 127 rows of 2N bytes (plus a chunk), which must stay below
         // 2^31 (offsets from 2^31 up read as out of range).  The automatic choice
-        // takes this variant only for N <= 128 * 128.
-        if (forced == TLG_VARIANT_TILE_64_DMA && !tB && 127 * 2 * N + 256 > (int64_t)INT32_MAX)
+        // takes these variants only for N <= 128 * 128.
+        if (is_narrow_dma(forced) && !tB && 127 * 2 * N + 256 > (int64_t)INT32_MAX)
             return TLG_ERR_UNSUPPORTED;
     } else if (M <= kSkinnyMaxRows && skinny_ok && skinny_pays(M, N, K)) {
         variant = TLG_VARIANT_SKINNY;
@@ -272,7 +275,9 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         // most 128 tiles of 128x128 and A stored [M,K]: 64x128 tiles, twice the
         // workgroups in one wave (measured on MI355X: 1024^3 13.5 -> 10.0 us,
         // 1000x1500x777 bf16 13.5 -> 10.8 us; at 2048^3, 256 tiles of 128x128,
-        // they are 1.5x slower).
+        // they are 1.5x slower), or 32x128 tiles where those still fit one wave of
+        // 256 workgroups (1024^3 10.65 -> 10.14 us, 256^3 5.18 -> 4.87 us; with 384
+        // of them, 1024x1536x1024, 9.8 -> 15.6 us).
         //
         // Once 256x256 tiles fill at least half the chip, the wave count decides
         // between the two tile sizes: a wave of 128x128 tiles costs about 0.37 of a
@@ -292,7 +297,8 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         else if (t128 < 128 && kt >= kSplitMinKTiles && choose_splits(t128, kt) >= 2)
             variant = TLG_VARIANT_TILE_128_DMA_SPLITK;
         else if (t128 <= 128 && !tA)
-            variant = TLG_VARIANT_TILE_64_DMA;
+            variant = ceil_div(M, kLds32BM) * ceil_div(N, kLds32BN) <= 256 ? TLG_VARIANT_TILE_32_DMA
+                                                                          : TLG_VARIANT_TILE_64_DMA;
         else
             variant = TLG_VARIANT_TILE_128_DMA;
     } else {
@@ -314,10 +320,10 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         }
     }
     if (is_tile(variant) || variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
-        variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA || is_streamk(variant)) {
+        variant == TLG_VARIANT_TILE_128_DMA_SPLITK || is_narrow_dma(variant) || is_streamk(variant)) {
         const int64_t b = (variant == TLG_VARIANT_TILE_256 || variant == TLG_VARIANT_TILE_256_W8 ||
                            variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_256_DMA_STREAMK) ? 256 : 128;
-        const int64_t bm = variant == TLG_VARIANT_TILE_64_DMA ? kLds64BM : b;
+        const int64_t bm = variant == TLG_VARIANT_TILE_64_DMA ? kLds64BM : variant == TLG_VARIANT_TILE_32_DMA ? kLds32BM : b;
         if (ceil_div(M, bm) * ceil_div(N, b) * splits > INT32_MAX) return TLG_ERR_INVALID_ARG;
     } else if (variant == TLG_VARIANT_SKINNY) {
         const int mr = skinny_rows(M);
@@ -328,8 +334,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
     p->ab = ab; p->c = c; p->tA = tA; p->tB = tB; p->clear = clear; p->relu = epi == TLG_EPI_RELU;
     p->variant = variant;
     const bool dma = variant == TLG_VARIANT_TILE_256_DMA || variant == TLG_VARIANT_TILE_128_DMA ||
-                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK || variant == TLG_VARIANT_TILE_64_DMA ||
-                     is_streamk(variant);
+                     variant == TLG_VARIANT_TILE_128_DMA_SPLITK || is_narrow_dma(variant) || is_streamk(variant);
     p->vec_a = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : va;
     p->vec_b = (variant == TLG_VARIANT_SKINNY || dma) ? 8 : vb;
     if (dma) {
@@ -397,6 +402,13 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         in.grid = ceil_div(M, kLds64BM) * ceil_div(N, kLds64BN);
         in.lds_bytes = (int64_t)kLds64Stages * (kLds64BM + kLds64BN) * kLds64BK * 2;
         in.k_tiles = (int32_t)ceil_div(K, kLds64BK);
+    } else if (variant == TLG_VARIANT_TILE_32_DMA) {
+        in.block_m = kLds32BM; in.block_n = kLds32BN; in.block_k = kLds32BK;
+        in.stages = kLds32Stages;
+        in.threads = kLds32Threads;
+        in.grid = ceil_div(M, kLds32BM) * ceil_div(N, kLds32BN);
+        in.lds_bytes = (int64_t)kLds32Stages * (kLds32BM + kLds32BN) * kLds32BK * 2;
+        in.k_tiles = (int32_t)ceil_div(K, kLds32BK);
     } else if (variant == TLG_VARIANT_SKINNY) {
         const int mr = skinny_rows(M), nb = skinny_cols(mr);
         const int64_t tiles = ceil_div(M, mr) * ceil_div(N, nb);
@@ -578,6 +590,11 @@ tlg_status launch_plan(const tlg_gemm_s& p, const void* A, const void* B, void* 
         gp.tiles_n = (int)ceil_div(p.N, kLds64BN);
         err = p.ab == TLG_F16 ? launch_lds64_f16(gp, p.tA, p.tB, (hipStream_t)stream)
                               : launch_lds64_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
+    } else if (p.variant == TLG_VARIANT_TILE_32_DMA) {
+        gp.tiles_m = (int)ceil_div(p.M, kLds32BM);
+        gp.tiles_n = (int)ceil_div(p.N, kLds32BN);
+        err = p.ab == TLG_F16 ? launch_lds32_f16(gp, p.tA, p.tB, (hipStream_t)stream)
+                              : launch_lds32_bf16(gp, p.tA, p.tB, (hipStream_t)stream);
     } else if (p.variant == TLG_VARIANT_TILE_128_DMA_SPLITK) {
         gp.tiles_m = (int)ceil_div(p.M, kLds128BM);
         gp.tiles_n = (int)ceil_div(p.N, kLds128BN);
@@ -909,7 +926,8 @@ struct TuneCandidate {
 std::vector<TuneCandidate> tune_space(int64_t M, int64_t N)
 {
     std::vector<TuneCandidate> c = {{TLG_VARIANT_TILE_256_DMA, 0}, {TLG_VARIANT_TILE_128_DMA, 0},
-                                    {TLG_VARIANT_TILE_64_DMA, 0},  {TLG_VARIANT_SKINNY, 0},
+                                    {TLG_VARIANT_TILE_64_DMA, 0},  {TLG_VARIANT_TILE_32_DMA, 0},
+                                    {TLG_VARIANT_SKINNY, 0},
                                     {TLG_VARIANT_TILE_256_W8, 0},  {TLG_VARIANT_TILE_256, 0},
                                     {TLG_VARIANT_TILE_128, 0}};
     c.push_back({TLG_VARIANT_TILE_256_DMA_STREAMK, 0});

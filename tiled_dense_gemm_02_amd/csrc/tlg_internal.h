@@ -98,26 +98,31 @@ inline hipError_t launch_tile(int cfg, const GemmParams& p, int ab_dtype, int tr
 }
 hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
 
-// Direct-load ring kernels (8 waves, 128-bit loads only): 256x256x64 tiles with
-// a 2-slot ring, and 128x128x64 tiles with a 4-slot ring for grids too small to
-// fill the chip with 256x256 tiles.
+// Direct-load ring kernels (128-bit loads only): 256x256x64 tiles with a 2-slot
+// ring, and 128x128x64 tiles with a 4-slot ring for grids too small to fill the
+// chip with 256x256 tiles (8 waves each); 64x128x128 (8 waves) and 32x128x128
+// (4 waves) tiles with 3-slot rings for smaller grids still.
 constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64, kLdsStages = 2, kLdsThreads = 512;
 constexpr int kLds128BM = 128, kLds128BN = 128, kLds128Stages = 4;
 constexpr int kLds64BM = 64, kLds64BN = 128, kLds64BK = 128, kLds64Stages = 3;
+constexpr int kLds32BM = 32, kLds32BN = 128, kLds32BK = 128, kLds32Stages = 3, kLds32Threads = 256;
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128sk_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128sk_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
-// 64 x 128 tiles; A must be K-contiguous (transpose_A == 0).
 // Persistent stream-K schedules of the 256 x 256 and 128 x 128 kernels.
 hipError_t launch_lds_sk2_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds_sk2_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_sk2_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_sk2_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+// 64 x 128 tiles; A must be K-contiguous (transpose_A == 0).
 hipError_t launch_lds64_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds64_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+// 32 x 128 tiles (4 waves); A must be K-contiguous (transpose_A == 0).
+hipError_t launch_lds32_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
+hipError_t launch_lds32_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 
 // Block-scaled FP8 GEMM (gemm_mx.hip).  A [M,K], B [N,K] FP8 bytes; SA [M,K/32],
 // SB [N,K/32] E8M0 bytes; K % 128 == 0.
