@@ -276,7 +276,7 @@ tlg_status plan_build(tlg_gemm_s* p, int64_t M, int64_t N, int64_t K, int ab, in
         // workgroups in one wave (measured on MI355X: 1024^3 13.5 -> 10.0 us,
         // 1000x1500x777 bf16 13.5 -> 10.8 us; at 2048^3, 256 tiles of 128x128,
         // they are 1.5x slower), or 32x128 tiles where those still fit one wave of
-        // 256 workgroups (1024^3 10.65 -> 10.14 us, 256^3 5.18 -> 4.87 us; with 384
+        // 256 workgroups (1024^3 10.5 -> 9.6 us, 256^3 5.17 -> 4.62 us; with 384
         // of them, 1024x1536x1024, 9.8 -> 15.6 us).
         //
         // Once 256x256 tiles fill at least half the chip, the wave count decides
