@@ -339,6 +339,15 @@ tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, in
                         void *stream);
 
 /*
+ * The number of queries one workgroup of tlg_attn_fwd takes for this shape
+ * (host only, no device needed): 128, or 64 when blocks of 128 queries would
+ * number at most 256 over all (batch, head) pairs (a grid too small to give
+ * every CU a workgroup).  The choice changes no result: every query's sums are
+ * formed in the same order either way.  0 for a non-positive size.
+ */
+int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads);
+
+/*
  * Dequant GEMM with 4-bit weights: the "dequant GEMM" of the overview page's
  * table of representative operators (load packed weights, apply scale and zero
  * point, convert, then multiply).  Shaped for decoding (few rows of A, one

@@ -339,6 +339,19 @@ def test_attention_validation_happens_before_any_launch():
         tlg.attention(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
 
 
+def test_attention_query_block_rule():
+    """64 queries per workgroup while blocks of 128 would number at most 256 over all
+    (batch, head) pairs, else 128 (host only)."""
+    qb = tlg.attention_query_block
+    assert qb(1, 1024, 8) == 64          # the page's instance: 8 x 8 = 64 blocks of 128
+    assert qb(2, 777, 3) == 64           # 7 x 3 x 2 = 42
+    assert qb(1, 2048, 16) == 64         # 16 x 16 = 256
+    assert qb(1, 2049, 16) == 128        # 17 x 16 = 272
+    assert qb(4, 4096, 32) == 128
+    assert qb(1, 1, 1) == 64
+    assert qb(0, 64, 2) == 0 and qb(1, 0, 2) == 0 and qb(1, 64, -1) == 0
+
+
 def test_dequant_and_sparse_validation_happens_before_any_launch():
     """tlg_gemm_w4 and tlg_gemm_sp reject bad requests with distinct statuses before
     touching a device (these pointers are never dereferenced)."""

@@ -94,6 +94,8 @@ def load_library():
         lib.tlg_gemm_tune.restype = i32
         lib.tlg_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_float, vp]
         lib.tlg_attn_fwd.restype = i32
+        lib.tlg_attn_query_block.argtypes = [i64, i64, i64]
+        lib.tlg_attn_query_block.restype = i32
         lib.tlg_gemm_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp]
         lib.tlg_gemm_w4.restype = i32
         lib.tlg_gemm_sp.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
@@ -410,6 +412,12 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor
     if st != 0:
         raise TlgError("tlg_attn_fwd", st)
     return O
+
+
+def attention_query_block(batch: int, seq: int, heads: int) -> int:
+    """Queries per workgroup that attention would use for this shape (tlg_attn_query_block;
+    host only): 128, or 64 for grids of at most 256 blocks of 128 queries."""
+    return int(load_library().tlg_attn_query_block(int(batch), int(seq), int(heads)))
 
 
 def attention_ptrs(q: int, k: int, v: int, o: int, batch: int, seq: int, heads: int, dim: int, dtype, causal: int,

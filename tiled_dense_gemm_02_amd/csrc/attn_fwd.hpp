@@ -15,10 +15,13 @@
 // bf16, 16-byte aligned; element (b, t, h, d) sits at ((b*S + t)*H + h)*D + d.
 //
 // gfx950 mapping.
-//   - Workgroup: 4 waves, 128 queries (32 per wave: two 16-row MFMA tiles).  Q
-//     fragments are loaded once into registers.  Key blocks of 64 keys (K and V
-//     tiles) stream through a two-slot LDS ring filled by global->LDS direct
-//     loads; the loads of block j+1 are in flight while block j is computed.
+//   - Workgroup: 4 waves, 128 queries (32 per wave: two 16-row MFMA tiles), or
+//     64 queries (16 per wave, one row tile) for grids that would not give every
+//     CU a workgroup: each wave's chain per key block (scores, softmax, P V) is
+//     then half as long, and twice the workgroups share the work.  Q fragments
+//     are loaded once into registers.  Key blocks of 64 keys (K and V tiles)
+//     stream through a two-slot LDS ring filled by global->LDS direct loads; the
+//     loads of block j+1 are in flight while block j is computed.
 //   - Both products run on v_mfma_f32_16x16x32 with the key-side operand first,
 //     so the score tile lands as S[q][key] with lane l holding query l%16 and
 //     keys 4(l/16)..+3 of each 16-key tile.  That is already the A-operand
@@ -116,11 +119,13 @@ __device__ inline float round_op(float x, uint32_t& bits)
 }
 
 // NEG: the softmax scale is negative (the row maximum of the scaled scores is
-// then the scale times the row minimum of the raw scores).
-template <int D, int T, bool CAUSAL, bool NEG>
+// then the scale times the row minimum of the raw scores).  RT: 16-row tiles of
+// queries per wave (2: 128 queries per workgroup, 1: 64).
+template <int D, int T, bool CAUSAL, bool NEG, int RT>
 __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 {
-    constexpr int BM = 128, BN = 64, NW = 4, WROWS = 32;
+    constexpr int NW = 4, WROWS = 16 * RT, BM = NW * WROWS, BN = 64;
+    static_assert(RT == 1 || RT == 2, "one or two 16-row query tiles per wave");
     using Lay = AttnLds<D>;
     constexpr int RB = Lay::RB, CH = Lay::CH, RPK = Lay::RPK;
     constexpr int TILE = BN * RB;                 // bytes of one K (or V) tile
@@ -153,12 +158,12 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
     const int q_last = min(q0 + BM, S) - 1;
     const int nkb = CAUSAL ? q_last / BN + 1 : (S + BN - 1) / BN;
 
-    // Q fragments of this wave's 32 rows (rows past S read as zeros).
-    u32x4 qf[2][KS];
+    // Q fragments of this wave's rows (rows past S read as zeros).
+    u32x4 qf[RT][KS];
     {
         const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char*)p.Q + head_off, head_bytes);
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
             const int q = q0 + wave * WROWS + rt * 16 + r16;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -199,15 +204,17 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
         }
     };
 
-    f32x4 oacc[2][DT];
-    f32x4 lacc[2];                       // row sums of P (all four entries equal)
+    f32x4 oacc[RT][DT];
+    f32x4 lacc[RT];                       // row sums of P (all four entries equal)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    float m_run[2] = {-INFINITY, -INFINITY};
+    float m_run[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) m_run[rt] = -INFINITY;
     // All-ones operand: P times it gives the row sums of the rounded P on the
     // matrix cores, exactly as the page sums its fp16 probability tile.
     const uint32_t one2 = T == DT_F16 ? 0x3C003C00u : 0x3F803F80u;
@@ -230,9 +237,9 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
             const char* kt_base = smem + (kb & 1) * SLOT;
             const char* vt_base = kt_base + TILE;
 
-            f32x4 sacc[2][4];
+            f32x4 sacc[RT][4];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) sacc[rt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
             // K fragments of step ks+1 are read while step ks's 8 MFMAs run (two
@@ -255,16 +262,16 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) sacc[rt][kt] = mfma16x16x32<T>(kf[ks & 1][kt], qf[rt][ks], sacc[rt][kt]);
+                    for (int rt = 0; rt < RT; ++rt) sacc[rt][kt] = mfma16x16x32<T>(kf[ks & 1][kt], qf[rt][ks], sacc[rt][kt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
 
             const bool need_mask = (kb0 + BN > S) || (CAUSAL && kb0 + BN - 1 > wq0);
-            u32x4 pf[2][2];
-            float alpha[2];
+            u32x4 pf[RT][2];
+            float alpha[RT];
             bool rescale = false;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int rt = 0; rt < RT; ++rt) {
                 const int q = wq0 + rt * 16 + r16;
                 // Score t of this lane is key kb0 + 4g + 16(t/4) + t%4; it is masked
                 // when that key lies past the row's last allowed key.
@@ -313,7 +320,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
             // maximum moved (alpha is exactly 1 for the others).
             if (__any(rescale)) {
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) lacc[rt][e] *= alpha[rt];
 #pragma unroll
@@ -323,7 +330,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
                 }
             }
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) lacc[rt] = mfma16x16x32<T>(ones, pf[rt][kk], lacc[rt]);
 
@@ -352,7 +359,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
+                    for (int rt = 0; rt < RT; ++rt)
                         oacc[rt][dt] = mfma16x16x32<T>(vfr[dt % (VPD + 1)][kk], pf[rt][kk], oacc[rt][dt]);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -370,7 +377,7 @@ __global__ void __launch_bounds__(256, 2) attn_fwd_kernel(AttnParams p)
     // bytes of a head).
     static_assert(DT % 2 == 0, "pairs of 16-dim blocks");
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
         const int q = wq0 + rt * 16 + r16;
         const float inv = 1.0f / lacc[rt][0];
         if (q >= S) continue;

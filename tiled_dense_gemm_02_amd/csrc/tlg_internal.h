@@ -148,7 +148,8 @@ struct AttnParams {
     void* O;
     int B, S, H;
     float scale_log2;   // softmax scale * log2(e)
-    int nqb;            // query blocks of 128 per (batch, head)
+    int block_q;        // queries per workgroup: 128 or 64
+    int nqb;            // query blocks of block_q per (batch, head)
 };
 hipError_t launch_attn(const AttnParams& p, int dim, int dtype, int causal, hipStream_t stream);
 
