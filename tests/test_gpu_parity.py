@@ -53,7 +53,9 @@ def test_config1_relu_256():
 
 def test_config2_1024():
     plan = _full_check(W.CONFIGS["c2"])
-    assert plan.info.block_k == 128 and plan.info.k_tiles == 8     # 64x128 tiles take K in tiles of 128
+    assert plan.info.block_m == 32 and plan.info.block_k == 128 and plan.info.k_tiles == 8   # 32x128 tiles, K in tiles of 128
+    plan = _full_check(W.CONFIGS["c2"], variant="tile64dma")
+    assert plan.info.block_m == 64 and plan.info.k_tiles == 8
     plan = _full_check(W.CONFIGS["c2"], variant="tile128dma")
     assert plan.info.k_tiles == 16          # 1024 / 64, the pages' K trip count
     plan = _full_check(W.CONFIGS["c2"], variant="tile128dma_sk")
