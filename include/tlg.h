@@ -348,6 +348,16 @@ tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, in
 int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads);
 
 /*
+ * As tlg_attn_fwd, with the number of queries per workgroup given: block_q = 64
+ * or 128, or 0 for the choice of tlg_attn_query_block (tlg_attn_fwd is this call
+ * with 0).  O does not depend on it; it is there for tests and tuning.  Returns
+ * TLG_ERR_INVALID_ARG for any other block_q, else as tlg_attn_fwd.
+ */
+tlg_status tlg_attn_fwd_block(const void *Q, const void *K, const void *V, void *O, int64_t batch,
+                              int64_t seq, int64_t heads, int64_t dim, int32_t dtype, int32_t causal,
+                              float softmax_scale, int32_t block_q, void *stream);
+
+/*
  * Dequant GEMM with 4-bit weights: the "dequant GEMM" of the overview page's
  * table of representative operators (load packed weights, apply scale and zero
  * point, convert, then multiply).  Shaped for decoding (few rows of A, one

@@ -335,6 +335,12 @@ def test_attention_validation_happens_before_any_launch():
     assert f(None, p, p, p, 1, 64, 2, 64, 1, 1, 0.125, None) == -3
     assert f(p + 8, ok[1], ok[2], ok[3], 1, 64, 2, 64, 1, 1, 0.125, None) == -4
     assert f(p, ok[1], ok[2], p + 4096, 1, 64, 2, 64, 1, 1, 0.125, None) == -1   # O overlaps Q
+    fb = lib.tlg_attn_fwd_block                          # the same checks, and the block size
+    assert fb(*ok, 1, 64, 2, 64, 1, 1, 0.125, 96, None) == -1
+    assert fb(*ok, 1, 64, 2, 64, 1, 1, 0.125, -64, None) == -1
+    assert fb(*ok, 1, 64, 2, 96, 1, 1, 0.125, 64, None) == -2
+    assert fb(None, None, None, None, 0, 64, 2, 64, 1, 1, 0.125, 128, None) == 0
+    assert fb(p + 8, ok[1], ok[2], ok[3], 1, 64, 2, 64, 1, 1, 0.125, 64, None) == -4
     with pytest.raises(ValueError):
         tlg.attention(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
 

@@ -264,6 +264,29 @@ def test_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("shape", [(1, 200, 2, 64, 1, "f16"), (2, 777, 3, 128, 0, "f16"), (1, 1024, 4, 128, 1, "bf16"),
+                                   (3, 129, 5, 64, 0, "bf16"), (1, 4096, 2, 64, 1, "f16")])
+def test_query_blocks_of_64_and_128_bit_identical(shape):
+    """Workgroups of 64 or 128 queries form every query's sums in the same order (the same
+    key blocks, MFMA steps and reference-maximum moves): their outputs must be equal bit for
+    bit, and the automatic choice must be one of them."""
+    import tiled_dense_gemm_02_amd as tlg
+    B, S, H, D, causal, dtype = shape
+    case = W.AttnCase(f"qblock-{B}x{S}x{H}x{D}-c{causal}-{dtype}", B, S, H, D, causal=causal, dtype=dtype, seed=1430)
+    log(f"[case] {case.name}")
+    dev = _device()
+    q, k, v = (t.to(dev) for t in W.make_attn_inputs(case))
+    outs = {}
+    for bq in (64, 128, 0):
+        outs[bq] = tlg.attention(q, k, v, causal=bool(causal), block_q=bq)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[64].view(torch.int16), outs[128].view(torch.int16))
+    assert torch.equal(outs[0].view(torch.int16), outs[64].view(torch.int16))
+    o = O.attn(B, S, H, D, W.bits16(q.cpu()), W.bits16(k.cpu()), W.bits16(v.cpu()), dtype=dtype, causal=causal)
+    gpu = O.decode(W.bits16(outs[0].cpu()), dtype).reshape(o.shape)
+    _check(case, gpu, o, float(v.float().abs().max()))
+
+
 def test_error_paths_enqueue_nothing():
     import tiled_dense_gemm_02_amd as tlg
     dev = _device()

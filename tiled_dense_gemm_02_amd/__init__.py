@@ -94,6 +94,8 @@ def load_library():
         lib.tlg_gemm_tune.restype = i32
         lib.tlg_attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_float, vp]
         lib.tlg_attn_fwd.restype = i32
+        lib.tlg_attn_fwd_block.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_float, i32, vp]
+        lib.tlg_attn_fwd_block.restype = i32
         lib.tlg_attn_query_block.argtypes = [i64, i64, i64]
         lib.tlg_attn_query_block.restype = i32
         lib.tlg_gemm_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp]
@@ -380,9 +382,10 @@ def gemm_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *, transpose
 
 
 def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor | None = None, *,
-              causal: bool = True, scale: float | None = None, stream=None) -> torch.Tensor:
+              causal: bool = True, scale: float | None = None, block_q: int = 0, stream=None) -> torch.Tensor:
     """Attention forward with online softmax (tlg_attn_fwd) on [batch, seq, heads, dim]
     device tensors of fp16 or bf16 (dim 64 or 128).  scale defaults to 1/sqrt(dim).
+    block_q: queries per workgroup, 64 or 128 (0: the library's choice; tlg_attn_fwd_block).
     Returns O (allocated when not given)."""
     for name, t in (("Q", Q), ("K", K), ("V", V)):
         if not isinstance(t, torch.Tensor):
@@ -406,11 +409,11 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor
     s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     lib = load_library()
     with torch.cuda.device(Q.device):
-        st = lib.tlg_attn_fwd(Q.data_ptr() or None, K.data_ptr() or None, V.data_ptr() or None,
-                              O.data_ptr() or None, B, S, H, D, _code(Q.dtype), int(bool(causal)), sc,
-                              ctypes.c_void_p(s))
+        st = lib.tlg_attn_fwd_block(Q.data_ptr() or None, K.data_ptr() or None, V.data_ptr() or None,
+                                    O.data_ptr() or None, B, S, H, D, _code(Q.dtype), int(bool(causal)), sc,
+                                    int(block_q), ctypes.c_void_p(s))
     if st != 0:
-        raise TlgError("tlg_attn_fwd", st)
+        raise TlgError("tlg_attn_fwd_block", st)
     return O
 
 

@@ -769,9 +769,11 @@ int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads)
     return blocks128 * heads * batch <= 256 ? 64 : 128;
 }
 
-tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t seq,
-                        int64_t heads, int64_t dim, int32_t dtype, int32_t causal, float softmax_scale, void* stream)
+tlg_status tlg_attn_fwd_block(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t seq,
+                              int64_t heads, int64_t dim, int32_t dtype, int32_t causal, float softmax_scale,
+                              int32_t block_q, void* stream)
 {
+    if (block_q != 0 && block_q != 64 && block_q != 128) return TLG_ERR_INVALID_ARG;
     if (batch < 0 || seq < 0 || heads < 0 || dim <= 0) return TLG_ERR_INVALID_ARG;
     if (!flag_ok(causal) || !std::isfinite(softmax_scale)) return TLG_ERR_INVALID_ARG;
     if (dtype != TLG_F16 && dtype != TLG_BF16) {
@@ -782,8 +784,8 @@ tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, in
     if (batch == 0 || seq == 0 || heads == 0) return TLG_OK;
     const uint64_t per_batch = (uint64_t)seq * (uint64_t)heads * (uint64_t)dim * 2u;
     if (per_batch >= (uint64_t(1) << 31)) return TLG_ERR_UNSUPPORTED;
-    const int64_t block_q = tlg_attn_query_block(batch, seq, heads);
-    const int64_t nqb = ceil_div(seq, block_q);
+    const int64_t bq = block_q ? block_q : tlg_attn_query_block(batch, seq, heads);
+    const int64_t nqb = ceil_div(seq, bq);
     if (batch > INT32_MAX || nqb * heads > INT32_MAX || nqb * heads * batch > INT32_MAX) return TLG_ERR_UNSUPPORTED;
     if (!Q || !K || !V || !O) return TLG_ERR_NULL;
     const uintptr_t q = (uintptr_t)Q, k = (uintptr_t)K, v = (uintptr_t)V, o = (uintptr_t)O;
@@ -795,10 +797,16 @@ tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, in
     ap.Q = Q; ap.K = K; ap.V = V; ap.O = O;
     ap.B = (int)batch; ap.S = (int)seq; ap.H = (int)heads;
     ap.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);   // log2(e)
-    ap.block_q = (int)block_q;
+    ap.block_q = (int)bq;
     ap.nqb = (int)nqb;
     const hipError_t err = launch_attn(ap, (int)dim, dtype == TLG_F16 ? DT_F16 : DT_BF16, causal, (hipStream_t)stream);
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
+}
+
+tlg_status tlg_attn_fwd(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t seq,
+                        int64_t heads, int64_t dim, int32_t dtype, int32_t causal, float softmax_scale, void* stream)
+{
+    return tlg_attn_fwd_block(Q, K, V, O, batch, seq, heads, dim, dtype, causal, softmax_scale, 0, stream);
 }
 
 tlg_status tlg_gemm_w4(const void* A, const void* Wq, const void* S, const void* Z, void* C, int64_t M, int64_t N,
