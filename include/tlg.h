@@ -75,7 +75,7 @@ typedef enum {
                                     of all but the last wave whole, then equal shares of the remaining
                                     tiles' K iterations (stream-K); the plan owns a workspace */
     TLG_VARIANT_TILE_128_DMA_STREAMK = 12, /* as 7, with the persistent stream-K schedule of 11 */
-    TLG_VARIANT_TILE_32_DMA = 13  /* 32x128x128, 8 wave64s, 3-slot ring of direct loads; A stored [M,K] only
+    TLG_VARIANT_TILE_32_DMA = 13  /* 32x128x128, 8 wave64s, 4-slot ring of direct loads; A stored [M,K] only
                                     (transpose_A == 0); grids whose 32x128 tiles fit one wave (256) */
 } tlg_variant;
 

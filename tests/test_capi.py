@@ -94,7 +94,7 @@ def test_variant_choice_and_geometry_for_the_workloads():
     # 1024^3: 64 tiles of 128x128 (too short a K to split) -> 256 tiles of 32x128, 8 K tiles of 128 each
     i = info(C["c2"])
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (13, 32, 128, 128, 256, 8)
-    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (3, 512, 3 * (32 + 128) * 128 * 2, 1, 0)
+    assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (4, 512, 4 * (32 + 128) * 128 * 2, 1, 0)
     i = info(C["c2"], "tile64dma")
     assert (i.variant, i.block_m, i.block_n, i.block_k, i.grid, i.k_tiles) == (10, 64, 128, 128, 128, 8)
     assert (i.stages, i.threads, i.lds_bytes, i.splits, i.workspace_bytes) == (3, 512, 3 * (64 + 128) * 128 * 2, 1, 0)

@@ -299,8 +299,8 @@ def test_zero_padding_invariant_on_gpu():
                                    (264, 136, 640, 1, 1)])
 def test_ring_depths_and_tilings_bit_identical(shape):
     """The direct-load kernels with a 2-slot ring of 64-wide K tiles (256x256 tiles), a
-    4-slot ring of 64-wide K tiles (128x128) and 3-slot rings of 128-wide K tiles (64x128
-    and 32x128, 8 waves each) all form every output's fp32 sum from the same MFMA
+    4-slot ring of 64-wide K tiles (128x128), a 3-slot ring of 128-wide K tiles (64x128)
+    and a 4-slot ring of 128-wide K tiles (32x128) all form every output's fp32 sum from the same MFMA
     16x16x32 steps in ascending K: their results must be bit-identical (a dropped,
     repeated or reordered K tile in any ring shows up here)."""
     M, N, K, tA, tB = shape

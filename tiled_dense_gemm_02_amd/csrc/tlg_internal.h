@@ -100,12 +100,12 @@ hipError_t launch_skinny(const GemmParams& p, int ab_dtype, hipStream_t stream);
 
 // Direct-load ring kernels (128-bit loads only): 256x256x64 tiles with a 2-slot
 // ring, and 128x128x64 tiles with a 4-slot ring for grids too small to fill the
-// chip with 256x256 tiles; 64x128x128 and 32x128x128 tiles with 3-slot rings for
-// smaller grids still (8 waves each).
+// chip with 256x256 tiles; 64x128x128 and 32x128x128 tiles with 3- and 4-slot rings
+// for smaller grids still (8 waves each).
 constexpr int kLdsBM = 256, kLdsBN = 256, kLdsBK = 64, kLdsStages = 2, kLdsThreads = 512;
 constexpr int kLds128BM = 128, kLds128BN = 128, kLds128Stages = 4;
 constexpr int kLds64BM = 64, kLds64BN = 128, kLds64BK = 128, kLds64Stages = 3;
-constexpr int kLds32BM = 32, kLds32BN = 128, kLds32BK = 128, kLds32Stages = 3, kLds32Threads = 512;
+constexpr int kLds32BM = 32, kLds32BN = 128, kLds32BK = 128, kLds32Stages = 4, kLds32Threads = 512;
 hipError_t launch_lds_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds_bf16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
 hipError_t launch_lds128_f16(const GemmParams& p, int transpose_A, int transpose_B, hipStream_t stream);
