@@ -356,6 +356,8 @@ def test_attention_query_block_rule():
     assert qb(4, 4096, 32) == 128
     assert qb(1, 1, 1) == 64
     assert qb(0, 64, 2) == 0 and qb(1, 0, 2) == 0 and qb(1, 64, -1) == 0
+    big = (1 << 62) - 1                  # products of the factors would overflow 64 bits
+    assert qb(big, big, big) == 128 and qb(1, 128, big) == 128
 
 
 def test_dequant_and_sparse_validation_happens_before_any_launch():

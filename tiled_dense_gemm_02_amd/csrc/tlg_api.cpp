@@ -765,7 +765,7 @@ int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads)
     // it gains at most 5% (causal) or loses up to 24% (non-causal, 1x4096x16x128:
     // 142 against 177 us), and 4x4096x32x{64,128} causal lose 7% and 18%.
     const int64_t blocks128 = ceil_div(seq, 128);
-    if (blocks128 > INT32_MAX || heads > INT32_MAX || batch > INT32_MAX) return 128;
+    if (blocks128 > 256 || heads > 256 || batch > 256) return 128;   // (each factor is at least 1)
     return blocks128 * heads * batch <= 256 ? 64 : 128;
 }
 
