@@ -22,7 +22,7 @@ launch and after the last one.  The mean is the headline; min / median / p90
 come from a second pass in which each launch has its own pair of events.  For the
 three target workloads the shader clock and socket power are sampled from a
 thread of this process through the amdsmi library (started before the first GPU
-call), over 1.5 s of further launches of the same workload right after the
+call), over 3 s of further launches of the same workload right after the
 timed ones (the driver refreshes the readings about once a second).
 """
 from __future__ import annotations
@@ -48,9 +48,9 @@ FLOP_PER_CLK_CU = {"f16": 4096, "bf16": 4096, "e4m3": 8192, "e5m2": 8192, "e2m1"
 PEAK_HBM_GBS = 8000.0
 WARM_MS = 100.0
 # The metrics table refreshes about once a second, so the clock window spans
-# 1.5 s of launches (one or two fresh readings); it is taken for the three target
+# 3 s of launches (about three fresh readings); it is taken for the three target
 # workloads only.
-CLOCK_MS = 1500.0
+CLOCK_MS = 3000.0
 CLOCK_WORKLOADS = ("c5a", "c3", "c5b")
 WARM_RULE = (f"W untimed launches, then more until >= {WARM_MS:.0f} ms of GPU time, then K timed launches "
              "between two HIP events on the launch stream (the mean); then K launches each between its own "
@@ -788,8 +788,8 @@ def main():
         WARM_MS = args.warm_ms
         WARM_RULE = WARM_RULE.replace(">= 100 ms", f">= {WARM_MS:g} ms")
     if args.no_clock:
+        WARM_RULE = WARM_RULE.split(f"; then {CLOCK_MS:.0f} ms")[0]
         CLOCK_MS = 0.0
-        WARM_RULE = WARM_RULE.split("; then 1500 ms")[0]
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               f"the sharding across GPUs is not built", file=sys.stderr)
