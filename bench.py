@@ -756,7 +756,7 @@ def secondary_entry(name, args, sampler, dev, log):
     return entry
 
 
-SECONDARY = ("c3", "c5b", "c2", "c4", "c1", "mx3", "mx6", "fa3", "w4a", "sp3")
+SECONDARY = ("c3", "c5b", "c2", "c4", "c1", "mx3", "mx6", "fa3", "fa1", "w4a", "sp3")
 # Oracle sample sizes: about 10 s of the oracle on 16 host threads.
 CPU_ROWS = {"c5a": 4096, "c3": 4096, "c2": 1024, "c1": 256, "c4": 1000, "c5b": 16, "mx1": 256, "mx2": 1000,
             "mx3": 2048, "mx4": 256, "mx5": 1000, "mx6": 2048}
