@@ -31,3 +31,23 @@ def test_stored_traffic_matches_current_kernel_code():
         rec = json.load(open(path))
         assert rec["kernel_hash"] == bench.kernel_hash(v), f"{w}: profile taken on other kernel code"
         assert bench.stored_traffic(w, v) == rec["traffic_bytes_per_launch"]
+
+
+def test_stored_kernel_traces_match_current_kernel_code():
+    """Every committed rocprofv3 kernel-trace summary names the kernel-source hash it was
+    taken on; that hash must be the current code's (a kernel change needs a new trace)."""
+    import glob
+    import re
+    variants = {"gemm_lds_256x256": 6, "gemm_lds_32x128": 13, "gemm_lds_64x128": 10, "gemm_mx_256x256": 9,
+                "gemm_skinny": 3, "gemm_sp_256x256": "sp", "gemm_w4": "w4", "attn_fwd": "attn"}
+    seen = 0
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        m = re.search(r"Kernel source hash \(bench\.kernel_hash\): (\w+)", open(path).read())
+        if not m:
+            continue
+        name = os.path.basename(path)
+        keys = [k for k in variants if name.startswith(k)]
+        assert len(keys) == 1, f"{name}: no kernel family for this summary"
+        assert m.group(1) == bench.kernel_hash(variants[keys[0]]), f"{name}: trace taken on other kernel code"
+        seen += 1
+    assert seen >= 10
