@@ -443,7 +443,7 @@ def measure_attn(case, steps, warmup, sampler=None, log=None, min_timed_ms=0.0):
             f"sets={nsets}")
     r = timed_launches(launch, stream, steps, warmup, sampler, sample_clock=False, min_timed_ms=min_timed_ms)
     r.update({"C": O, "nsets": nsets,
-              "describe": f"attn_fwd block={tlg.attention_query_block(case.B, case.S, case.H)}x64 threads=256 "
+              "describe": f"attn_fwd block={tlg.attention_query_block(case.B, case.S, case.H, case.D, case.causal)}x64 threads=256 "
                           f"dim={case.D} causal={case.causal} dtype={case.dtype}"})
     return r
 

@@ -342,10 +342,11 @@ tlg_status tlg_attn_fwd(const void *Q, const void *K, const void *V, void *O, in
  * The number of queries one workgroup of tlg_attn_fwd takes for this shape
  * (host only, no device needed): 128, or 64 when blocks of 128 queries would
  * number at most 256 over all (batch, head) pairs (a grid too small to give
- * every CU a workgroup).  The choice changes no result: every query's sums are
- * formed in the same order either way.  0 for a non-positive size.
+ * every CU a workgroup), or at most 1024 with causal != 0 and dim == 64.  The
+ * choice changes no result: every query's sums are formed in the same order
+ * either way.  0 for a non-positive batch, seq or heads.
  */
-int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads);
+int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads, int64_t dim, int32_t causal);
 
 /*
  * As tlg_attn_fwd, with the number of queries per workgroup given: block_q = 64

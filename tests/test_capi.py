@@ -347,17 +347,22 @@ def test_attention_validation_happens_before_any_launch():
 
 def test_attention_query_block_rule():
     """64 queries per workgroup while blocks of 128 would number at most 256 over all
-    (batch, head) pairs, else 128 (host only)."""
+    (batch, head) pairs, or at most 1024 for causal attention with dim 64, else 128 (host
+    only)."""
     qb = tlg.attention_query_block
-    assert qb(1, 1024, 8) == 64          # the page's instance: 8 x 8 = 64 blocks of 128
-    assert qb(2, 777, 3) == 64           # 7 x 3 x 2 = 42
-    assert qb(1, 2048, 16) == 64         # 16 x 16 = 256
-    assert qb(1, 2049, 16) == 128        # 17 x 16 = 272
-    assert qb(4, 4096, 32) == 128
-    assert qb(1, 1, 1) == 64
-    assert qb(0, 64, 2) == 0 and qb(1, 0, 2) == 0 and qb(1, 64, -1) == 0
+    assert qb(1, 1024, 8, 64, True) == 64           # the page's instance: 8 x 8 = 64 blocks of 128
+    assert qb(2, 777, 3, 128, False) == 64          # 7 x 3 x 2 = 42
+    assert qb(1, 2048, 16, 128, True) == 64         # 16 x 16 = 256
+    assert qb(1, 2049, 16, 128, True) == 128        # 17 x 16 = 272
+    assert qb(1, 2049, 16, 64, False) == 128
+    assert qb(1, 2049, 16, 64, True) == 64          # causal dim 64: up to 1024 blocks
+    assert qb(2, 4096, 16, 64, True) == 64          # 1024
+    assert qb(2, 4097, 16, 64, True) == 128         # 1056
+    assert qb(4, 4096, 32, 64, True) == 128 and qb(4, 4096, 32, 128, True) == 128
+    assert qb(1, 1, 1, 64, False) == 64
+    assert qb(0, 64, 2, 64, True) == 0 and qb(1, 0, 2, 64, True) == 0 and qb(1, 64, -1, 64, True) == 0
     big = (1 << 62) - 1                  # products of the factors would overflow 64 bits
-    assert qb(big, big, big) == 128 and qb(1, 128, big) == 128
+    assert qb(big, big, big, 64, True) == 128 and qb(1, 128, big, 64, True) == 128
 
 
 def test_dequant_and_sparse_validation_happens_before_any_launch():

@@ -96,7 +96,7 @@ def load_library():
         lib.tlg_attn_fwd.restype = i32
         lib.tlg_attn_fwd_block.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, ctypes.c_float, i32, vp]
         lib.tlg_attn_fwd_block.restype = i32
-        lib.tlg_attn_query_block.argtypes = [i64, i64, i64]
+        lib.tlg_attn_query_block.argtypes = [i64, i64, i64, i64, i32]
         lib.tlg_attn_query_block.restype = i32
         lib.tlg_gemm_w4.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp]
         lib.tlg_gemm_w4.restype = i32
@@ -417,10 +417,11 @@ def attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor
     return O
 
 
-def attention_query_block(batch: int, seq: int, heads: int) -> int:
+def attention_query_block(batch: int, seq: int, heads: int, dim: int, causal: bool) -> int:
     """Queries per workgroup that attention would use for this shape (tlg_attn_query_block;
-    host only): 128, or 64 for grids of at most 256 blocks of 128 queries."""
-    return int(load_library().tlg_attn_query_block(int(batch), int(seq), int(heads)))
+    host only): 128, or 64 for grids of at most 256 blocks of 128 queries (1024 when causal
+    with dim 64)."""
+    return int(load_library().tlg_attn_query_block(int(batch), int(seq), int(heads), int(dim), int(bool(causal))))
 
 
 def attention_ptrs(q: int, k: int, v: int, o: int, batch: int, seq: int, heads: int, dim: int, dtype, causal: int,

@@ -754,19 +754,23 @@ tlg_status tlg_gemm_run_mx(tlg_gemm_t plan, const void* A, const void* SA, const
     return err == hipSuccess ? TLG_OK : TLG_ERR_HIP;
 }
 
-int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads)
+int32_t tlg_attn_query_block(int64_t batch, int64_t seq, int64_t heads, int64_t dim, int32_t causal)
 {
     if (batch <= 0 || seq <= 0 || heads <= 0) return 0;
     // Queries per workgroup: 128, or 64 when blocks of 128 would leave CUs without
-    // a workgroup (at most 256 of them).  Measured on MI355X (fp16, one process):
-    // with 64 queries, the page's instance 1x1024x8x64 causal (64 blocks of 128)
-    // goes from 19.6 to 13.2 us, 2x777x3x128 non-causal (42) from 21.5 to 15.0,
-    // 1x2048x8x128 causal (128) from 48.8 to 37.7; with 512 or more blocks of 128
-    // it gains at most 5% (causal) or loses up to 24% (non-causal, 1x4096x16x128:
-    // 142 against 177 us), and 4x4096x32x{64,128} causal lose 7% and 18%.
+    // a workgroup (at most 256 of them), and for causal dim 64 up to 1024 blocks.
+    // Measured on MI355X (fp16, one process): with 64 queries, the page's instance
+    // 1x1024x8x64 causal (64 blocks of 128) goes from 19.6 to 13.2 us, 2x777x3x128
+    // non-causal (42) from 21.5 to 15.0, 1x2048x8x128 causal (128) from 48.8 to
+    // 37.7; causal dim 64 with 512-1024 blocks gains 2-6% (1x8192x16x64: 217.8 ->
+    // 206.6 us, 2x4096x16x64: 119.6 -> 112.9, 2x2048x16x64: 47.9 -> 47.1); other
+    // grids of 512 or more blocks gain at most 1% or lose up to 24% (non-causal
+    // 1x4096x16x128: 142 against 177 us; causal 1x4096x32x128: 178 against 193),
+    // and 4x4096x32x{64,128} causal lose 7% and 18%.
     const int64_t blocks128 = ceil_div(seq, 128);
-    if (blocks128 > 256 || heads > 256 || batch > 256) return 128;   // (each factor is at least 1)
-    return blocks128 * heads * batch <= 256 ? 64 : 128;
+    if (blocks128 > 1024 || heads > 1024 || batch > 1024) return 128;   // (each factor is at least 1)
+    const int64_t blocks = blocks128 * heads * batch;
+    return blocks <= 256 || (causal && dim == 64 && blocks <= 1024) ? 64 : 128;
 }
 
 tlg_status tlg_attn_fwd_block(const void* Q, const void* K, const void* V, void* O, int64_t batch, int64_t seq,
@@ -784,7 +788,7 @@ tlg_status tlg_attn_fwd_block(const void* Q, const void* K, const void* V, void*
     if (batch == 0 || seq == 0 || heads == 0) return TLG_OK;
     const uint64_t per_batch = (uint64_t)seq * (uint64_t)heads * (uint64_t)dim * 2u;
     if (per_batch >= (uint64_t(1) << 31)) return TLG_ERR_UNSUPPORTED;
-    const int64_t bq = block_q ? block_q : tlg_attn_query_block(batch, seq, heads);
+    const int64_t bq = block_q ? block_q : tlg_attn_query_block(batch, seq, heads, dim, causal);
     const int64_t nqb = ceil_div(seq, bq);
     if (batch > INT32_MAX || nqb * heads > INT32_MAX || nqb * heads * batch > INT32_MAX) return TLG_ERR_UNSUPPORTED;
     if (!Q || !K || !V || !O) return TLG_ERR_NULL;
